@@ -1,0 +1,259 @@
+"""ctypes binding of libvsa (include/vsa.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.  The
+functions keep the C names; tensors are PyTorch device tensors (memory and streams
+only), masks are ``workloads``-style dicts or ``vsa_mask_desc`` structs.  A missing
+library raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvsa.so")
+
+VSA_OK, VSA_ERR_INVALID_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_WORKSPACE, VSA_ERR_HIP = 0, -1, -2, -3, -4
+VSA_BF16, VSA_F32 = 0, 1
+VSA_LAYOUT_FRAME_MAJOR, VSA_LAYOUT_TILE_MAJOR = 0, 1
+VSA_MASK_ALL, VSA_MASK_BOX, VSA_MASK_STRIPE, VSA_MASK_STA = 0, 1, 2, 3
+VSA_TILE_EMPTY, VSA_TILE_FULL, VSA_TILE_BOUNDARY = 0, 1, 2
+VSA_FWD_FORCE_MASK, VSA_FWD_REORDER_IO, VSA_FWD_WRITE_LSE = 1, 2, 4
+
+_KINDS = {"all": VSA_MASK_ALL, "box": VSA_MASK_BOX, "stripe": VSA_MASK_STRIPE, "sta": VSA_MASK_STA}
+_LAYOUTS = {"frame": VSA_LAYOUT_FRAME_MAJOR, "tile": VSA_LAYOUT_TILE_MAJOR}
+_MASK_FIELDS = ("kind", "sink_frames", "rt", "rh", "rw", "Tw", "To", "Ts", "Sw", "So", "Ss",
+                "win_t", "win_h", "win_w")
+
+
+class vsa_grid(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "Hg", "Wg", "tile_t", "tile_h", "tile_w")]
+
+
+class vsa_mask_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in _MASK_FIELDS]
+
+
+class vsa_tile_lists(ctypes.Structure):
+    _fields_ = [("cls", ctypes.c_void_p), ("n_full", ctypes.c_void_p), ("n_bnd", ctypes.c_void_p),
+                ("full_idx", ctypes.c_void_p), ("bnd_idx", ctypes.c_void_p)]
+
+
+class VsaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"libvsa status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+_SIGNATURES = {
+    "vsa_last_error": (ctypes.c_char_p, []),
+    "vsa_unique_masks": (_I, [ctypes.POINTER(vsa_mask_desc), _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "vsa_tile_counts": (_I, [ctypes.POINTER(vsa_grid), _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "vsa_classify_tiles": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(vsa_mask_desc), _I, _I, _I,
+                                ctypes.POINTER(vsa_tile_lists), _P]),
+    "vsa_fwd_workspace_bytes": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
+    "vsa_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I,
+                                 ctypes.POINTER(vsa_mask_desc), ctypes.POINTER(vsa_tile_lists), _I, _I,
+                                 ctypes.c_float, _I, _P, ctypes.c_size_t, _P]),
+    "vsa_reorder_tokens": (_I, [_P, _P, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I, _P]),
+    "vsa_profile_workspace_bytes": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
+    "vsa_profile_heads": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I, _P, _I,
+                               ctypes.POINTER(vsa_mask_desc), _I, _P, _P, ctypes.c_float, _P,
+                               ctypes.c_size_t, _P]),
+}
+
+
+def load(path=None):
+    """Load libvsa.so (built in-tree by __graft_entry__.build()).  Raises if missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libvsa.so not found at {p}: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != VSA_OK:
+        raise VsaError(status, load().vsa_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def make_grid(g):
+    if isinstance(g, vsa_grid):
+        return g
+    return vsa_grid(g["T"], g["Hg"], g["Wg"], g.get("tile_t", 0), g.get("tile_h", 0), g.get("tile_w", 0))
+
+
+def make_masks(masks):
+    arr = (vsa_mask_desc * len(masks))()
+    for i, m in enumerate(masks):
+        if isinstance(m, vsa_mask_desc):
+            arr[i] = m
+            continue
+        vals = dict(m)
+        kind = vals["kind"]
+        vals["kind"] = _KINDS[kind] if isinstance(kind, str) else int(kind)
+        arr[i] = vsa_mask_desc(*[int(vals.get(f, 0)) for f in _MASK_FIELDS])
+    return arr
+
+
+def _layout(layout):
+    return _LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return VSA_BF16
+    if t.dtype == torch.float32:
+        return VSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def vsa_last_error():
+    return load().vsa_last_error().decode()
+
+
+def vsa_unique_masks(masks):
+    arr = make_masks(masks)
+    hm = (_I * len(masks))()
+    nu = _I()
+    _check(load().vsa_unique_masks(arr, len(masks), hm, ctypes.byref(nu)))
+    return list(hm), nu.value
+
+
+def vsa_tile_counts(grid, Bq, Bk):
+    nq, nk = _I(), _I()
+    _check(load().vsa_tile_counts(ctypes.byref(make_grid(grid)), Bq, Bk, ctypes.byref(nq), ctypes.byref(nk)))
+    return nq.value, nk.value
+
+
+def alloc_tile_lists(grid, masks, Bq, Bk, device, with_cls=True):
+    nQ, nK = vsa_tile_counts(grid, Bq, Bk)
+    head_map, U = vsa_unique_masks(masks)
+    kw = dict(device=device)
+    return {
+        "cls": torch.empty((U, nQ, nK), dtype=torch.uint8, **kw) if with_cls else None,
+        "n_full": torch.empty((U, nQ), dtype=torch.int32, **kw),
+        "n_bnd": torch.empty((U, nQ), dtype=torch.int32, **kw),
+        "full_idx": torch.empty((U, nQ, nK), dtype=torch.int32, **kw),
+        "bnd_idx": torch.empty((U, nQ, nK), dtype=torch.int32, **kw),
+        "head_map": head_map, "n_unique": U, "nQ": nQ, "nK": nK, "Bq": Bq, "Bk": Bk,
+    }
+
+
+def _lists_struct(t):
+    return vsa_tile_lists(*[(t[n].data_ptr() if t[n] is not None else None)
+                            for n in ("cls", "n_full", "n_bnd", "full_idx", "bnd_idx")])
+
+
+def vsa_classify_tiles(grid, layout, masks, Bq, Bk, out=None, device="cuda", stream=None, with_cls=True):
+    """Classify tiles; returns the dict of device tensors (allocated when out is None)."""
+    if out is None:
+        out = alloc_tile_lists(grid, masks, Bq, Bk, device, with_cls)
+    dev = out["n_full"].device
+    arr = make_masks(masks)
+    st = _lists_struct(out)
+    _check(load().vsa_classify_tiles(ctypes.byref(make_grid(grid)), _layout(layout), arr, len(masks), Bq, Bk,
+                                     ctypes.byref(st), _stream(stream, dev)))
+    return out
+
+
+def vsa_fwd_workspace_bytes(B, S, H, D, dtype, flags):
+    n = ctypes.c_size_t()
+    _check(load().vsa_fwd_workspace_bytes(B, S, H, D, dtype, flags, ctypes.byref(n)))
+    return n.value
+
+
+def vsa_sparse_attn_fwd(q, k, v, grid, layout, masks, tiles, scale=0.0, flags=0, o=None, lse=None,
+                        workspace=None, stream=None):
+    """Block-sparse attention forward; q, k, v contiguous [B, S, H, D] on one device.
+    Returns (o, lse) with lse None unless VSA_FWD_WRITE_LSE is in flags."""
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [B, S, H, D]")
+    B, S, H, D = q.shape
+    dt = _dtype(q)
+    if o is None:
+        o = torch.empty_like(q)
+    if (flags & VSA_FWD_WRITE_LSE) and lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    need = vsa_fwd_workspace_bytes(B, S, H, D, dt, flags)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lists_struct(tiles)
+    _check(load().vsa_sparse_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dt, B, S, H, D, ctypes.byref(make_grid(grid)),
+        _layout(layout), make_masks(masks), ctypes.byref(st), tiles["Bq"], tiles["Bk"], float(scale),
+        flags, _ptr(workspace), ws_bytes, _stream(stream, q.device)))
+    return o, (lse if flags & VSA_FWD_WRITE_LSE else None)
+
+
+def vsa_reorder_tokens(src, grid, inverse=False, dst=None, stream=None):
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous [B, S, H, D]")
+    B, S, H, D = src.shape
+    if dst is None:
+        dst = torch.empty_like(src)
+    _check(load().vsa_reorder_tokens(_ptr(src), _ptr(dst), _dtype(src), B, H, D, ctypes.byref(make_grid(grid)),
+                                     1 if inverse else 0, _stream(stream, src.device)))
+    return dst
+
+
+def vsa_profile_workspace_bytes(B, S, H, D, n_samples, n_cand):
+    n = ctypes.c_size_t()
+    _check(load().vsa_profile_workspace_bytes(B, S, H, D, n_samples, n_cand, ctypes.byref(n)))
+    return n.value
+
+
+def vsa_profile_heads(q, k, v, grid, layout, sample_idx, cands, scale=0.0, workspace=None, stream=None):
+    """Sampled-query profiler; sample_idx int32 [H, n] on the device.  Returns (err [H, n_cand] f32,
+    route [H] int32) device tensors."""
+    B, S, H, D = q.shape
+    n = sample_idx.shape[1]
+    nc = len(cands)
+    err = torch.empty((H, nc), dtype=torch.float32, device=q.device)
+    route = torch.empty((H,), dtype=torch.int32, device=q.device)
+    need = vsa_profile_workspace_bytes(B, S, H, D, n, nc)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(load().vsa_profile_heads(
+        _ptr(q), _ptr(k), _ptr(v), _dtype(q), B, S, H, D, ctypes.byref(make_grid(grid)), _layout(layout),
+        _ptr(sample_idx.contiguous()), n, make_masks(cands), nc, _ptr(err), _ptr(route), float(scale),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
+    return err, route
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)

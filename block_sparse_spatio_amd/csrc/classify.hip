@@ -1,0 +1,92 @@
+// Tile classification kernel: for every distinct mask and query tile, the class of
+// every key tile (full / boundary / empty) and the ascending compact lists of full
+// and boundary key tiles (Sparse VideoGen on TPU, "logical sparsity is not physical
+// sparsity"; video-DiT attention blog, section 7.3: the per-Q-block K-block table).
+//
+// One workgroup per (query tile, mask).  The query range's boxes are computed once;
+// each thread classifies key tiles with interval arithmetic (vsa_geom.h), and a
+// workgroup-wide prefix count keeps the lists in ascending key-tile order.
+// HBM-bound on the class map and list writes; integer-exact.
+#include "vsa_geom.h"
+
+namespace vsa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__global__ __launch_bounds__(kThreads) void classify_kernel(Geom g, MaskTable masks, int Bq, int Bk,
+                                                            int nQ, int nK, uint8_t* __restrict__ cls,
+                                                            int32_t* __restrict__ n_full,
+                                                            int32_t* __restrict__ n_bnd,
+                                                            int32_t* __restrict__ full_idx,
+                                                            int32_t* __restrict__ bnd_idx) {
+  const int qt = blockIdx.x;
+  const int u = blockIdx.y;
+  const DevMask m = masks.m[u];
+  const int r0 = qt * Bq;
+  const int r1 = imin(r0 + Bq, g.S);
+  const bool q_padded = (r0 + Bq) > g.S;
+
+  Box R[11];
+  const int nr = decompose(g, r0, r1, R);
+
+  __shared__ int s_cnt[2][kWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const size_t row = (size_t)u * nQ + qt;
+  uint8_t* cls_row = cls ? cls + row * nK : nullptr;
+  int32_t* full_row = full_idx + row * nK;
+  int32_t* bnd_row = bnd_idx + row * nK;
+
+  int base_full = 0, base_bnd = 0;
+  for (int k0 = 0; k0 < nK; k0 += kThreads) {
+    const int kt = k0 + threadIdx.x;
+    int c = VSA_TILE_EMPTY;
+    if (kt < nK) {
+      const int c0 = kt * Bk;
+      const int c1 = imin(c0 + Bk, g.S);
+      Box C[11];
+      const int nc = decompose(g, c0, c1, C);
+      c = tile_class(g, m, R, nr, C, nc, q_padded || (c0 + Bk) > g.S);
+      if (cls_row) cls_row[kt] = (uint8_t)c;
+    }
+    const uint64_t bf = __ballot(c == VSA_TILE_FULL);
+    const uint64_t bb = __ballot(c == VSA_TILE_BOUNDARY);
+    if (lane == 0) {
+      s_cnt[0][wave] = __popcll(bf);
+      s_cnt[1][wave] = __popcll(bb);
+    }
+    __syncthreads();
+    int off_f = base_full, off_b = base_bnd, tot_f = 0, tot_b = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) { off_f += s_cnt[0][w]; off_b += s_cnt[1][w]; }
+      tot_f += s_cnt[0][w];
+      tot_b += s_cnt[1][w];
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (c == VSA_TILE_FULL) full_row[off_f + __popcll(bf & below)] = kt;
+    if (c == VSA_TILE_BOUNDARY) bnd_row[off_b + __popcll(bb & below)] = kt;
+    base_full += tot_f;
+    base_bnd += tot_b;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    n_full[row] = base_full;
+    n_bnd[row] = base_bnd;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_classify(const Geom& g, const MaskTable& masks, int32_t U, int32_t Bq,
+                           int32_t Bk, int32_t nQ, int32_t nK, const vsa_tile_lists& out,
+                           hipStream_t stream) {
+  dim3 grid(nQ, U);
+  hipLaunchKernelGGL(classify_kernel, grid, dim3(kThreads), 0, stream, g, masks, Bq, Bk, nQ, nK,
+                     out.cls, out.n_full, out.n_bnd, out.full_idx, out.bnd_idx);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

@@ -1,0 +1,388 @@
+// libvsa C ABI: argument validation, descriptor deduplication and normalisation,
+// workspace sizing and kernel launches.  Every check runs before the first HIP call,
+// so invalid arguments are rejected (with a message in vsa_last_error) on any machine.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "vsa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+vsa_status fail(vsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+vsa_status ok() {
+  g_err.clear();
+  return VSA_OK;
+}
+
+vsa_status hip_fail(hipError_t e, const char* what) {
+  return fail(VSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr long long kMaxS = 1LL << 30;
+
+vsa_status check_grid(const vsa_grid* g, vsa_layout layout, bool need_tile, long long* S) {
+  if (!g) return fail(VSA_ERR_INVALID_ARG, "grid is NULL");
+  if (g->T <= 0 || g->Hg <= 0 || g->Wg <= 0)
+    return fail(VSA_ERR_INVALID_ARG, "grid T, Hg, Wg must be positive (got %d, %d, %d)", g->T, g->Hg,
+                g->Wg);
+  if (g->T > 32767 || g->Hg > 32767 || g->Wg > 32767)
+    return fail(VSA_ERR_UNSUPPORTED, "grid dimensions above 32767 are not supported");
+  const long long s = (long long)g->T * g->Hg * g->Wg;
+  if (s > kMaxS) return fail(VSA_ERR_UNSUPPORTED, "sequence length %lld above 2^30", s);
+  if (layout != VSA_LAYOUT_FRAME_MAJOR && layout != VSA_LAYOUT_TILE_MAJOR)
+    return fail(VSA_ERR_INVALID_ARG, "unknown layout %d", (int)layout);
+  const bool tile_set = g->tile_t > 0 || g->tile_h > 0 || g->tile_w > 0;
+  if (layout == VSA_LAYOUT_TILE_MAJOR || need_tile || tile_set) {
+    if (g->tile_t <= 0 || g->tile_h <= 0 || g->tile_w <= 0)
+      return fail(VSA_ERR_INVALID_ARG, "tile-major layout and sliding-tile masks need tile_t/h/w > 0");
+    if (g->T % g->tile_t || g->Hg % g->tile_h || g->Wg % g->tile_w)
+      return fail(VSA_ERR_INVALID_ARG, "tile %dx%dx%d does not divide grid %dx%dx%d", g->tile_t,
+                  g->tile_h, g->tile_w, g->T, g->Hg, g->Wg);
+  }
+  if (g->tile_t < 0 || g->tile_h < 0 || g->tile_w < 0)
+    return fail(VSA_ERR_INVALID_ARG, "negative tile size");
+  *S = s;
+  return VSA_OK;
+}
+
+vsa::Geom make_geom(const vsa_grid* g, vsa_layout layout) {
+  vsa::Geom G;
+  G.T = g->T; G.Hg = g->Hg; G.Wg = g->Wg;
+  G.bt = g->tile_t > 0 ? g->tile_t : 1;
+  G.bh = g->tile_h > 0 ? g->tile_h : 1;
+  G.bw = g->tile_w > 0 ? g->tile_w : 1;
+  G.nT = G.T / G.bt; G.nH = G.Hg / G.bh; G.nW = G.Wg / G.bw;
+  G.HW = G.Hg * G.Wg;
+  G.S = G.T * G.HW;
+  G.layout = (int32_t)layout;
+  return G;
+}
+
+bool fits16(long long v) { return v >= -32768 && v <= 32767; }
+
+// Validate one descriptor and convert it to the kernels' 16-bit form.  Periods, widths,
+// radii and windows beyond what the grid can reach are clamped to an equivalent value.
+vsa_status normalise(const vsa_mask_desc& d, const vsa_grid* g, int index, vsa::DevMask* out) {
+  memset(out, 0, sizeof *out);
+  if (d.sink_frames < 0) return fail(VSA_ERR_INVALID_ARG, "mask %d: sink_frames < 0", index);
+  out->kind = (int16_t)d.kind;
+  out->sink = (int16_t)(d.sink_frames < g->T ? d.sink_frames : g->T);
+  const bool box_unused = d.rt == 0 && d.rh == 0 && d.rw == 0;
+  const bool stripe_unused = d.Tw == 0 && d.To == 0 && d.Ts == 0 && d.Sw == 0 && d.So == 0 && d.Ss == 0;
+  const bool sta_unused = d.win_t == 0 && d.win_h == 0 && d.win_w == 0;
+  auto clamp_r = [](int r, int n) -> int16_t { return (int16_t)(r < 0 ? -1 : (r < n ? r : n)); };
+  switch (d.kind) {
+    case VSA_MASK_ALL:
+      if (!box_unused || !stripe_unused || !sta_unused)
+        return fail(VSA_ERR_INVALID_ARG, "mask %d: ALL with non-zero parameters", index);
+      break;
+    case VSA_MASK_BOX:
+      if (!stripe_unused || !sta_unused)
+        return fail(VSA_ERR_INVALID_ARG, "mask %d: BOX with stripe/window fields set", index);
+      out->rt = clamp_r(d.rt, g->T);
+      out->rh = clamp_r(d.rh, g->Hg);
+      out->rw = clamp_r(d.rw, g->Wg);
+      break;
+    case VSA_MASK_STRIPE: {
+      if (!box_unused || !sta_unused)
+        return fail(VSA_ERR_INVALID_ARG, "mask %d: STRIPE with box/window fields set", index);
+      if (d.Ts < 1 || d.Ss < 1) return fail(VSA_ERR_INVALID_ARG, "mask %d: stripe periods must be >= 1", index);
+      if (d.Tw < 0 || d.Sw < 0) return fail(VSA_ERR_INVALID_ARG, "mask %d: stripe widths must be >= 0", index);
+      const long long HW = (long long)g->Hg * g->Wg;
+      // |dt - To| < T + |To|: a period at least that large never wraps
+      long long Ts = d.Ts, Ss = d.Ss;
+      const long long tmax = (long long)g->T + llabs((long long)d.To);
+      const long long smax = HW + llabs((long long)d.So);
+      if (Ts > tmax) Ts = tmax;
+      if (Ss > smax) Ss = smax;
+      long long Tw = d.Tw < Ts ? d.Tw : Ts, Sw = d.Sw < Ss ? d.Sw : Ss;
+      if (!fits16(d.To) || !fits16(d.So) || !fits16(Ts) || !fits16(Ss) || !fits16(tmax) || !fits16(smax))
+        return fail(VSA_ERR_UNSUPPORTED, "mask %d: stripe parameters or frame size exceed 16 bits", index);
+      out->Tw = (int16_t)Tw; out->To = (int16_t)d.To; out->Ts = (int16_t)Ts;
+      out->Sw = (int16_t)Sw; out->So = (int16_t)d.So; out->Ss = (int16_t)Ss;
+      break;
+    }
+    case VSA_MASK_STA: {
+      if (!box_unused || !stripe_unused)
+        return fail(VSA_ERR_INVALID_ARG, "mask %d: STA with box/stripe fields set", index);
+      if (d.win_t < 1 || d.win_h < 1 || d.win_w < 1)
+        return fail(VSA_ERR_INVALID_ARG, "mask %d: STA window must be >= 1 tile per axis", index);
+      const int nT = g->T / g->tile_t, nH = g->Hg / g->tile_h, nW = g->Wg / g->tile_w;
+      out->wt = (int16_t)(d.win_t < nT ? d.win_t : nT);
+      out->wh = (int16_t)(d.win_h < nH ? d.win_h : nH);
+      out->ww = (int16_t)(d.win_w < nW ? d.win_w : nW);
+      break;
+    }
+    default:
+      return fail(VSA_ERR_INVALID_ARG, "mask %d: unknown kind %d", index, d.kind);
+  }
+  return VSA_OK;
+}
+
+bool any_sta(const vsa_mask_desc* m, int n) {
+  for (int i = 0; i < n; ++i)
+    if (m[i].kind == VSA_MASK_STA) return true;
+  return false;
+}
+
+// Dedupe + normalise H descriptors into a table.  head_map[h] = slot.
+vsa_status build_table(const vsa_mask_desc* masks, int32_t H, const vsa_grid* g, vsa::MaskTable* table,
+                       vsa::HeadMap* hm, int32_t* U) {
+  if (!masks) return fail(VSA_ERR_INVALID_ARG, "masks is NULL");
+  if (H <= 0) return fail(VSA_ERR_INVALID_ARG, "H must be positive");
+  if (H > VSA_MAX_HEADS) return fail(VSA_ERR_UNSUPPORTED, "H=%d above VSA_MAX_HEADS", H);
+  int32_t first[VSA_MAX_UNIQUE_MASKS];
+  int32_t u = 0;
+  memset(table, 0, sizeof *table);
+  memset(hm, 0, sizeof *hm);
+  for (int h = 0; h < H; ++h) {
+    int slot = -1;
+    for (int j = 0; j < u; ++j)
+      if (memcmp(&masks[first[j]], &masks[h], sizeof(vsa_mask_desc)) == 0) { slot = j; break; }
+    if (slot < 0) {
+      if (u == VSA_MAX_UNIQUE_MASKS)
+        return fail(VSA_ERR_UNSUPPORTED, "more than %d distinct masks", VSA_MAX_UNIQUE_MASKS);
+      vsa_status st = normalise(masks[h], g, h, &table->m[u]);
+      if (st != VSA_OK) return st;
+      first[u] = h;
+      slot = u++;
+    }
+    hm->slot[h] = (uint8_t)slot;
+  }
+  *U = u;
+  return VSA_OK;
+}
+
+int elem_size(vsa_dtype dt) { return dt == VSA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa_last_error(void) { return g_err.c_str(); }
+
+vsa_status vsa_unique_masks(const vsa_mask_desc* masks, int32_t H, int32_t* head_map, int32_t* n_unique) {
+  if (!masks || !n_unique) return fail(VSA_ERR_INVALID_ARG, "masks and n_unique must be non-NULL");
+  if (H <= 0) return fail(VSA_ERR_INVALID_ARG, "H must be positive");
+  if (H > VSA_MAX_HEADS) return fail(VSA_ERR_UNSUPPORTED, "H=%d above VSA_MAX_HEADS", H);
+  int32_t first[VSA_MAX_HEADS];
+  int32_t u = 0;
+  for (int h = 0; h < H; ++h) {
+    int slot = -1;
+    for (int j = 0; j < u; ++j)
+      if (memcmp(&masks[first[j]], &masks[h], sizeof(vsa_mask_desc)) == 0) { slot = j; break; }
+    if (slot < 0) { first[u] = h; slot = u++; }
+    if (head_map) head_map[h] = slot;
+  }
+  *n_unique = u;
+  return ok();
+}
+
+vsa_status vsa_tile_counts(const vsa_grid* grid, int32_t Bq, int32_t Bk, int32_t* nQ, int32_t* nK) {
+  long long S;
+  vsa_status st = check_grid(grid, VSA_LAYOUT_FRAME_MAJOR, false, &S);
+  if (st != VSA_OK) return st;
+  if (Bq < 1 || Bk < 1 || Bq > 4096 || Bk > 4096) return fail(VSA_ERR_INVALID_ARG, "tile sizes must be in 1..4096");
+  if (!nQ || !nK) return fail(VSA_ERR_INVALID_ARG, "nQ/nK must be non-NULL");
+  *nQ = (int32_t)((S + Bq - 1) / Bq);
+  *nK = (int32_t)((S + Bk - 1) / Bk);
+  return ok();
+}
+
+vsa_status vsa_classify_tiles(const vsa_grid* grid, vsa_layout layout, const vsa_mask_desc* masks, int32_t H,
+                              int32_t Bq, int32_t Bk, const vsa_tile_lists* out, void* stream) {
+  long long S;
+  vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && any_sta(masks, H), &S);
+  if (st != VSA_OK) return st;
+  if (Bq < 1 || Bk < 1 || Bq > 4096 || Bk > 4096) return fail(VSA_ERR_INVALID_ARG, "tile sizes must be in 1..4096");
+  if (!out || !out->n_full || !out->n_bnd || !out->full_idx || !out->bnd_idx)
+    return fail(VSA_ERR_INVALID_ARG, "tile list arrays must be non-NULL (cls may be NULL)");
+  vsa::MaskTable table;
+  vsa::HeadMap hm;
+  int32_t U = 0;
+  st = build_table(masks, H, grid, &table, &hm, &U);
+  if (st != VSA_OK) return st;
+  const int32_t nQ = (int32_t)((S + Bq - 1) / Bq), nK = (int32_t)((S + Bk - 1) / Bk);
+  hipError_t e = vsa::launch_classify(make_geom(grid, layout), table, U, Bq, Bk, nQ, nK, *out,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "classify launch");
+  return ok();
+}
+
+vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D, vsa_dtype dtype, int32_t flags,
+                                   size_t* bytes) {
+  if (!bytes) return fail(VSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0) return fail(VSA_ERR_INVALID_ARG, "B, S, H, D must be positive");
+  if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  *bytes = (flags & VSA_FWD_REORDER_IO) ? 3ull * B * S * H * D * elem_size(dtype) : 0;
+  return ok();
+}
+
+vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, vsa_dtype dtype,
+                               int32_t B, int32_t S, int32_t H, int32_t D, const vsa_grid* grid, vsa_layout layout,
+                               const vsa_mask_desc* masks, const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk,
+                               float scale, int32_t flags, void* workspace, size_t ws_bytes, void* stream) {
+  long long S_grid;
+  vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && any_sta(masks, H), &S_grid);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !o) return fail(VSA_ERR_INVALID_ARG, "q, k, v, o must be non-NULL");
+  if (o == q || o == k || o == v) return fail(VSA_ERR_INVALID_ARG, "o must not alias q, k or v");
+  if (B <= 0 || H <= 0) return fail(VSA_ERR_INVALID_ARG, "B and H must be positive");
+  if (S != S_grid) return fail(VSA_ERR_INVALID_ARG, "S=%d but grid gives T*Hg*Wg=%lld", S, S_grid);
+  if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (D != 64 && D != 128) return fail(VSA_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", D);
+  if (flags & ~(VSA_FWD_FORCE_MASK | VSA_FWD_REORDER_IO | VSA_FWD_WRITE_LSE))
+    return fail(VSA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if ((flags & VSA_FWD_WRITE_LSE) && !lse) return fail(VSA_ERR_INVALID_ARG, "VSA_FWD_WRITE_LSE needs lse");
+  if (dtype == VSA_BF16) {
+    if ((Bq != 64 && Bq != 128 && Bq != 256) || Bk != 64)
+      return fail(VSA_ERR_UNSUPPORTED, "bf16 tiles Bq=%d Bk=%d (supported: Bq 64/128/256, Bk 64)", Bq, Bk);
+  } else {
+    if ((Bq != 32 && Bq != 64 && Bq != 128) || (Bk != 32 && Bk != 64))
+      return fail(VSA_ERR_UNSUPPORTED, "f32 tiles Bq=%d Bk=%d (supported: Bq 32/64/128, Bk 32/64)", Bq, Bk);
+  }
+  if (!tiles || !tiles->n_full || !tiles->n_bnd || !tiles->full_idx || !tiles->bnd_idx)
+    return fail(VSA_ERR_INVALID_ARG, "tile lists must be non-NULL");
+  if (!isfinite(scale)) return fail(VSA_ERR_INVALID_ARG, "scale is not finite");
+  const bool reorder = (flags & VSA_FWD_REORDER_IO) != 0;
+  if (reorder && layout != VSA_LAYOUT_TILE_MAJOR)
+    return fail(VSA_ERR_INVALID_ARG, "VSA_FWD_REORDER_IO needs the tile-major layout");
+  const size_t eb = elem_size(dtype);
+  const size_t nelem = (size_t)B * S * H * D;
+  if (reorder) {
+    if (!workspace || ws_bytes < 3 * nelem * eb)
+      return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, 3 * nelem * eb);
+  }
+  vsa::MaskTable table;
+  vsa::HeadMap hm;
+  int32_t U = 0;
+  st = build_table(masks, H, grid, &table, &hm, &U);
+  if (st != VSA_OK) return st;
+
+  vsa::FwdArgs a;
+  memset(&a, 0, sizeof a);
+  a.g = make_geom(grid, layout);
+  a.B = B; a.S = S; a.H = H; a.D = D;
+  a.Bq = Bq; a.Bk = Bk;
+  a.nQ = (S + Bq - 1) / Bq;
+  a.nK = (S + Bk - 1) / Bk;
+  a.scale = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
+  a.force_mask = (flags & VSA_FWD_FORCE_MASK) ? 1 : 0;
+  a.write_lse = (flags & VSA_FWD_WRITE_LSE) ? 1 : 0;
+  a.lse_frame_major = reorder ? 1 : 0;
+  a.lse = lse;
+  a.n_full = tiles->n_full; a.n_bnd = tiles->n_bnd;
+  a.full_idx = tiles->full_idx; a.bnd_idx = tiles->bnd_idx;
+  hipStream_t hs = (hipStream_t)stream;
+  const vsa::Geom& G = a.g;
+  char* ws = (char*)workspace;
+  if (reorder) {
+    void* wq = ws;
+    void* wk = ws + nelem * eb;
+    void* wv = ws + 2 * nelem * eb;
+    hipError_t e;
+    if ((e = vsa::launch_reorder(q, wq, (int)eb, B, H, D, G, 0, hs)) != hipSuccess) return hip_fail(e, "reorder q");
+    if ((e = vsa::launch_reorder(k, wk, (int)eb, B, H, D, G, 0, hs)) != hipSuccess) return hip_fail(e, "reorder k");
+    if ((e = vsa::launch_reorder(v, wv, (int)eb, B, H, D, G, 0, hs)) != hipSuccess) return hip_fail(e, "reorder v");
+    // each workgroup reads its own query rows before writing the same output rows, so
+    // the output may overwrite the reordered queries in place
+    a.q = wq; a.k = wk; a.v = wv; a.o = wq;
+  } else {
+    a.q = q; a.k = k; a.v = v; a.o = o;
+  }
+  hipError_t e = dtype == VSA_BF16 ? vsa::launch_attn_bf16(a, table, hm, hs) : vsa::launch_attn_f32(a, table, hm, hs);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (reorder) {
+    e = vsa::launch_reorder(ws, o, (int)eb, B, H, D, G, 1, hs);
+    if (e != hipSuccess) return hip_fail(e, "inverse reorder o");
+  }
+  return ok();
+}
+
+vsa_status vsa_reorder_tokens(const void* src, void* dst, vsa_dtype dtype, int32_t B, int32_t H, int32_t D,
+                              const vsa_grid* grid, int32_t inverse, void* stream) {
+  long long S;
+  vsa_status st = check_grid(grid, VSA_LAYOUT_TILE_MAJOR, true, &S);
+  if (st != VSA_OK) return st;
+  if (!src || !dst) return fail(VSA_ERR_INVALID_ARG, "src and dst must be non-NULL");
+  if (src == dst) return fail(VSA_ERR_INVALID_ARG, "src and dst must not alias");
+  if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B <= 0 || H <= 0 || D <= 0) return fail(VSA_ERR_INVALID_ARG, "B, H, D must be positive");
+  if (((long long)H * D * elem_size(dtype)) % 16)
+    return fail(VSA_ERR_UNSUPPORTED, "token row of H*D elements must be a multiple of 16 bytes");
+  hipError_t e = vsa::launch_reorder(src, dst, elem_size(dtype), B, H, D, make_geom(grid, VSA_LAYOUT_TILE_MAJOR),
+                                     inverse ? 1 : 0, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reorder launch");
+  return ok();
+}
+
+vsa_status vsa_profile_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n_samples,
+                                       int32_t n_cand, size_t* bytes) {
+  if (!bytes) return fail(VSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || n_samples <= 0 || n_cand <= 0)
+    return fail(VSA_ERR_INVALID_ARG, "sizes must be positive");
+  *bytes = vsa::profile_ws_floats(B, H, D, n_samples, n_cand, vsa::profile_chunks(B, S, H)) * sizeof(float);
+  return ok();
+}
+
+vsa_status vsa_profile_heads(const void* q, const void* k, const void* v, vsa_dtype dtype, int32_t B, int32_t S,
+                             int32_t H, int32_t D, const vsa_grid* grid, vsa_layout layout,
+                             const int32_t* sample_idx, int32_t n_samples, const vsa_mask_desc* cands,
+                             int32_t n_cand, float* err, int32_t* route, float scale, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  long long S_grid;
+  vsa_status st = check_grid(grid, layout, cands && n_cand > 0 && n_cand <= 4 && any_sta(cands, n_cand), &S_grid);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !sample_idx || !err || !route)
+    return fail(VSA_ERR_INVALID_ARG, "q, k, v, sample_idx, err, route must be non-NULL");
+  if (B <= 0 || H <= 0) return fail(VSA_ERR_INVALID_ARG, "B and H must be positive");
+  if (S != S_grid) return fail(VSA_ERR_INVALID_ARG, "S=%d but grid gives T*Hg*Wg=%lld", S, S_grid);
+  if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (dtype != VSA_BF16) return fail(VSA_ERR_UNSUPPORTED, "the profiler takes bf16 inputs");
+  if (D != 64 && D != 128) return fail(VSA_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", D);
+  if (n_samples < 1 || n_samples > 256) return fail(VSA_ERR_INVALID_ARG, "n_samples must be in 1..256");
+  if (!cands || n_cand < 2 || n_cand > 4) return fail(VSA_ERR_INVALID_ARG, "n_cand must be in 2..4");
+  if (!isfinite(scale)) return fail(VSA_ERR_INVALID_ARG, "scale is not finite");
+  vsa::MaskTable table;
+  memset(&table, 0, sizeof table);
+  for (int c = 0; c < n_cand; ++c) {
+    st = normalise(cands[c], grid, c, &table.m[c]);
+    if (st != VSA_OK) return st;
+  }
+  vsa::ProfArgs a;
+  memset(&a, 0, sizeof a);
+  a.n_chunks = vsa::profile_chunks(B, S, H);
+  const size_t need = vsa::profile_ws_floats(B, H, D, n_samples, n_cand, a.n_chunks) * sizeof(float);
+  if (!workspace || ws_bytes < need)
+    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  const int nK = (S + 63) / 64;
+  a.chunk_tiles = (nK + a.n_chunks - 1) / a.n_chunks;
+  a.q = q; a.k = k; a.v = v;
+  a.sample_idx = sample_idx;
+  a.err = err; a.route = route;
+  a.ws = (float*)workspace;
+  a.B = B; a.S = S; a.H = H; a.D = D; a.n = n_samples; a.n_cand = n_cand;
+  a.scale = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
+  a.is_bf16 = 1;
+  a.g = make_geom(grid, layout);
+  hipError_t e = vsa::launch_profile(a, table, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "profiler launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,416 @@
+// Exact geometry of masks over position ranges, shared by the HIP kernels.
+//
+// Two jobs:
+//  1. Tile classification (full / boundary / empty) without an element loop.  A
+//     contiguous range of executed positions is a union of at most 2n-1 "boxes",
+//     products of coordinate intervals (n = 3 digits (t,y,x) in frame-major order,
+//     6 digits (tile t,h,w, in-tile t,h,w) in tile-major order).  Every mask kind is
+//     a product of per-axis predicates of a coordinate difference (or of tile
+//     coordinates, for sliding tiles), OR-ed with the key-only sink predicate.  Over
+//     a pair of boxes each difference takes every value of an interval, independently
+//     per axis, so "all pairs kept" and "some pair kept" reduce to interval tests:
+//     a band |d| <= r, or a counting function for the periodic stripe predicate.
+//  2. The element mask of a boundary tile for one query row: the key range is cut
+//     into runs of constant (t, y) and contiguous x; in each run the kept keys of a
+//     box, stripe or sliding-tile mask form a few contiguous bit ranges.
+//
+// Mask definitions: Sparse VideoGen on TPU ("how to accelerate attention": spatial
+// and temporal heads, frame-F00 sink); PSA notes, key design 1 (six-tuple stripes);
+// Sliding Tile Attention explainer, method section 3 (tile-granular window).
+#pragma once
+
+#include <stdint.h>
+
+#include "vsa_internal.h"
+
+namespace vsa {
+
+#define VSA_HD __host__ __device__ __forceinline__
+
+VSA_HD int imin(int a, int b) { return a < b ? a : b; }
+VSA_HD int imax(int a, int b) { return a > b ? a : b; }
+VSA_HD int iabs(int a) { return a < 0 ? -a : a; }
+// floor division for a possibly negative numerator and positive divisor
+VSA_HD int fdiv(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+struct Box {
+  int t0, t1, y0, y1, x0, x1;
+};
+
+// (t, y, x) of executed position p.
+VSA_HD void pos_coords(const Geom& g, int p, int& t, int& y, int& x) {
+  if (g.layout == VSA_LAYOUT_FRAME_MAJOR) {
+    t = p / g.HW;
+    int r = p - t * g.HW;
+    y = r / g.Wg;
+    x = r - y * g.Wg;
+  } else {
+    int vol = g.bt * g.bh * g.bw;
+    int tau = p / vol, io = p - tau * vol;
+    int nHW = g.nH * g.nW;
+    int tt = tau / nHW, r = tau - tt * nHW;
+    int th = r / g.nW, tw = r - th * g.nW;
+    int it = io / (g.bh * g.bw), r2 = io - it * (g.bh * g.bw);
+    int ih = r2 / g.bw, iw = r2 - ih * g.bw;
+    t = tt * g.bt + it;
+    y = th * g.bh + ih;
+    x = tw * g.bw + iw;
+  }
+}
+
+// Frame-major index of the token at executed position p.
+VSA_HD int frame_index(const Geom& g, int p) {
+  int t, y, x;
+  pos_coords(g, p, t, y, x);
+  return (t * g.Hg + y) * g.Wg + x;
+}
+
+// Digits of the executed order, most significant first.
+VSA_HD int order_digits(const Geom& g, int* radix) {
+  if (g.layout == VSA_LAYOUT_FRAME_MAJOR) {
+    radix[0] = g.T; radix[1] = g.Hg; radix[2] = g.Wg;
+    return 3;
+  }
+  radix[0] = g.nT; radix[1] = g.nH; radix[2] = g.nW;
+  radix[3] = g.bt; radix[4] = g.bh; radix[5] = g.bw;
+  return 6;
+}
+
+// Box of positions [cur, cur + cnt*W[j+1]) given that digits < j are those of cur,
+// digit j runs over cnt values from cur's digit j, and digits > j are full.
+VSA_HD Box level_box(const Geom& g, int n, const int* radix, const int* W, int cur, int j,
+                     int cnt) {
+  int lo[6], hi[6];
+  for (int k = 0; k < n; ++k) {
+    int d = (cur / W[k + 1]) % radix[k];
+    if (k < j) { lo[k] = d; hi[k] = d; }
+    else if (k == j) { lo[k] = d; hi[k] = d + cnt - 1; }
+    else { lo[k] = 0; hi[k] = radix[k] - 1; }
+  }
+  Box b;
+  if (n == 3) {
+    b.t0 = lo[0]; b.t1 = hi[0]; b.y0 = lo[1]; b.y1 = hi[1]; b.x0 = lo[2]; b.x1 = hi[2];
+  } else {
+    // axis a: tile digit a, in-tile digit a+3.  When the tile digit is an interval the
+    // in-tile digit is full, so each axis is a single coordinate interval.
+    b.t0 = lo[0] * g.bt + lo[3]; b.t1 = hi[0] * g.bt + hi[3];
+    b.y0 = lo[1] * g.bh + lo[4]; b.y1 = hi[1] * g.bh + hi[4];
+    b.x0 = lo[2] * g.bw + lo[5]; b.x1 = hi[2] * g.bw + hi[5];
+  }
+  return b;
+}
+
+// Split positions [lo, end) into at most 2n-1 boxes (mixed-radix range decomposition).
+VSA_HD int decompose(const Geom& g, int lo, int end, Box* out) {
+  int radix[6];
+  int n = order_digits(g, radix);
+  int W[7];
+  W[n] = 1;
+  for (int k = n - 1; k >= 0; --k) W[k] = W[k + 1] * radix[k];
+  int nb = 0, cur = lo;
+  if (cur >= end) return 0;
+  // ascending: align cur to ever coarser digit boundaries
+  int j = n - 1;
+  for (; j >= 0; --j) {
+    int blk = W[j];
+    int next = ((cur + blk - 1) / blk) * blk;
+    if (next > end) break;
+    if (next > cur) {
+      out[nb++] = level_box(g, n, radix, W, cur, j, (next - cur) / W[j + 1]);
+      cur = next;
+    }
+    if (cur == end) return nb;
+  }
+  if (j < 0) j = 0;
+  // descending: whole runs of digit j, then finer digits
+  for (; j < n && cur < end; ++j) {
+    int cnt = (end - cur) / W[j + 1];
+    if (cnt > 0) {
+      out[nb++] = level_box(g, n, radix, W, cur, j, cnt);
+      cur += cnt * W[j + 1];
+    }
+  }
+  return nb;
+}
+
+// ---------------------------------------------------------------------------
+// predicates over intervals of a coordinate difference
+// ---------------------------------------------------------------------------
+// #{v in [0, m] : v mod P < w}, m >= -1
+VSA_HD int band_prefix(int m, int P, int w) {
+  if (m < 0) return 0;
+  int wc = imin(w, P);
+  return ((m + 1) / P) * wc + imin((m + 1) % P, wc);
+}
+// #{u in [a, b] : (|u| mod P) < w}
+VSA_HD int band_count(int a, int b, int P, int w) {
+  if (a > b || w <= 0) return 0;
+  int c = 0;
+  if (b >= 0) {
+    int lo = imax(a, 0);
+    c += band_prefix(b, P, w) - band_prefix(lo - 1, P, w);
+  }
+  if (a < 0) {
+    int lo = imax(-b, 1), hi = -a;
+    c += band_prefix(hi, P, w) - band_prefix(lo - 1, P, w);
+  }
+  return c;
+}
+
+// |d| <= r over d in [a, b]; r < 0 = unbounded
+VSA_HD void radius_test(int a, int b, int r, bool& all, bool& any) {
+  if (r < 0) { all = true; any = true; return; }
+  all = (a >= -r) && (b <= r);
+  any = (a <= r) && (b >= -r);
+}
+
+// (|d - o| mod P) <= w - 1 over d in [a, b]
+VSA_HD void periodic_test(int a, int b, int o, int P, int w, bool& all, bool& any) {
+  int c = band_count(a - o, b - o, P, w);
+  all = (c == b - a + 1);
+  any = (c > 0);
+}
+
+VSA_HD int sta_start(int a, int w, int n) { return imin(imax(a - w / 2, 0), imax(n - w, 0)); }
+
+// sliding tile window on one axis: tile coords a in [a0, a1] (queries), b in [b0, b1]
+VSA_HD void sta_test(int a0, int a1, int b0, int b1, int w, int n, bool& all, bool& any) {
+  int s0 = sta_start(a0, w, n), s1 = sta_start(a1, w, n);
+  all = (s1 <= b0) && (b1 <= s0 + w - 1);
+  any = (s0 <= b1) && (s1 + w - 1 >= b0);
+}
+
+VSA_HD bool s_contiguous(const Geom& g, const Box& b) {
+  return b.y0 == b.y1 || (b.x0 == 0 && b.x1 == g.Wg - 1);
+}
+
+// all / any kept over query box r x key box c for the mask without its sink.
+VSA_HD void box_pair_test(const Geom& g, const DevMask& m, const Box& r, const Box& c, bool& all,
+                          bool& any) {
+  switch (m.kind) {
+    case VSA_MASK_ALL:
+      all = true; any = true;
+      return;
+    case VSA_MASK_BOX: {
+      bool a0, n0, a1, n1, a2, n2;
+      radius_test(c.t0 - r.t1, c.t1 - r.t0, m.rt, a0, n0);
+      radius_test(c.y0 - r.y1, c.y1 - r.y0, m.rh, a1, n1);
+      radius_test(c.x0 - r.x1, c.x1 - r.x0, m.rw, a2, n2);
+      all = a0 && a1 && a2;
+      any = n0 && n1 && n2;
+      return;
+    }
+    case VSA_MASK_STRIPE: {
+      bool at, nt;
+      periodic_test(c.t0 - r.t1, c.t1 - r.t0, m.To, m.Ts, m.Tw, at, nt);
+      bool as = true, ns = false;
+      if (s_contiguous(g, r) && s_contiguous(g, c)) {
+        int sq0 = r.y0 * g.Wg + r.x0, sq1 = r.y1 * g.Wg + r.x1;
+        int sk0 = c.y0 * g.Wg + c.x0, sk1 = c.y1 * g.Wg + c.x1;
+        periodic_test(sk0 - sq1, sk1 - sq0, m.So, m.Ss, m.Sw, as, ns);
+      } else {
+        int dx0 = c.x0 - r.x1, dx1 = c.x1 - r.x0;
+        for (int dy = c.y0 - r.y1; dy <= c.y1 - r.y0; ++dy) {
+          bool a, n;
+          periodic_test(dy * g.Wg + dx0, dy * g.Wg + dx1, m.So, m.Ss, m.Sw, a, n);
+          as = as && a;
+          ns = ns || n;
+        }
+      }
+      all = at && as;
+      any = nt && ns;
+      return;
+    }
+    case VSA_MASK_STA: {
+      bool a0, n0, a1, n1, a2, n2;
+      sta_test(r.t0 / g.bt, r.t1 / g.bt, c.t0 / g.bt, c.t1 / g.bt, m.wt, g.nT, a0, n0);
+      sta_test(r.y0 / g.bh, r.y1 / g.bh, c.y0 / g.bh, c.y1 / g.bh, m.wh, g.nH, a1, n1);
+      sta_test(r.x0 / g.bw, r.x1 / g.bw, c.x0 / g.bw, c.x1 / g.bw, m.ww, g.nW, a2, n2);
+      all = a0 && a1 && a2;
+      any = n0 && n1 && n2;
+      return;
+    }
+    default:
+      all = false; any = false;
+      return;
+  }
+}
+
+// Tile class of query boxes R[nr] x key boxes C[nc] (padded: the tile reaches past S).
+VSA_HD int tile_class(const Geom& g, const DevMask& m, const Box* R, int nr, const Box* C, int nc,
+                      bool padded) {
+  bool all = true, any = false;
+  for (int i = 0; i < nr; ++i) {
+    for (int j = 0; j < nc; ++j) {
+      Box c = C[j];
+      if (c.t0 < m.sink) {  // key frames below the sink are kept for every query
+        any = true;
+        if (c.t1 < m.sink) continue;
+        c.t0 = m.sink;
+      }
+      bool a, n;
+      box_pair_test(g, m, R[i], c, a, n);
+      all = all && a;
+      any = any || n;
+      if (!all && any) return VSA_TILE_BOUNDARY;
+    }
+  }
+  if (!any) return VSA_TILE_EMPTY;
+  return (all && !padded) ? VSA_TILE_FULL : VSA_TILE_BOUNDARY;
+}
+
+// ---------------------------------------------------------------------------
+// element mask of one query row over a key tile (bit i = key c0 + i kept)
+// ---------------------------------------------------------------------------
+struct QueryPos {
+  int t, y, x, s;     // coordinates, s = y*Wg + x
+  int st, sh, sw;     // STA window starts (tile coordinates)
+};
+
+VSA_HD QueryPos make_query(const Geom& g, const DevMask& m, int p) {
+  QueryPos q;
+  pos_coords(g, p, q.t, q.y, q.x);
+  q.s = q.y * g.Wg + q.x;
+  q.st = q.sh = q.sw = 0;
+  if (m.kind == VSA_MASK_STA) {
+    q.st = sta_start(q.t / g.bt, m.wt, g.nT);
+    q.sh = sta_start(q.y / g.bh, m.wh, g.nH);
+    q.sw = sta_start(q.x / g.bw, m.ww, g.nW);
+  }
+  return q;
+}
+
+VSA_HD uint64_t bit_range(int lo, int hi) {  // bits lo..hi inclusive, 0 <= lo <= hi < 64
+  uint64_t ones = ~0ull >> (63 - (hi - lo));
+  return ones << lo;
+}
+
+// kept keys of a run (fixed t, y; x in [x0, x1]; bit of x0 is off) for query q
+VSA_HD uint64_t run_mask(const Geom& g, const DevMask& m, const QueryPos& q, int t, int y, int x0,
+                         int x1, int off) {
+  if (t < m.sink || m.kind == VSA_MASK_ALL) return bit_range(off, off + x1 - x0);
+  switch (m.kind) {
+    case VSA_MASK_BOX: {
+      if (m.rt >= 0 && iabs(t - q.t) > m.rt) return 0;
+      if (m.rh >= 0 && iabs(y - q.y) > m.rh) return 0;
+      int lo = x0, hi = x1;
+      if (m.rw >= 0) { lo = imax(lo, q.x - m.rw); hi = imin(hi, q.x + m.rw); }
+      return lo <= hi ? bit_range(off + lo - x0, off + hi - x0) : 0;
+    }
+    case VSA_MASK_STRIPE: {
+      if ((iabs(t - q.t - m.To) % m.Ts) >= m.Tw) return 0;
+      // u = s_k - s_q - So over the run; kept where (|u| mod Ss) < Sw
+      int ubase = y * g.Wg - q.s - m.So;  // u = x + ubase
+      int ua = x0 + ubase, ub = x1 + ubase;
+      uint64_t bits = 0;
+      if (ub >= 0) {
+        int lo = imax(ua, 0);
+        for (int j = lo / m.Ss; j <= ub / m.Ss; ++j) {
+          int a = imax(lo, j * m.Ss), b = imin(ub, j * m.Ss + m.Sw - 1);
+          if (a <= b) bits |= bit_range(off + a - ubase - x0, off + b - ubase - x0);
+        }
+      }
+      if (ua < 0) {
+        int lo = imax(-ub, 1), hi = -ua;  // |u| in [lo, hi]
+        for (int j = lo / m.Ss; j <= hi / m.Ss; ++j) {
+          int a = imax(lo, j * m.Ss), b = imin(hi, j * m.Ss + m.Sw - 1);
+          if (a <= b) bits |= bit_range(off - b - ubase - x0, off - a - ubase - x0);
+        }
+      }
+      return bits;
+    }
+    case VSA_MASK_STA: {
+      int at = t / g.bt, ay = y / g.bh;
+      if (at < q.st || at >= q.st + m.wt) return 0;
+      if (ay < q.sh || ay >= q.sh + m.wh) return 0;
+      int lo = imax(x0, q.sw * g.bw), hi = imin(x1, (q.sw + m.ww) * g.bw - 1);
+      return lo <= hi ? bit_range(off + lo - x0, off + hi - x0) : 0;
+    }
+    default:
+      return 0;
+  }
+}
+
+// Run cursor over executed positions: advances through maximal runs of constant
+// (t, y) with contiguous x.
+struct RunCursor {
+  int p;                 // current position
+  int t, y, x;           // its coordinates
+  int tt, th, tw, it, ih, iw;  // tile-major digits
+};
+
+VSA_HD RunCursor run_begin(const Geom& g, int p) {
+  RunCursor c;
+  c.p = p;
+  if (g.layout == VSA_LAYOUT_FRAME_MAJOR) {
+    pos_coords(g, p, c.t, c.y, c.x);
+    c.tt = c.th = c.tw = c.it = c.ih = c.iw = 0;
+  } else {
+    int vol = g.bt * g.bh * g.bw;
+    int tau = p / vol, io = p - tau * vol;
+    int nHW = g.nH * g.nW;
+    c.tt = tau / nHW;
+    int r = tau - c.tt * nHW;
+    c.th = r / g.nW;
+    c.tw = r - c.th * g.nW;
+    c.it = io / (g.bh * g.bw);
+    int r2 = io - c.it * (g.bh * g.bw);
+    c.ih = r2 / g.bw;
+    c.iw = r2 - c.ih * g.bw;
+    c.t = c.tt * g.bt + c.it;
+    c.y = c.th * g.bh + c.ih;
+    c.x = c.tw * g.bw + c.iw;
+  }
+  return c;
+}
+
+// length of the run starting at the cursor, capped by end
+VSA_HD int run_len(const Geom& g, const RunCursor& c, int end) {
+  int room = (g.layout == VSA_LAYOUT_FRAME_MAJOR) ? g.Wg - c.x : g.bw - c.iw;
+  return imin(room, end - c.p);
+}
+
+VSA_HD void run_advance(const Geom& g, RunCursor& c, int len) {
+  c.p += len;
+  if (g.layout == VSA_LAYOUT_FRAME_MAJOR) {
+    c.x += len;
+    if (c.x >= g.Wg) {
+      c.x = 0;
+      if (++c.y >= g.Hg) { c.y = 0; ++c.t; }
+    }
+  } else {
+    c.iw += len;
+    if (c.iw >= g.bw) {
+      c.iw = 0;
+      if (++c.ih >= g.bh) {
+        c.ih = 0;
+        if (++c.it >= g.bt) {
+          c.it = 0;
+          if (++c.tw >= g.nW) {
+            c.tw = 0;
+            if (++c.th >= g.nH) { c.th = 0; ++c.tt; }
+          }
+        }
+      }
+    }
+    c.t = c.tt * g.bt + c.it;
+    c.y = c.th * g.bh + c.ih;
+    c.x = c.tw * g.bw + c.iw;
+  }
+}
+
+// Keep bits of keys [c0, min(c0 + nbits, S)) for query q (nbits <= 64).
+VSA_HD uint64_t tile_row_mask(const Geom& g, const DevMask& m, const QueryPos& q, int c0,
+                              int nbits) {
+  int end = imin(c0 + nbits, g.S);
+  uint64_t bits = 0;
+  RunCursor c = run_begin(g, c0);
+  while (c.p < end) {
+    int len = run_len(g, c, end);
+    bits |= run_mask(g, m, q, c.t, c.y, c.x, c.x + len - 1, c.p - c0);
+    run_advance(g, c, len);
+  }
+  return bits;
+}
+
+}  // namespace vsa

@@ -1,0 +1,93 @@
+// Internal declarations shared by the host API and the kernels of libvsa.
+// Not part of the public ABI (include/vsa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vsa.h"
+
+namespace vsa {
+
+// Mask descriptor as the kernels see it: 16-bit fields so that a table of
+// VSA_MAX_UNIQUE_MASKS descriptors plus the head map fits in kernel arguments.
+// The host normalises every descriptor first (periods and radii clamped to the grid,
+// which leaves the predicate unchanged) and rejects values that do not fit.
+struct DevMask {
+  int16_t kind, sink;
+  int16_t rt, rh, rw;
+  int16_t Tw, To, Ts, Sw, So, Ss;
+  int16_t wt, wh, ww;
+  int16_t pad0, pad1;
+};
+static_assert(sizeof(DevMask) == 32, "DevMask layout");
+
+// Geometry of the token grid and the executed order.
+struct Geom {
+  int32_t T, Hg, Wg;
+  int32_t bt, bh, bw;    // 3D tile (tile-major layout and STA masks), else 1
+  int32_t nT, nH, nW;    // tile grid
+  int32_t S, HW;
+  int32_t layout;        // VSA_LAYOUT_*
+};
+
+struct MaskTable {
+  DevMask m[VSA_MAX_UNIQUE_MASKS];
+};
+
+struct HeadMap {
+  uint8_t slot[VSA_MAX_HEADS];
+};
+
+// ---- launch wrappers (defined next to their kernels) ----
+hipError_t launch_classify(const Geom& g, const MaskTable& masks, int32_t U, int32_t Bq,
+                           int32_t Bk, int32_t nQ, int32_t nK, const vsa_tile_lists& out,
+                           hipStream_t stream);
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* n_full;
+  const int32_t* n_bnd;
+  const int32_t* full_idx;
+  const int32_t* bnd_idx;
+  int32_t B, S, H, D;
+  int32_t nQ, nK;
+  int32_t Bq, Bk;
+  float scale;
+  int32_t force_mask;
+  int32_t write_lse;
+  int32_t lse_frame_major;  // executed order is tile-major; write lse in frame-major order
+  Geom g;
+};
+
+hipError_t launch_attn_bf16(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
+                            hipStream_t stream);
+hipError_t launch_attn_f32(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
+                           hipStream_t stream);
+hipError_t launch_reorder(const void* src, void* dst, int32_t elem_bytes, int32_t B,
+                          int32_t H, int32_t D, const Geom& g, int32_t inverse,
+                          hipStream_t stream);
+
+struct ProfArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* sample_idx;
+  float* err;
+  int32_t* route;
+  float* ws;
+  int32_t B, S, H, D, n, n_cand, n_chunks, chunk_tiles;
+  float scale;
+  int32_t is_bf16;
+  Geom g;
+};
+size_t profile_ws_floats(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand,
+                         int32_t n_chunks);
+int32_t profile_chunks(int32_t B, int32_t S, int32_t H);
+hipError_t launch_profile(const ProfArgs& a, const MaskTable& cands, hipStream_t stream);
+
+}  // namespace vsa

@@ -1,0 +1,232 @@
+/*
+ * vsa.h -- C ABI of libvsa: mask-driven block-sparse attention over 3D video
+ * token sequences on AMD Instinct MI355X (gfx950).
+ *
+ * The problem, as the pages state it:
+ *   - Q, K, V are [B, S, H, D] tensors of S video tokens (DSA study guide,
+ *     sections 5-6: per-device shards [B, S/N, H, D]; this library works on one
+ *     GPU's full sequence);
+ *   - the tokens come from a latent grid of T frames x Hg rows x Wg columns;
+ *   - every head has a mask (spatial, temporal, first-frame sink, sliding tile
+ *     window, PSA stripe six-tuple);
+ *   - attention is O = softmax(Q K^T * scale + M) V (Sliding Tile Attention
+ *     explainer, method section 2, eq. (1));
+ *   - the mask is reduced to a per-(query-tile, key-tile) class: full, boundary or
+ *     empty (Sparse VideoGen on TPU, "logical sparsity is not physical sparsity");
+ *     empty tiles are skipped, full tiles run without an in-tile mask, boundary
+ *     tiles apply an exact element mask (same page, "avoid in-tile masking when
+ *     nothing needs masking"), and every kept key contributes through online
+ *     softmax (DSA study guide, section 18).
+ *
+ * Conventions for every entry point
+ *   - Device pointers are caller-owned HIP device memory; the library never
+ *     allocates or frees device memory and keeps no state between calls.
+ *   - Host pointers (descriptors) are read only during the call.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *     stream).  The return status covers argument validation and launch errors;
+ *     faults during execution surface at the caller's next synchronisation.
+ *   - On error nothing is enqueued, the function returns a negative vsa_status and
+ *     vsa_last_error() returns a message for the calling thread.  No C++
+ *     exception crosses this boundary.
+ *   - Argument validation happens before any HIP call, so invalid arguments are
+ *     rejected on machines without a GPU as well.
+ */
+#ifndef VSA_H_
+#define VSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VSA_OK = 0,
+  VSA_ERR_INVALID_ARG = -1, /* malformed argument (null pointer, bad shape, ...) */
+  VSA_ERR_UNSUPPORTED = -2, /* well-formed but not implemented (D, dtype, tile size) */
+  VSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  VSA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} vsa_status;
+
+typedef enum { VSA_BF16 = 0, VSA_F32 = 1 } vsa_dtype;
+
+/* Order of the S positions along the sequence axis of Q/K/V/O.
+ *   FRAME_MAJOR: position p = (t*Hg + y)*Wg + x (tokens of one frame contiguous).
+ *   TILE_MAJOR:  the grid is cut into tiles of tile_t x tile_h x tile_w tokens; the
+ *     tiles are ordered row-major over the tile grid and the tokens row-major inside
+ *     a tile, so every tile is contiguous (Sliding Tile Attention explainer, method
+ *     section 3; PSA notes, key design 2).  T, Hg, Wg must be multiples of the tile. */
+typedef enum { VSA_LAYOUT_FRAME_MAJOR = 0, VSA_LAYOUT_TILE_MAJOR = 1 } vsa_layout;
+
+/* Latent grid.  S = T*Hg*Wg.  tile_* is the 3D token tile used by TILE_MAJOR and by
+ * STA masks (0 when unused). */
+typedef struct {
+  int32_t T, Hg, Wg;
+  int32_t tile_t, tile_h, tile_w;
+} vsa_grid;
+
+typedef enum {
+  VSA_MASK_ALL = 0,    /* every pair kept */
+  VSA_MASK_BOX = 1,    /* |dt|<=rt && |dy|<=rh && |dx|<=rw, radius < 0 = unbounded */
+  VSA_MASK_STRIPE = 2, /* PSA: (|t_k-t_q-To| mod Ts) <= Tw-1 && (|s_k-s_q-So| mod Ss) <= Sw-1 */
+  VSA_MASK_STA = 3     /* sliding tile window of win_t x win_h x win_w tiles */
+} vsa_mask_kind;
+
+/* Per-head mask descriptor.  Every kind also keeps keys whose frame index is below
+ * sink_frames (first-frame attention sink: Sparse VideoGen on TPU, "how to
+ * accelerate attention", both masks keep frame F00; DSA study guide, section 3).
+ *   BOX:    spatial head = {BOX, 1, rt=1, rh=-1, rw=-1}; temporal head =
+ *           {BOX, 1, rt=-1, rh=r, rw=r} (Sparse VideoGen on TPU; DSA section 3).
+ *   STRIPE: s = y*Wg + x; Ts >= 1 and Ss >= 1 (PSA notes, key design 1); the
+ *           absolute value is taken before the modulus, so To/So != 0 is asymmetric.
+ *   STA:    with a, b the query and key tile coordinates along an axis of n tiles,
+ *           start = clamp(a - w/2, 0, n - w) and the pair is kept iff
+ *           start <= b < start + w on all three axes; the window is shifted inward
+ *           at the edges and keeps its size (Sliding Tile Attention explainer,
+ *           method section 3).  Requires grid tile_* > 0 dividing T, Hg, Wg.
+ * Unused fields must be zero.  Descriptors that compare equal field by field share
+ * one classification. */
+typedef struct {
+  int32_t kind;
+  int32_t sink_frames;
+  int32_t rt, rh, rw;
+  int32_t Tw, To, Ts, Sw, So, Ss;
+  int32_t win_t, win_h, win_w;
+} vsa_mask_desc;
+
+/* Tile classes stored in vsa_tile_lists.cls. */
+enum { VSA_TILE_EMPTY = 0, VSA_TILE_FULL = 1, VSA_TILE_BOUNDARY = 2 };
+
+/* Output of the classifier, all caller-allocated device arrays.  With
+ * nQ = ceil(S/Bq), nK = ceil(S/Bk) and U = number of distinct descriptors:
+ *   cls       uint8 [U][nQ][nK]  tile class (may be NULL: not written)
+ *   n_full    int32 [U][nQ]      number of FULL key tiles of each query tile
+ *   n_bnd     int32 [U][nQ]      number of BOUNDARY key tiles
+ *   full_idx  int32 [U][nQ][nK]  ascending FULL key-tile indices in the first
+ *                                n_full entries of each row; the rest is unspecified
+ *   bnd_idx   int32 [U][nQ][nK]  same for BOUNDARY tiles
+ * A tile reaching past S is padded and never FULL (Sparse VideoGen on TPU,
+ * "aligning the sparse mask with execution": padding contributes zero weight).
+ * Unique descriptors are numbered in order of first appearance in masks[]. */
+typedef struct {
+  uint8_t* cls;
+  int32_t* n_full;
+  int32_t* n_bnd;
+  int32_t* full_idx;
+  int32_t* bnd_idx;
+} vsa_tile_lists;
+
+/* Limits. */
+#define VSA_MAX_HEADS 256
+#define VSA_MAX_UNIQUE_MASKS 64
+
+/* Host-only helpers ---------------------------------------------------------- */
+
+/* Deduplicate per-head descriptors.  head_map (host, [H], may be NULL) receives
+ * each head's unique-descriptor slot; *n_unique the number of distinct ones. */
+vsa_status vsa_unique_masks(const vsa_mask_desc* masks, int32_t H, int32_t* head_map,
+                            int32_t* n_unique);
+
+/* nQ = ceil(S/Bq), nK = ceil(S/Bk) for the grid. */
+vsa_status vsa_tile_counts(const vsa_grid* grid, int32_t Bq, int32_t Bk, int32_t* nQ,
+                           int32_t* nK);
+
+/* Tile classification -------------------------------------------------------- */
+
+/* Classify every (query tile, key tile) of each distinct mask and write compact
+ * ascending lists (Sparse VideoGen on TPU, "logical sparsity is not physical
+ * sparsity"; video-DiT attention blog, section 7.3: a per-Q-block table of the K
+ * blocks it computes).  The result is exact: it equals counting kept pairs of the
+ * materialised mask in each tile.
+ *   grid, layout:  token grid and sequence order of the positions
+ *   masks:         host [H] descriptors (deduplicated internally)
+ *   Bq, Bk:        query / key tile sizes in positions, 1..4096
+ *   out:           device arrays sized for U unique masks (see vsa_tile_lists)
+ * Errors: INVALID_ARG for a null pointer, bad grid or descriptor; UNSUPPORTED when
+ * H > VSA_MAX_HEADS or U > VSA_MAX_UNIQUE_MASKS. */
+vsa_status vsa_classify_tiles(const vsa_grid* grid, vsa_layout layout,
+                              const vsa_mask_desc* masks, int32_t H, int32_t Bq,
+                              int32_t Bk, const vsa_tile_lists* out, void* stream);
+
+/* Attention forward ----------------------------------------------------------- */
+
+#define VSA_FWD_FORCE_MASK 1  /* ablation: run every listed tile through the masked path */
+#define VSA_FWD_REORDER_IO 2  /* TILE_MAJOR only: q/k/v/o are frame-major; reorder into the
+                                 workspace, attend in tile-major order, reorder O back */
+#define VSA_FWD_WRITE_LSE 4   /* write lse (must then be non-NULL) */
+
+/* Workspace bytes vsa_sparse_attn_fwd needs for these arguments (0 without
+ * VSA_FWD_REORDER_IO; 3*B*S*H*D elements of dtype with it). */
+vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D,
+                                   vsa_dtype dtype, int32_t flags, size_t* bytes);
+
+/* Block-sparse masked attention forward.
+ *   q, k, v:  device [B][S][H][D], dtype, contiguous
+ *   o:        device [B][S][H][D], dtype (output; must not alias q/k/v)
+ *   lse:      device float [B][H][S] = m + ln(l), natural log (written only with
+ *             VSA_FWD_WRITE_LSE; -inf for a row with no kept key)
+ *   grid, layout, masks[H]: as given to vsa_classify_tiles for `tiles`
+ *   tiles:    lists from vsa_classify_tiles with the same grid, layout, masks, Bq, Bk
+ *   Bq, Bk:   bf16: Bq in {64, 128, 256}, Bk = 64; f32: Bq in {32, 64, 128}, Bk in {32, 64}
+ *   scale:    softmax scale; 0 selects 1/sqrt(D)
+ *   flags:    VSA_FWD_* bits
+ *   workspace, ws_bytes: device scratch, see vsa_fwd_workspace_bytes (may be NULL
+ *             when 0 bytes are needed)
+ * Output rows whose query has no kept key are 0.  D must be 64 or 128.
+ * The full tiles take an unmasked path and boundary tiles an element-masked path;
+ * both feed one online softmax per query row, so the result does not depend on
+ * the split (Sparse VideoGen on TPU, "avoid in-tile masking ..."). */
+vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                               float* lse, vsa_dtype dtype, int32_t B, int32_t S,
+                               int32_t H, int32_t D, const vsa_grid* grid,
+                               vsa_layout layout, const vsa_mask_desc* masks,
+                               const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk,
+                               float scale, int32_t flags, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* Tile-major reorder ---------------------------------------------------------- */
+
+/* Permute the sequence axis of src [B][S][H][D] into dst (no aliasing):
+ * inverse = 0: frame-major -> tile-major; inverse != 0: tile-major -> frame-major.
+ * grid tile_* must divide T, Hg, Wg (Sliding Tile Attention explainer, method
+ * section 3: tokens of a tile are contiguous). */
+vsa_status vsa_reorder_tokens(const void* src, void* dst, vsa_dtype dtype, int32_t B,
+                              int32_t H, int32_t D, const vsa_grid* grid,
+                              int32_t inverse, void* stream);
+
+/* Head profiler --------------------------------------------------------------- */
+
+/* Workspace bytes vsa_profile_heads needs. */
+vsa_status vsa_profile_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D,
+                                       int32_t n_samples, int32_t n_cand, size_t* bytes);
+
+/* Sampled-query head profiler (Sparse VideoGen on TPU, "how to accelerate
+ * attention": sample a few queries, compute their outputs under full attention and
+ * each candidate mask, route the head to the mask with the smallest deviation;
+ * "supporting dynamic routing with fixed tensor shapes": one flag per head).
+ *   q, k, v:     device [B][S][H][D], dtype
+ *   sample_idx:  device int32 [H][n_samples], positions in [0, S), shared across b
+ *   cands:       host [n_cand] descriptors, cands[0] is the reference (normally ALL);
+ *                2 <= n_cand <= 4
+ *   err:         device float [H][n_cand]: sqrt(sum over b, samples, channels of
+ *                (o_c - o_0)^2); err[h][0] = 0
+ *   route:       device int32 [H]: argmin over c >= 1 of err[h][c], lowest c on ties
+ *   n_samples:   1..256
+ * Errors as for the other entry points; WORKSPACE when ws_bytes is too small. */
+vsa_status vsa_profile_heads(const void* q, const void* k, const void* v, vsa_dtype dtype,
+                             int32_t B, int32_t S, int32_t H, int32_t D,
+                             const vsa_grid* grid, vsa_layout layout,
+                             const int32_t* sample_idx, int32_t n_samples,
+                             const vsa_mask_desc* cands, int32_t n_cand, float* err,
+                             int32_t* route, float scale, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/* Thread-local message of the last error on this thread ("" if none). */
+const char* vsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H_ */

@@ -1,0 +1,158 @@
+"""The C ABI: the library loads, exports every symbol include/vsa.h declares, and its
+host-only helpers and argument validation work without a GPU (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_spatio_amd as vsa
+import workloads as W
+from block_sparse_spatio_amd import _lib
+from tests.conftest import ROOT
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "vsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = vsa.load()
+    names = _declared_functions()
+    assert {"vsa_classify_tiles", "vsa_sparse_attn_fwd", "vsa_profile_heads"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "vsa.h"\nint main(void){ vsa_grid g = {1,1,1,0,0,0}; (void)g; return 0; }\n')
+    r = os.system(f"gcc -std=c99 -Wall -Werror -I{ROOT}/include -c {src} -o {tmp_path}/t.o")
+    assert r == 0
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(_lib.vsa_grid) == 24
+    assert ctypes.sizeof(_lib.vsa_mask_desc) == 56
+    assert ctypes.sizeof(_lib.vsa_tile_lists) == 40
+
+
+def test_unique_masks_and_counts():
+    masks = [W.mask_spatial(1)] * 3 + [W.mask_temporal(4)] * 2 + [W.mask_spatial(1)]
+    hm, u = vsa.vsa_unique_masks(masks)
+    assert u == 2 and hm == [0, 0, 0, 1, 1, 0]
+    assert vsa.vsa_tile_counts(W.grid(21, 45, 80), 128, 64) == (591, 1182)
+    assert vsa.vsa_tile_counts(W.grid(30, 48, 80), 128, 64) == (900, 1800)
+
+
+def test_workspace_sizes():
+    assert vsa.vsa_fwd_workspace_bytes(1, 115200, 24, 128, vsa.VSA_BF16, 0) == 0
+    assert vsa.vsa_fwd_workspace_bytes(1, 115200, 24, 128, vsa.VSA_BF16, vsa.VSA_FWD_REORDER_IO) \
+        == 3 * 115200 * 24 * 128 * 2
+    assert vsa.vsa_profile_workspace_bytes(2, 75600, 40, 128, 64, 3) > 0
+
+
+class _Fake:
+    """Stand-in tensor: the validation paths below fail before any pointer is used."""
+    def __init__(self, shape, dtype):
+        import torch
+        self.shape = shape
+        self.dtype = dtype
+        self.device = torch.device("cpu")
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return 0x1000
+
+
+def _call_fwd(**over):
+    import torch
+    lib = vsa.load()
+    g = over.pop("grid", W.grid(4, 8, 8))
+    masks = over.pop("masks", [W.mask_spatial(1), W.mask_temporal(1)])
+    args = dict(q=0x1000, k=0x2000, v=0x3000, o=0x4000, lse=None, dtype=vsa.VSA_BF16, B=1, S=256, H=2, D=64,
+                layout=0, Bq=64, Bk=64, scale=0.0, flags=0, ws=None, ws_bytes=0)
+    args.update(over)
+    lists = _lib.vsa_tile_lists(0x5000, 0x6000, 0x7000, 0x8000, 0x9000)
+    arr = _lib.make_masks(masks)
+    st = lib.vsa_sparse_attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dtype"],
+                                 args["B"], args["S"], args["H"], args["D"], ctypes.byref(_lib.make_grid(g)),
+                                 args["layout"], arr, ctypes.byref(lists), args["Bq"], args["Bk"],
+                                 args["scale"], args["flags"], args["ws"], args["ws_bytes"], None)
+    del torch
+    return st, vsa.vsa_last_error()
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(S=255), -1, "S=255"),
+    (dict(D=96), -2, "D=96"),
+    (dict(dtype=7), -1, "dtype"),
+    (dict(Bq=96), -2, "Bq=96"),
+    (dict(q=None), -1, "non-NULL"),
+    (dict(o=0x1000), -1, "alias"),
+    (dict(flags=64), -1, "flag"),
+    (dict(flags=4), -1, "lse"),
+    (dict(flags=2), -1, "tile-major"),
+    (dict(flags=2, layout=1, grid=W.grid(4, 8, 8, (2, 4, 4))), -3, "workspace"),
+    (dict(grid=W.grid(4, 8, 8, (3, 4, 4)), layout=1), -1, "divide"),
+    (dict(masks=[W.mask_stripe(1, 0, 0, 1, 0, 5), W.mask_all()]), -1, "period"),
+    (dict(masks=[W.mask_sta(1, 1, 1), W.mask_all()]), -1, "tile"),
+    (dict(masks=[dict(W.mask_all(), rt=3), W.mask_all()]), -1, "ALL"),
+    (dict(masks=[dict(W.mask_all(), kind=9), W.mask_all()]), -1, "kind"),
+    (dict(scale=float("nan")), -1, "scale"),
+])
+def test_fwd_validation(over, status, needle):
+    st, msg = _call_fwd(**over)
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_classify_validation():
+    lib = vsa.load()
+    arr = _lib.make_masks([W.mask_spatial(1)])
+    lists = _lib.vsa_tile_lists(None, None, None, None, None)
+    st = lib.vsa_classify_tiles(ctypes.byref(_lib.make_grid(W.grid(4, 8, 8))), 0, arr, 1, 64, 64,
+                                ctypes.byref(lists), None)
+    assert st == -1 and "non-NULL" in vsa.vsa_last_error()
+    lists = _lib.vsa_tile_lists(0x10, 0x20, 0x30, 0x40, 0x50)
+    st = lib.vsa_classify_tiles(ctypes.byref(_lib.make_grid(W.grid(0, 8, 8))), 0, arr, 1, 64, 64,
+                                ctypes.byref(lists), None)
+    assert st == -1 and "positive" in vsa.vsa_last_error()
+    st = lib.vsa_classify_tiles(ctypes.byref(_lib.make_grid(W.grid(4, 8, 8))), 0, arr, 1, 0, 64,
+                                ctypes.byref(lists), None)
+    assert st == -1
+    many = _lib.make_masks([W.mask_box(i, -1, -1) for i in range(65)])
+    st = lib.vsa_classify_tiles(ctypes.byref(_lib.make_grid(W.grid(70, 2, 2))), 0, many, 65, 64, 64,
+                                ctypes.byref(lists), None)
+    assert st == -2 and "distinct" in vsa.vsa_last_error()
+
+
+def test_profile_validation():
+    lib = vsa.load()
+    g = _lib.make_grid(W.grid(4, 8, 8))
+    cands = _lib.make_masks([W.mask_all(), W.mask_spatial(1), W.mask_temporal(1)])
+    err = ctypes.c_void_p(0x10)
+    st = lib.vsa_profile_heads(0x1, 0x2, 0x3, vsa.VSA_F32, 1, 256, 2, 64, ctypes.byref(g), 0, 0x4, 8,
+                               cands, 3, err, 0x5, 0.0, 0x6, 1 << 20, None)
+    assert st == -2 and "bf16" in vsa.vsa_last_error()
+    st = lib.vsa_profile_heads(0x1, 0x2, 0x3, vsa.VSA_BF16, 1, 256, 2, 64, ctypes.byref(g), 0, 0x4, 8,
+                               cands, 3, err, 0x5, 0.0, 0x6, 16, None)
+    assert st == -3
+    st = lib.vsa_profile_heads(0x1, 0x2, 0x3, vsa.VSA_BF16, 1, 256, 2, 64, ctypes.byref(g), 0, 0x4, 300,
+                               cands, 3, err, 0x5, 0.0, 0x6, 1 << 30, None)
+    assert st == -1
+
+
+def test_reorder_validation():
+    lib = vsa.load()
+    g = _lib.make_grid(W.grid(4, 8, 8))
+    st = lib.vsa_reorder_tokens(0x1, 0x2, vsa.VSA_BF16, 1, 2, 64, ctypes.byref(g), 0, None)
+    assert st == -1 and "tile" in vsa.vsa_last_error()
+    g = _lib.make_grid(W.grid(4, 8, 8, (2, 4, 4)))
+    st = lib.vsa_reorder_tokens(0x1, 0x1, vsa.VSA_BF16, 1, 2, 64, ctypes.byref(g), 0, None)
+    assert st == -1 and "alias" in vsa.vsa_last_error()

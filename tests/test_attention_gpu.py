@@ -1,0 +1,181 @@
+"""Attention forward on the GPU against the CPU oracle (spec tolerances:
+fp32 max-abs <= 1e-5; bf16 max-abs <= 2e-2 and mean-abs <= 1e-3, the oracle run on
+the same bf16-rounded inputs)."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_spatio_amd as vsa
+import oracle
+import workloads as W
+from tests.gpu_helpers import assert_close, dev, run_attention, sample_rows_per_tile, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_config_fp32(gpu_lib):
+    cfg = W.config("tiny")
+    q, k, v = W.qkv(cfg["B"], 256, cfg["H"], cfg["D"], "f32", seed=cfg["seed"])
+    for masks in (cfg["masks"], cfg["extra_masks"]):
+        say(f"tiny fp32 masks={masks}")
+        o, lse, _ = run_attention(q, k, v, cfg["grid"], "frame", masks, 32, 32, flags=vsa.VSA_FWD_WRITE_LSE)
+        ref_o, ref_lse = oracle.attention(q, k, v, cfg["grid"], "frame", masks)
+        assert_close(o, ref_o, "f32", "tiny fp32")
+        assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-5
+    # the all-keep mask is dense attention: compare with a library routine too
+    o, _, _ = run_attention(q, k, v, cfg["grid"], "frame", cfg["extra_masks"], 32, 32)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(x.double().permute(0, 2, 1, 3) for x in (q, k, v))).permute(0, 2, 1, 3)
+    assert (o.double().cpu() - ref).abs().max() <= 1e-5
+
+
+@pytest.mark.parametrize("Bq,Bk", [(32, 64), (64, 32), (128, 64)])
+def test_fp32_tile_shapes(gpu_lib, Bq, Bk):
+    g = W.grid(3, 7, 9)  # S = 189: ragged tails on both sides
+    masks = [W.mask_spatial(1), W.mask_temporal(2), W.mask_stripe(2, 0, 3, 3, 1, 10)]
+    q, k, v = W.qkv(2, 189, 3, 128, "f32", seed=11)
+    o, _, _ = run_attention(q, k, v, g, "frame", masks, Bq, Bk)
+    ref, _ = oracle.attention(q, k, v, g, "frame", masks)
+    assert_close(o, ref, "f32", f"fp32 Bq={Bq} Bk={Bk}")
+
+
+SMALL_CASES = [
+    # (grid, layout, masks, D, B)
+    (W.grid(5, 6, 7), "frame", [W.mask_spatial(1), W.mask_temporal(2), W.mask_all()], 128, 1),
+    (W.grid(4, 9, 10), "frame", [W.mask_box(0, 2, 3, 0), W.mask_box(2, -1, 1, 2)], 128, 2),
+    (W.grid(6, 5, 16), "frame", [W.mask_stripe(1, 0, 3, 1, 0, 16), W.mask_stripe(2, 1, 2, 4, 0, 80),
+                                 W.mask_stripe(3, 0, 7, 2, 3, 5)], 128, 1),
+    (W.grid(4, 8, 8, (2, 4, 4)), "tile", [W.mask_sta(1, 1, 1), W.mask_sta(2, 2, 1, sink_frames=1)], 128, 1),
+    (W.grid(4, 8, 8, (2, 4, 4)), "tile", [W.mask_temporal(2), W.mask_stripe(1, 0, 2, 3, 0, 9)], 64, 1),
+    (W.grid(3, 11, 13), "frame", [W.mask_spatial(0, sink_frames=0), W.mask_temporal(1)], 64, 1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+@pytest.mark.parametrize("Bq", [64, 128, 256])
+def test_small_bf16(gpu_lib, case, Bq):
+    g, layout, masks, D, B = SMALL_CASES[case]
+    S = W.seq_len(g)
+    q, k, v = W.qkv(B, S, len(masks), D, "bf16", seed=100 + case)
+    say(f"small bf16 case={case} Bq={Bq} S={S} D={D} layout={layout}")
+    o, lse, _ = run_attention(q, k, v, g, layout, masks, Bq, 64, flags=vsa.VSA_FWD_WRITE_LSE)
+    ref_o, ref_lse = oracle.attention(q, k, v, g, layout, masks)
+    assert_close(o, ref_o, "bf16", f"case {case} Bq {Bq}")
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 5e-3
+
+
+def test_force_mask_matches_specialised_path(gpu_lib):
+    """The B1 ablation (every tile through the masked path) equals the full/boundary
+    split bit for bit: on a full tile the element mask keeps everything."""
+    g = W.grid(6, 8, 16)
+    masks = [W.mask_spatial(1), W.mask_temporal(3), W.mask_all()]
+    q, k, v = W.qkv(1, W.seq_len(g), 3, 128, "bf16", seed=5)
+    o1, _, _ = run_attention(q, k, v, g, "frame", masks, 128, 64)
+    o2, _, _ = run_attention(q, k, v, g, "frame", masks, 128, 64, flags=vsa.VSA_FWD_FORCE_MASK)
+    assert torch.equal(o1, o2)
+
+
+def test_deterministic(gpu_lib):
+    g = W.grid(5, 10, 16)
+    masks = [W.mask_temporal(2), W.mask_stripe(2, 0, 3, 2, 0, 16)]
+    q, k, v = W.qkv(1, W.seq_len(g), 2, 128, "bf16", seed=6)
+    o1, _, _ = run_attention(q, k, v, g, "frame", masks, 128, 64)
+    o2, _, _ = run_attention(q, k, v, g, "frame", masks, 128, 64)
+    assert torch.equal(o1, o2)
+
+
+def test_zero_query_is_mean_of_kept_values(gpu_lib):
+    g = W.grid(4, 6, 10)
+    S = W.seq_len(g)
+    masks = [W.mask_box(1, 1, 2, sink_frames=1)]
+    _, k, v = W.qkv(1, S, 1, 128, "bf16", seed=8)
+    q = torch.zeros_like(k)
+    o, _, _ = run_attention(q, k, v, g, "frame", masks, 64, 64)
+    c = oracle.token_coords(g, "frame", np.arange(S))
+    keep = oracle.keep_matrix(masks[0], g, c, c)
+    vv = v[0, :, 0].double().numpy()
+    ref = np.stack([vv[keep[i]].mean(axis=0) for i in range(S)])
+    assert_close(o[0, :, 0], ref, "bf16", "zero query")
+
+
+def test_self_only_stripe_is_identity(gpu_lib):
+    g = W.grid(3, 5, 20)
+    masks = [W.mask_stripe(1, 0, 10, 1, 0, 500, sink_frames=0)]
+    q, k, v = W.qkv(1, W.seq_len(g), 1, 128, "bf16", seed=9)
+    o, _, _ = run_attention(q, k, v, g, "frame", masks, 128, 64)
+    assert torch.equal(o.cpu(), v)
+
+
+def test_empty_rows_are_zero(gpu_lib):
+    g = W.grid(3, 4, 8)
+    masks = [W.mask_stripe(1, 5, 99, 4, 0, 4, sink_frames=0)]
+    q, k, v = W.qkv(1, W.seq_len(g), 1, 64, "bf16", seed=10)
+    o, lse, tiles = run_attention(q, k, v, g, "frame", masks, 64, 64, flags=vsa.VSA_FWD_WRITE_LSE)
+    assert int(tiles["n_full"].sum() + tiles["n_bnd"].sum()) == 0
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_sta_reorder_io_matches_frame_major(gpu_lib):
+    """Tile-major attention with the reorder inside the call equals frame-major attention
+    with the same coordinate mask, and the oracle."""
+    g = W.grid(6, 16, 32, (2, 8, 8))  # 128-token tiles: query and key tiles nest inside them
+    S = W.seq_len(g)
+    masks = [W.mask_sta(1, 1, 3), W.mask_sta(2, 1, 3, sink_frames=1)]
+    q, k, v = W.qkv(1, S, 2, 128, "bf16", seed=12)
+    o_t, lse_t, tiles = run_attention(q, k, v, g, "tile", masks, 128, 64, reorder_io=True,
+                                      flags=vsa.VSA_FWD_WRITE_LSE)
+    o_f, lse_f, _ = run_attention(q, k, v, g, "frame", masks, 128, 64, flags=vsa.VSA_FWD_WRITE_LSE)
+    ref, ref_lse = oracle.attention(q, k, v, g, "frame", masks)
+    assert_close(o_t, ref, "bf16", "sta tile-major")
+    assert_close(o_f, ref, "bf16", "sta frame-major")
+    assert np.abs(lse_t.cpu().numpy() - ref_lse).max() <= 5e-3
+    assert int(tiles["n_bnd"][0].sum()) == 0  # sliding tiles: full or empty only
+    # tiles that straddle two sliding tiles are boundary tiles and still exact
+    g2 = W.grid(6, 16, 16, (3, 4, 4))
+    q2, k2, v2 = W.qkv(1, W.seq_len(g2), 2, 128, "bf16", seed=13)
+    masks2 = [W.mask_sta(1, 3, 3), W.mask_sta(2, 1, 3, sink_frames=1)]
+    o2, _, tiles2 = run_attention(q2, k2, v2, g2, "tile", masks2, 128, 64, reorder_io=True)
+    assert int(tiles2["n_bnd"].sum()) > 0
+    assert_close(o2, oracle.attention(q2, k2, v2, g2, "frame", masks2)[0], "bf16", "sta straddling")
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+_FULL = {}
+
+
+def _full_inputs(name):
+    if name not in _FULL:
+        _FULL.clear()
+        cfg = W.config(name)
+        S = W.seq_len(cfg["grid"])
+        say(f"drawing inputs for {name}")
+        _FULL[name] = (cfg, W.qkv(cfg["B"], S, cfg["H"], cfg["D"], cfg["dtype"], seed=cfg["seed"]))
+    return _FULL[name]
+
+
+@pytest.mark.parametrize("name,Bq,which", [
+    ("wan_mixed", 128, "masks"), ("wan_single", 128, "masks"), ("wan_single", 64, "masks"),
+    ("wan_single", 256, "masks"), ("wan_single", 128, "extra_masks"), ("sta_hunyuan", 128, "masks"),
+    ("stripe_route", 128, "masks")])
+def test_full_config_sampled_rows(gpu_lib, name, Bq, which):
+    cfg, (q, k, v) = _full_inputs(name)
+    g, layout, masks = cfg["grid"], cfg["layout"], cfg[which]
+    S = W.seq_len(g)
+    say(f"full config {name} Bq={Bq} {which}: S={S} H={cfg['H']} B={cfg['B']}")
+    d = dev()
+    qd, kd, vd = q.to(d), k.to(d), v.to(d)
+    reorder = layout == "tile"
+    tiles = vsa.vsa_classify_tiles(g, layout, masks, Bq, cfg["Bk"], device=d, with_cls=False)
+    o, lse = vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles,
+                                     flags=vsa.VSA_FWD_WRITE_LSE | (vsa.VSA_FWD_REORDER_IO if reorder else 0))
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    # oracle on sampled rows (frame-major indices: the reorder is inside the call)
+    rows = sample_rows_per_tile(S, Bq, seed=3, per_tile=0, max_tiles=24)
+    heads = list(range(0, cfg["H"], max(1, cfg["H"] // 8)))
+    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
+    got = o[:, rows][:, :, heads]
+    assert_close(got, ref_o, "bf16", f"{name} sampled rows")
+    assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3

@@ -1,0 +1,101 @@
+"""Tile classification on the GPU: bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_helpers import check_lists_against, dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_desc(rng, layout):
+    kinds = ["all", "box", "stripe"] + (["sta"] if layout == "tile" else [])
+    kind = kinds[rng.integers(len(kinds))]
+    sink = int(rng.integers(0, 3))
+    if kind == "all":
+        return W.mask_all()
+    if kind == "box":
+        r = lambda: int(rng.integers(-1, 4))  # noqa: E731
+        return W.mask_box(r(), r(), r(), sink_frames=sink)
+    if kind == "stripe":
+        return W.mask_stripe(int(rng.integers(0, 4)), int(rng.integers(-2, 3)), int(rng.integers(1, 6)),
+                             int(rng.integers(0, 5)), int(rng.integers(-3, 4)), int(rng.integers(1, 40)),
+                             sink_frames=sink)
+    return W.mask_sta(int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(1, 4)),
+                      sink_frames=sink)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_classify_random_small(gpu_lib, seed):
+    rng = np.random.default_rng(seed)
+    layout = "tile" if seed % 3 == 2 else "frame"
+    if layout == "tile":
+        tile = tuple(int(x) for x in rng.integers(1, 4, 3))
+        g = W.grid(tile[0] * int(rng.integers(1, 4)), tile[1] * int(rng.integers(1, 4)),
+                   tile[2] * int(rng.integers(1, 5)), tile)
+    else:
+        g = W.grid(int(rng.integers(1, 7)), int(rng.integers(1, 9)), int(rng.integers(1, 12)))
+    H = int(rng.integers(1, 5))
+    masks = [_random_desc(rng, layout) for _ in range(H)]
+    Bq = int(rng.choice([1, 3, 8, 16, 32, 64, 128]))
+    Bk = int(rng.choice([1, 5, 16, 32, 64]))
+    say(f"classify seed={seed} grid={g} layout={layout} Bq={Bq} Bk={Bk} masks={masks}")
+    tiles = gpu_lib.vsa_classify_tiles(g, layout, masks, Bq, Bk, device=dev())
+    torch.cuda.synchronize()
+    hm, U = gpu_lib.vsa_unique_masks(masks)
+    for h, desc in enumerate(masks):
+        ref = oracle.classify(g, layout, desc, Bq, Bk)
+        check_lists_against(tiles, hm[h], ref["q_tiles"], ref["cls"])
+
+
+def _sampled_q_tiles(nQ, rng, n=6):
+    return np.unique(np.concatenate([[0, nQ - 1, nQ // 2], rng.choice(nQ, n, replace=False)]))
+
+
+@pytest.mark.parametrize("name,Bq", [("wan_mixed", 128), ("wan_single", 64), ("wan_single", 128),
+                                     ("wan_single", 256), ("sta_hunyuan", 128), ("stripe_route", 128)])
+def test_classify_full_configs(gpu_lib, name, Bq):
+    cfg = W.config(name)
+    g, layout, masks = cfg["grid"], cfg["layout"], cfg["masks"]
+    say(f"classify full config {name} Bq={Bq}")
+    tiles = gpu_lib.vsa_classify_tiles(g, layout, masks, Bq, cfg["Bk"], device=dev())
+    torch.cuda.synchronize()
+    hm, U = gpu_lib.vsa_unique_masks(masks)
+    rng = np.random.default_rng(7)
+    nQ = tiles["nQ"]
+    seen = set()
+    for h, desc in enumerate(masks):
+        u = hm[h]
+        if u in seen:
+            continue
+        seen.add(u)
+        qts = _sampled_q_tiles(nQ, rng, 3 if U > 8 else 6)
+        ref = oracle.classify(g, layout, desc, Bq, cfg["Bk"], q_tiles=qts)
+        check_lists_against(tiles, u, qts, ref["cls"])
+    # whole-map properties: the lists agree with the class map everywhere
+    cls = tiles["cls"].cpu()
+    assert torch.equal((cls == 1).sum(-1).int(), tiles["n_full"].cpu())
+    assert torch.equal((cls == 2).sum(-1).int(), tiles["n_bnd"].cpu())
+    if name == "sta_hunyuan":
+        # sliding tiles: every tile pair is full or empty; 3x3x3 tiles of 384 tokens
+        # = 27 * 6 key tiles of 64 per query tile
+        assert int(tiles["n_bnd"].sum()) == 0
+        assert torch.all(tiles["n_full"].cpu() == 27 * 6)
+    if name == "wan_single" and Bq == 128:
+        # |dt| <= 3 plus sink keeps 152 of 441 frame pairs; the kept-pair count
+        # equals the sum over FULL tiles plus the kept pairs inside BOUNDARY tiles,
+        # so the FULL tiles alone stay below it
+        full_pairs = int(tiles["n_full"].sum()) * 128 * 64
+        assert full_pairs <= 152 * 3600 * 3600
+
+
+def test_classify_null_cls(gpu_lib):
+    g = W.grid(5, 6, 7)
+    masks = [W.mask_temporal(2)]
+    t = gpu_lib.vsa_classify_tiles(g, "frame", masks, 32, 16, device=dev(), with_cls=False)
+    torch.cuda.synchronize()
+    ref = oracle.classify(g, "frame", masks[0], 32, 16)
+    t["cls"] = None
+    check_lists_against(t, 0, ref["q_tiles"], ref["cls"])
