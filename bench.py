@@ -1,0 +1,328 @@
+"""Benchmark of the block-sparse video attention hot path on one MI355X.
+
+One step = one pass of the path over one batch of synthetic input: tile
+classification of the layer's masks (vsa_classify_tiles) followed by the sparse
+attention forward (vsa_sparse_attn_fwd).  The default workload is the Wan-2.1-14B
+720p-shaped mixed-head layer (21 x 45 x 80 = 75,600 tokens, 40 heads, d = 128,
+bf16, heads 0-19 spatial and 20-39 temporal with a frame-0 sink, tiles 128 x 64).
+
+Prints one JSON line.  `value` is effective TFLOP/s over executed tiles
+(4*D FLOP per executed (query, key) pair, the pages' convention) for the whole
+step; the roofline block reports the attention kernel alone against the bf16
+dense MFMA peak, timed with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no structured sparsity)
+PEAK_HBM_GBS = 8000.0
+METRIC = "sparse-attn ms/call + effective TFLOP/s at 75.6K tokens; % of bf16 MFMA peak"
+ATTN_SOURCES = ["attn_bf16.hip", "mfma_tile.h", "vsa_geom.h"]
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_spatio_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# FLOP accounting
+# ---------------------------------------------------------------------------
+def executed_pairs(tiles, head_map, B, S):
+    """Sum over heads and batch of |R|*|C| over the listed (executed) tiles."""
+    import torch
+    Bq, Bk, nQ, nK = tiles["Bq"], tiles["Bk"], tiles["nQ"], tiles["nK"]
+    rows = torch.full((nQ,), Bq, dtype=torch.int64)
+    rows[-1] = S - (nQ - 1) * Bq
+    last_cols = S - (nK - 1) * Bk
+    nf = tiles["n_full"].cpu().long()
+    nb = tiles["n_bnd"].cpu().long()
+    # a tail key tile is never FULL; it is the last entry of a boundary list when listed
+    bi = tiles["bnd_idx"].cpu()
+    idx = (nb - 1).clamp(min=0)
+    last = torch.gather(bi, 2, idx.unsqueeze(-1)).squeeze(-1).long()
+    has_tail = (nb > 0) & (last == nK - 1)
+    cols = (nf + nb) * Bk - has_tail.long() * (Bk - last_cols)
+    per_slot = (cols * rows.unsqueeze(0)).sum(dim=1)  # [U]
+    total = 0
+    for h in range(len(head_map)):
+        total += int(per_slot[head_map[h]])
+    return total * B
+
+
+def kept_pairs(g, masks, B):
+    """Exact kept (query, key) pairs of frame-major coordinate masks, counted per frame
+    pair from per-axis difference histograms (measurement accounting)."""
+    T, Hg, Wg = g["T"], g["Hg"], g["Wg"]
+    HW = Hg * Wg
+    total = 0
+    cache = {}
+    for m in masks:
+        key = tuple(sorted(m.items()))
+        if key in cache:
+            total += cache[key]
+            continue
+        sink = m["sink_frames"]
+        if m["kind"] == "all":
+            c = (T * HW) ** 2
+        elif m["kind"] == "box":
+            def axis(n, r):
+                if r < 0:
+                    return n * n
+                d = np.arange(-(n - 1), n)
+                return int(np.sum((n - np.abs(d))[np.abs(d) <= r]))
+            within = axis(Hg, m["rh"]) * axis(Wg, m["rw"])
+            c = 0
+            for tq in range(T):
+                for tk in range(T):
+                    if tk < sink:
+                        c += HW * HW
+                    elif m["rt"] < 0 or abs(tk - tq) <= m["rt"]:
+                        c += within
+        elif m["kind"] == "stripe":
+            ds = np.arange(-(HW - 1), HW)
+            intra = (np.abs(ds - m["So"]) % m["Ss"]) <= m["Sw"] - 1
+            n_intra = int(np.sum((HW - np.abs(ds))[intra]))
+            c = 0
+            for tq in range(T):
+                for tk in range(T):
+                    if tk < sink:
+                        c += HW * HW
+                    elif (abs(tk - tq - m["To"]) % m["Ts"]) <= m["Tw"] - 1:
+                        c += n_intra
+        elif m["kind"] == "sta":
+            bt, bh, bw = g["tile_t"], g["tile_h"], g["tile_w"]
+            vol = bt * bh * bw
+            per_axis = []
+            for n, w in ((T // bt, m["win_t"]), (Hg // bh, m["win_h"]), (Wg // bw, m["win_w"])):
+                per_axis.append(n * min(w, n))
+            c = per_axis[0] * per_axis[1] * per_axis[2] * vol * vol
+        else:
+            raise ValueError(m["kind"])
+        cache[key] = c
+        total += c
+    return total * B
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+def cpu_baseline(cfg, q, k, v, tiles, head_map, budget_s=12.0):
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    g, masks = cfg["grid"], cfg["masks"]
+    S = g["T"] * g["Hg"] * g["Wg"]
+    Bq, Bk, nQ, nK = tiles["Bq"], tiles["Bk"], tiles["nQ"], tiles["nK"]
+    nf = tiles["n_full"].cpu().numpy()
+    nb = tiles["n_bnd"].cpu().numpy()
+    # heads of both kinds, query tiles spread over the sequence
+    uniq = sorted(set(head_map))
+    heads = [head_map.index(u) for u in uniq][:4]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(nQ)
+    work = 0
+    rows_done = 0
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < budget_s and i < nQ:
+        qt = int(order[i])
+        i += 1
+        rows = np.arange(qt * Bq, min(S, (qt + 1) * Bq))
+        oracle.attention(q[:1], k[:1], v[:1], g, "frame", masks, rows=rows, heads=heads)
+        for h in heads:
+            u = head_map[h]
+            work += (int(nf[u, qt]) + int(nb[u, qt])) * Bk * len(rows) * 4 * cfg["D"]
+        rows_done += len(rows) * len(heads)
+    dt = time.perf_counter() - t0
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {"value": work / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} query rows ({len(heads)} heads x {i} query tiles of {Bq}) of batch 0, "
+                      f"fp64 NumPy, {dt:.1f} s; work counted as executed-tile FLOP of those rows"}
+
+
+# ---------------------------------------------------------------------------
+def traffic_from_profiles(khash, n_launch_units):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_bf16_wan_mixed_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != khash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="wan_mixed")
+    ap.add_argument("--Bq", type=int, default=None)
+    ap.add_argument("--flags", type=int, default=0, help="extra VSA_FWD_* flags (e.g. 1 = B1 ablation)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the all-keep dense run")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run the tile-major reorder (a plain row copy) over a MIB-sized tensor, "
+                         "5 times: the known-size kernel that calibrates HBM byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by head with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import block_sparse_spatio_amd as vsa
+    import workloads as W
+
+    vsa.load()
+    dev = torch.device("cuda:0")
+    if args.copy_probe:
+        gp = W.grid(30, 48, 80, (6, 8, 8))
+        Sp = W.seq_len(gp)
+        Hp = max(1, (args.copy_probe << 20) // (Sp * 128 * 2))
+        x = torch.randn((1, Sp, Hp, 128), device=dev).to(torch.bfloat16)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            vsa.vsa_reorder_tokens(x, gp, dst=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": x.numel() * 2, "copy_probe_bytes_written": y.numel() * 2,
+                          "launches": 5}), flush=True)
+        return 0
+    cfg = W.config(args.config)
+    g, layout, masks = cfg["grid"], cfg["layout"], cfg["masks"]
+    B, H, D = cfg["B"], cfg["H"], cfg["D"]
+    S = W.seq_len(g)
+    Bq = args.Bq or cfg["Bq"]
+    Bk = cfg["Bk"]
+    reorder = layout == "tile"
+    flags = args.flags | (vsa.VSA_FWD_REORDER_IO if reorder else 0)
+    print(f"[bench] {args.config}: B={B} S={S} H={H} D={D} Bq={Bq} Bk={Bk} drawing inputs", file=sys.stderr,
+          flush=True)
+    q, k, v = W.qkv(B, S, H, D, cfg["dtype"], seed=cfg["seed"])
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    head_map, U = vsa.vsa_unique_masks(masks)
+    tiles = vsa.alloc_tile_lists(g, masks, Bq, Bk, dev, with_cls=False)
+    ws_bytes = vsa.vsa_fwd_workspace_bytes(B, S, H, D, vsa.VSA_BF16 if cfg["dtype"] == "bf16" else vsa.VSA_F32,
+                                           flags)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        vsa.vsa_classify_tiles(g, layout, masks, Bq, Bk, out=tiles, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles, flags=flags, o=o, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    cls_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    fwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    attn_ms = float(np.mean(fwd_ms))
+
+    f_exec = 4.0 * D * executed_pairs(tiles, head_map, B, S)
+    f_kept = 4.0 * D * kept_pairs(g, masks, B)
+    f_dense = 4.0 * D * float(S) * S * H * B
+    value = f_exec / (ms_step * 1e-3) / 1e12
+    achieved = f_exec / (attn_ms * 1e-3) / 1e12
+
+    dense = {}
+    if not args.no_dense:
+        all_masks = [W.mask_all()] * H
+        dt_tiles = vsa.vsa_classify_tiles(g, layout, all_masks, Bq, Bk, device=dev, with_cls=False)
+        for _ in range(2):
+            vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, all_masks, dt_tiles, flags=flags, o=o, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_dense = 3
+        e0.record(stream)
+        for _ in range(n_dense):
+            vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, all_masks, dt_tiles, flags=flags, o=o, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        d_ms = e0.elapsed_time(e1) / n_dense
+        dense = {"dense_ms_per_call": round(d_ms, 3), "speedup_vs_dense": round(d_ms / attn_ms, 3),
+                 "dense_tflops": round(f_dense / (d_ms * 1e-3) / 1e12, 1)}
+        del dt_tiles
+
+    khash = kernel_hash()
+    traffic = traffic_from_profiles(khash, 1)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.config, "B": B, "S": S, "H": H, "D": D, "grid": [g["T"], g["Hg"], g["Wg"]],
+                   "layout": layout, "Bq": Bq, "Bk": Bk, "masks": sorted({m["kind"] for m in masks}),
+                   "unique_masks": U, "flags": flags},
+        "attn_ms_per_call": round(attn_ms, 4),
+        "attn_ms_p10_p90": [round(float(np.percentile(fwd_ms, 10)), 4), round(float(np.percentile(fwd_ms, 90)), 4)],
+        "classify_ms": round(float(np.mean(cls_ms)), 4),
+        "tflops_executed_attn": round(achieved, 2),
+        "pct_of_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
+        "tflops_kept": round(f_kept / (attn_ms * 1e-3) / 1e12, 2),
+        "tflops_dense_equiv": round(f_dense / (attn_ms * 1e-3) / 1e12, 2),
+        "executed_tflop": round(f_exec / 1e12, 3),
+        "kept_tflop": round(f_kept / 1e12, 3),
+        "dense_tflop": round(f_dense / 1e12, 3),
+        **dense,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_fwd_bf16_kernel", "kernel_hash": khash},
+    }
+    if not args.no_cpu and layout == "frame":
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, tiles, head_map)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
