@@ -7,43 +7,135 @@
 // masking when nothing needs masking"); both feed one online softmax per query row, the
 // running max/sum merge of the DSA study guide, section 18.
 //
-// CDNA4 mapping.  One workgroup = one (b, h, query tile) of Bq = 32*NW rows, NW waves of
-// 64 lanes, each wave owning 32 query rows.  The kernel computes the transposed products
-//     S^T = K Q^T      (v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q in VGPRs)
-//     O^T += V^T P^T   (A = V^T rows from LDS, B = P^T straight from the S^T registers)
-// so that a lane's accumulator column is one query row: the row max and row sum of the
-// online softmax are in-register reductions plus one exchange with the lane 32 apart,
-// and P never leaves registers.  K rows are stored in LDS in the order the S^T output
-// layout wants (bits 2 and 3 of the row index swapped), so the 16 S^T values a lane holds
-// per 32-key block are keys 8g..8g+7 and 16+8g..16+8g+7 (g = lane/32): exactly the
-// 8 consecutive k-slots the P^T operand of the next MFMA needs.  V is transposed once
-// per tile while it is staged into LDS.  Both LDS tiles use XOR swizzles so that the
-// 16-byte operand reads and the staging writes spread over all banks.
-// K/V tiles are prefetched into registers one tile ahead while the current tile computes.
-#include "mfma_tile.h"
+// CDNA4 mapping.
+//  * One workgroup = one (b, h, query tile of Bq = 32*NW rows); NW waves of 64 lanes,
+//    each wave owns 32 query rows.  The kernel forms the transposed products
+//        S^T = K Q^T     (v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q in VGPRs)
+//        O^T += V^T P^T  (A = V columns read with ds_read_b64_tr_b16, B = P^T from the
+//                         S^T registers)
+//    so each lane's accumulator column is one query row: the softmax row max and row sum
+//    are in-register reductions plus one v_permlane32_swap with the lane 32 apart, and
+//    P never leaves registers.
+//  * K and V tiles (64 keys) move HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging), double-buffered: the loads of tile i+1 are in flight while tile i computes.
+//    K rows are stored with bits 2 and 3 of the row index swapped, so that the S^T output
+//    layout hands every lane 8 consecutive keys per register half: exactly the 8
+//    consecutive k-slots of the P^T operand.  V stays row-major; the transposing LDS read
+//    delivers the V^T operand.  16-byte chunks are XOR-swizzled per row so that the
+//    operand reads spread over all LDS banks (the DMA writes are contiguous anyway).
+//  * The running max is refreshed lazily: the accumulator is rescaled only when a row's
+//    tile max exceeds the reference by more than 2^8 in exp2 units (any lane of the
+//    wave), which keeps every probability <= 256 and the result exact up to rounding.
+//  * 2 waves per SIMD (register budget 256), so the MFMA work of one wave overlaps the
+//    softmax VALU work of another.
+#include <type_traits>
+
+#include "vsa_geom.h"
 
 namespace vsa {
 
 namespace {
 
-using namespace mfma;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int BK = 64;
+constexpr float kLazyLog2 = 8.0f;  // rescale only when the max grows by more than 2^8
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdArgs a, MaskTable masks,
-                                                                HeadMap hm) {
-  constexpr int NT = NW * 64;
-  constexpr int KSTEPS = D / 16;
-  constexpr int DB = D / 32;
+struct Cfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int ROWB = D * 2;                   // bytes of one K/V row
+  static constexpr int CH = D / 8;                     // 16-byte chunks per row
+  static constexpr int TILE_B = BK * ROWB;             // one K (or V) tile
+  static constexpr int STAGE_B = 2 * TILE_B;           // K + V
+  static constexpr int ROWS_PER_DMA = 1024 / ROWB;     // rows written by one wave-wide DMA
+  static constexpr int DMA_PER_TENSOR = BK / ROWS_PER_DMA;
+  static constexpr int NI = DMA_PER_TENSOR / NW;       // DMAs per wave per tensor per tile
+  static constexpr int ROWS_PER_BANKLINE = 256 / ROWB; // rows sharing one 256-byte bank line
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DB = D / 32;
+  static_assert(NI >= 1 && DMA_PER_TENSOR % NW == 0, "DMA split");
+};
 
-  __shared__ TileSmem<D> sm;
+__device__ __forceinline__ int swap_bits23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// K chunk swizzle: the 16 rows read by one quarter-wave land on distinct banks
+template <int D, int NW>
+__device__ __forceinline__ int ksw(int row) {
+  using C = Cfg<D, NW>;
+  return (row / C::ROWS_PER_BANKLINE) & (C::CH - 1);
+}
+// V chunk swizzle: the 4 rows of one transposing read land on distinct 64-byte segments
+template <int D, int NW>
+__device__ __forceinline__ int vsw(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One wave-wide 16-byte-per-lane DMA from global memory into LDS at m0 + 16*lane
+// (global_load_lds_dwordx4).  Issued through asm so that the compiler does not guard
+// every later LDS read with a wait for all DMAs in flight: the kernel waits for the
+// DMAs of a stage itself (wait_vmcnt) before the barrier that publishes the stage.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory", "m0");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release fence
+// would also wait for every DMA in flight).  LDS reads issued before it are complete
+// (lgkmcnt(0)); DMA completion is waited for explicitly with wait_vmcnt.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const int32_t* __restrict__ n_bnd_p,
+                          const int32_t* __restrict__ full_idx_p, const int32_t* __restrict__ bnd_idx_p,
+                          MaskTable masks, HeadMap hm) {
+  using C = Cfg<D, NW>;
+  constexpr int KSTEPS = C::KSTEPS;
+  constexpr int DB = C::DB;
+  // two stage buffers as separate objects, so the compiler can tell the DMA into one
+  // from the operand reads of the other and does not serialise them
+  __shared__ __attribute__((aligned(1024))) char smem0[C::STAGE_B];
+  __shared__ __attribute__((aligned(1024))) char smem1[C::STAGE_B];
 
   const Geom& g = a.g;
   const int S = a.S, H = a.H;
   const int Bq = 32 * NW;
 
   // ---- workgroup -> (b, h, query tile).  Workgroups are dealt to the 8 XCDs
-  // round-robin; XCD x takes query tiles [x*cq, (x+1)*cq) of every head, so the work
-  // of each XCD has the same head mix and its resident workgroups share K/V in L2. ----
+  // round-robin; XCD x takes query tiles [x*cq, (x+1)*cq) of every head, so every XCD
+  // sees the same head mix and its resident workgroups share K/V in its L2. ----
   const int cq = (a.nQ + 7) / 8;
   const int xcd = blockIdx.x & 7;
   const int kk = blockIdx.x >> 3;
@@ -58,22 +150,24 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdArgs a, MaskT
   const size_t lrow = (size_t)slot * a.nQ + qt;
   // list lengths and entries are clamped to the list row, so malformed lists cannot
   // send a load outside the tensors
-  const int nf = imin(imax(a.n_full[lrow], 0), a.nK);
-  const int nb = imin(imax(a.n_bnd[lrow], 0), a.nK);
-  const int32_t* full_list = a.full_idx + lrow * a.nK;
-  const int32_t* bnd_list = a.bnd_idx + lrow * a.nK;
+  // (the lists come in as read-only, non-aliased arguments so that the uniform loads
+  // below are scalar loads and never wait on the vector-memory counter)
+  const int nf = imin(imax(n_full_p[lrow], 0), a.nK);
+  const int nb = imin(imax(n_bnd_p[lrow], 0), a.nK);
+  const int32_t* full_list = full_idx_p + lrow * a.nK;
+  const int32_t* bnd_list = bnd_idx_p + lrow * a.nK;
   const int n_tiles = nf + nb;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g2 = lane >> 5;
   const int l32 = lane & 31;
 
   const uint16_t* qp = (const uint16_t*)a.q;
   const uint16_t* kp = (const uint16_t*)a.k;
   const uint16_t* vp = (const uint16_t*)a.v;
-  const size_t tok_stride = (size_t)H * D;
+  const int tok_stride = H * D;  // elements between consecutive tokens
   const size_t base_bh = ((size_t)b * S) * tok_stride + (size_t)h * D;
 
   // ---- this lane's query row: B operand of S^T = K Q^T ----
@@ -87,40 +181,182 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdArgs a, MaskT
   }
   const QueryPos qpos = make_query(g, m, qrow_c);
 
-  f32x16 acc[DB];
+  // ---- per-lane DMA sources (element offsets inside a tile) and LDS read offsets ----
+  int dma_k[C::NI], dma_v[C::NI];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  const float c_log2 = a.scale * 1.4426950408889634f;
+  for (int i = 0; i < C::NI; ++i) {
+    const int R = (wave * C::NI + i) * C::ROWS_PER_DMA + lane / C::CH;
+    const int p = lane % C::CH;
+    const int rk = swap_bits23(R);
+    dma_k[i] = rk * tok_stride + ((p ^ ksw<D, NW>(R)) * 8);
+    dma_v[i] = R * tok_stride + ((p ^ vsw<D, NW>(R)) * 8);
+  }
+  int kofs[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) kofs[s] = l32 * C::ROWB + (((2 * s + g2) ^ ksw<D, NW>(l32)) * 16);
+  int vofs[DB];
+  {
+    const int r4 = (lane & 15) >> 2;  // row within the 4-row group of one transposing read
+    const int gq = (lane >> 4) & 1;
+    const int c4 = lane & 3;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 4 * db + 2 * gq + (c4 >> 1);
+      vofs[db] = (8 * g2 + r4) * C::ROWB + ((chunk ^ vsw<D, NW>(r4)) * 16) + (c4 & 1) * 8;
+    }
+  }
 
-  Stager<D, NT> stg;
   auto tile_of = [&](int it) -> int {
     return imin(imax(it < nf ? full_list[it] : bnd_list[it - nf], 0), a.nK - 1);
   };
 
-  if (n_tiles > 0) stg.load(kp, vp, base_bh, tok_stride, tile_of(0) * BK, S, tid);
+  // issue the K and V DMAs of key tile kt into stage buffer `stage`
+  auto issue = [&](int kt, char* stage) {
+    const int c0 = kt * BK;
+    const uint16_t* kb = kp + base_bh + (size_t)c0 * tok_stride;
+    const uint16_t* vb = vp + base_bh + (size_t)c0 * tok_stride;
+    const bool tail = c0 + BK > S;
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) {
+      int ok = dma_k[i], ov = dma_v[i];
+      if (tail) {  // rows past S read row S-1: those keys are masked, their data finite
+        const int R = (wave * C::NI + i) * C::ROWS_PER_DMA + lane / C::CH;
+        const int p = lane % C::CH;
+        const int rk = imin(swap_bits23(R), S - 1 - c0);
+        ok = rk * tok_stride + ((p ^ ksw<D, NW>(R)) * 8);
+        ov = imin(R, S - 1 - c0) * tok_stride + ((p ^ vsw<D, NW>(R)) * 8);
+      }
+      const int dma = wave * C::NI + i;
+      dma16(kb + ok, lds_addr(stage + dma * 1024));
+      dma16(vb + ov, lds_addr(stage + C::TILE_B + dma * 1024));
+    }
+  };
 
-  for (int it = 0; it < n_tiles; ++it) {
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY;  // reference max, raw score units
+  float l_run = 0.f;        // this lane's share of the row sum
+  const float c_log2 = a.scale * 1.4426950408889634f;
+  const float lazy = kLazyLog2 / c_log2;
+
+  // one key tile: prefetch the next tile into the other stage, wait for this one,
+  // then S^T, mask, softmax and O^T update from this stage
+  auto step = [&](auto stage_tag, int it) {
+    constexpr int ST = decltype(stage_tag)::value;
+    char* cur = ST == 0 ? smem0 : smem1;
+    char* nxt = ST == 0 ? smem1 : smem0;
     const int kt = tile_of(it);
     const bool boundary = (it >= nf) || a.force_mask;
-    __syncthreads();
-    stg.store(sm, tid);
-    __syncthreads();
-    if (it + 1 < n_tiles) stg.load(kp, vp, base_bh, tok_stride, tile_of(it + 1) * BK, S, tid);
+    if (it + 1 < n_tiles) {
+      issue(tile_of(it + 1), nxt);
+      wait_vmcnt<2 * C::NI>();  // this tile's DMAs (issued one step earlier) are done
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_lds();
+    const char* sk = cur;
+    const char* sv = cur + C::TILE_B;
 
-    f32x16 st[2];
-    qk_tile<D>(sm, qf, l32, g2, st);
-    if (boundary) apply_mask(st, tile_row_mask(g, m, qpos, kt * BK, BK), g2);
-    uint32_t pk[2][8];
-    const float alpha = softmax_step(st, c_log2, m_run, l_run, pk);
+    // ---- S^T = K Q^T : two 32-key blocks; operands fetched a few steps ahead ----
+    f32x16 s[2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-    pv_tile<D>(sm, pk, l32, g2, acc);
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      u32x4 kf[KSTEPS];
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) kf[ks] = *(const u32x4*)(sk + kb * 32 * C::ROWB + kofs[ks]);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], s[kb], 0, 0, 0);
+    }
+    // ask the scheduler to issue each block's LDS reads ahead of its MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, KSTEPS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KSTEPS / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, KSTEPS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KSTEPS + KSTEPS / 2, 0);
+
+    // ---- element mask (boundary tiles): register (kb, i) holds key kb*32 + (i>>3)*16 +
+    // 8*g2 + (i&7); gather those 32 bits of the 64-bit tile mask into one word ----
+    if (boundary) {
+      const uint64_t bits = tile_row_mask(g, m, qpos, kt * BK, BK);
+      const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
+      const uint32_t w = ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
+                         (((hi >> (8 * g2)) & 0xffu) << 16) | (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int bit = kb * 16 + i;
+          const uint32_t f = (uint32_t)((int32_t)(w << (31 - bit)) >> 31);  // all ones if kept
+          s[kb][i] = __uint_as_float((__float_as_uint(s[kb][i]) & f) | (0xff800000u & ~f));
+        }
+    }
+
+    // ---- online softmax with lazy rescaling ----
+    float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
+    mt = pair_max(mt);
+    const bool grow = mt > m_run + lazy;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // lanes that do not grow keep their reference and scale by exactly 1 (their
+      // reference may still be -inf, which must not meet a -inf - -inf)
+      const float m_new = grow ? mt : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c_log2) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c_log2;
+    uint32_t pk[2][8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_log2, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c_log2, -mc));
+        lsum += p0 + p1;
+        pk[kb][i >> 1] = pack_bf16x2(p0, p1);
+      }
+    l_run += lsum;
+
+    // ---- O^T += V^T P^T : four 16-key steps ----
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kb = j >> 1, hf = j & 1;
+      const bf16x8 pf = __builtin_bit_cast(
+          bf16x8, u32x4{pk[kb][hf * 4 + 0], pk[kb][hf * 4 + 1], pk[kb][hf * 4 + 2], pk[kb][hf * 4 + 3]});
+      i16x4 v0[DB], v1[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char* base = sv + vofs[db] + j * 16 * C::ROWB;
+        v0[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+        v1[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * C::ROWB));
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 vf = __builtin_bit_cast(
+            bf16x8, u32x4{__builtin_bit_cast(u32x2, v0[db])[0], __builtin_bit_cast(u32x2, v0[db])[1],
+                          __builtin_bit_cast(u32x2, v1[db])[0], __builtin_bit_cast(u32x2, v1[db])[1]});
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
+      }
+    }
+    barrier_lds();  // every wave is done with this stage before it is refilled
+  };
+
+  if (n_tiles > 0) issue(tile_of(0), smem0);
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   // ---- epilogue: O = acc / l, lse = scale*m + ln(l) ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < S) {
     uint16_t* op = (uint16_t*)a.o + base_bh + (size_t)qrow * tok_stride;
@@ -135,8 +371,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdArgs a, MaskT
       }
     if (a.write_lse && g2 == 0) {
       const int lpos = a.lse_frame_major ? frame_index(g, qrow) : qrow;
-      a.lse[((size_t)b * H + h) * S + lpos] =
-          l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+      a.lse[((size_t)b * H + h) * S + lpos] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
     }
   }
 }
@@ -146,15 +381,16 @@ hipError_t launch_t(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
   const int cq = (a.nQ + 7) / 8;
   const long long n_blocks = 8LL * cq * a.B * a.H;
   if (n_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)n_blocks), dim3(NW * 64), 0, st,
-                     a, masks, hm);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)n_blocks), dim3(NW * 64), 0, st, a, a.n_full,
+                     a.n_bnd, a.full_idx, a.bnd_idx, masks, hm);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
-                            hipStream_t stream) {
+hipError_t launch_attn_bf16(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm, hipStream_t stream) {
+  // element offsets inside one (b, h) slab use 32-bit arithmetic
+  if ((long long)a.S * a.H * a.D >= (1LL << 31)) return hipErrorInvalidValue;
   const int nw = a.Bq / 32;
   if (a.D == 128) {
     if (nw == 2) return launch_t<128, 2>(a, masks, hm, stream);
