@@ -349,6 +349,9 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     barrier_lds();  // every wave is done with this stage before it is refilled
   };
 
+  // The query fragments must have landed before the first DMA is issued: the compiler
+  // counts only its own loads, so a later wait for them would also wait for the DMAs.
+  wait_vmcnt<0>();
   if (n_tiles > 0) issue(tile_of(0), smem0);
   for (int it = 0; it < n_tiles; it += 2) {
     step(std::integral_constant<int, 0>{}, it);
