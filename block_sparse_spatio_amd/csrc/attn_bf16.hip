@@ -41,6 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -102,9 +103,12 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
 // (lgkmcnt(0)); DMA completion is waited for explicitly with wait_vmcnt.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> one dword of bf16 (round to nearest even), one v_cvt_pk_bf16_f32
+__device__ __forceinline__ bf16x2 pack_bf16x2(float lo, float hi) {
+  return __builtin_convertvector(f32x2{lo, hi}, bf16x2);
 }
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -241,13 +245,13 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   const float lazy = kLazyLog2 / c_log2;
 
   // one key tile: prefetch the next tile into the other stage, wait for this one,
-  // then S^T, mask, softmax and O^T update from this stage
-  auto step = [&](auto stage_tag, int it) {
+  // then S^T, (mask,) softmax and O^T update from this stage
+  auto step = [&](auto stage_tag, auto bnd_tag, int it) {
     constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool BOUNDARY = decltype(bnd_tag)::value;
     char* cur = ST == 0 ? smem0 : smem1;
     char* nxt = ST == 0 ? smem1 : smem0;
     const int kt = tile_of(it);
-    const bool boundary = (it >= nf) || a.force_mask;
     if (it + 1 < n_tiles) {
       issue(tile_of(it + 1), nxt);
       wait_vmcnt<2 * C::NI>();  // this tile's DMAs (issued one step earlier) are done
@@ -258,7 +262,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     const char* sk = cur;
     const char* sv = cur + C::TILE_B;
 
-    // ---- S^T = K Q^T : two 32-key blocks; operands fetched a few steps ahead ----
+    // ---- S^T = K Q^T : two 32-key blocks ----
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -278,7 +282,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 
     // ---- element mask (boundary tiles): register (kb, i) holds key kb*32 + (i>>3)*16 +
     // 8*g2 + (i&7); gather those 32 bits of the 64-bit tile mask into one word ----
-    if (boundary) {
+    if constexpr (BOUNDARY) {
       const uint64_t bits = tile_row_mask(g, m, qpos, kt * BK, BK);
       const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
       const uint32_t w = ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
@@ -312,25 +316,26 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
       m_run = m_new;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * c_log2;
-    uint32_t pk[2][8];
-    float lsum = 0.f;
+    bf16x2 pk[2][8];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_log2, -mc));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c_log2, -mc));
-        lsum += p0 + p1;
         pk[kb][i >> 1] = pack_bf16x2(p0, p1);
+        // the row sum adds exactly the rounded probabilities the PV product uses
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[kb][i >> 1], ones, l_run, false);
       }
-    l_run += lsum;
 
     // ---- O^T += V^T P^T : four 16-key steps ----
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int kb = j >> 1, hf = j & 1;
       const bf16x8 pf = __builtin_bit_cast(
-          bf16x8, u32x4{pk[kb][hf * 4 + 0], pk[kb][hf * 4 + 1], pk[kb][hf * 4 + 2], pk[kb][hf * 4 + 3]});
+          bf16x8, u32x4{__builtin_bit_cast(uint32_t, pk[kb][hf * 4 + 0]), __builtin_bit_cast(uint32_t, pk[kb][hf * 4 + 1]),
+                        __builtin_bit_cast(uint32_t, pk[kb][hf * 4 + 2]), __builtin_bit_cast(uint32_t, pk[kb][hf * 4 + 3])});
       i16x4 v0[DB], v1[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -340,23 +345,42 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = __builtin_bit_cast(
-            bf16x8, u32x4{__builtin_bit_cast(u32x2, v0[db])[0], __builtin_bit_cast(u32x2, v0[db])[1],
-                          __builtin_bit_cast(u32x2, v1[db])[0], __builtin_bit_cast(u32x2, v1[db])[1]});
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
+        // concatenating the two halves lets both reads land in one register tuple
+        const i16x8 v = __builtin_shufflevector(v0[db], v1[db], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pf, acc[db], 0, 0, 0);
       }
     }
     barrier_lds();  // every wave is done with this stage before it is refilled
   };
 
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Full = std::integral_constant<bool, false>;
+  using Bnd = std::integral_constant<bool, true>;
   // The query fragments must have landed before the first DMA is issued: the compiler
   // counts only its own loads, so a later wait for them would also wait for the DMAs.
   wait_vmcnt<0>();
   if (n_tiles > 0) issue(tile_of(0), smem0);
-  for (int it = 0; it < n_tiles; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
+  // full tiles without any mask code, then boundary tiles; stages alternate throughout
+  const int n_full_path = a.force_mask ? 0 : nf;
+  int it = 0;
+  for (; it + 1 < n_full_path; it += 2) {
+    step(S0{}, Full{}, it);
+    step(S1{}, Full{}, it + 1);
   }
+  if (it < n_full_path) {
+    step(S0{}, Full{}, it);
+    ++it;
+    if (it < n_tiles) {
+      step(S1{}, Bnd{}, it);
+      ++it;
+    }
+  }
+  for (; it + 1 < n_tiles; it += 2) {
+    step(S0{}, Bnd{}, it);
+    step(S1{}, Bnd{}, it + 1);
+  }
+  if (it < n_tiles) step(S0{}, Bnd{}, it);
 
   // ---- epilogue: O = acc / l, lse = scale*m + ln(l) ----
   const float l_tot = pair_sum(l_run);
@@ -368,8 +392,8 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = db * 32 + r4 * 8 + g2 * 4;
-        const uint32_t w0 = pack_bf16x2(acc[db][r4 * 4 + 0] * inv, acc[db][r4 * 4 + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(acc[db][r4 * 4 + 2] * inv, acc[db][r4 * 4 + 3] * inv);
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, pack_bf16x2(acc[db][r4 * 4 + 0] * inv, acc[db][r4 * 4 + 1] * inv));
+        const uint32_t w1 = __builtin_bit_cast(uint32_t, pack_bf16x2(acc[db][r4 * 4 + 2] * inv, acc[db][r4 * 4 + 3] * inv));
         *(u32x2*)(op + d) = u32x2{w0, w1};
       }
     if (a.write_lse && g2 == 0) {
