@@ -128,10 +128,12 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   using C = Cfg<D, NW>;
   constexpr int KSTEPS = C::KSTEPS;
   constexpr int DB = C::DB;
-  // two stage buffers as separate objects, so the compiler can tell the DMA into one
-  // from the operand reads of the other and does not serialise them
-  __shared__ __attribute__((aligned(1024))) char smem0[C::STAGE_B];
-  __shared__ __attribute__((aligned(1024))) char smem1[C::STAGE_B];
+  // K and V rings of two tiles each, as separate objects so that the compiler can tell
+  // a DMA into one buffer from the operand reads of another
+  __shared__ __attribute__((aligned(1024))) char kbuf0[C::TILE_B];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[C::TILE_B];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[C::TILE_B];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[C::TILE_B];
 
   const Geom& g = a.g;
   const int S = a.S, H = a.H;
@@ -152,10 +154,10 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   const int slot = hm.slot[h];
   const DevMask m = masks.m[slot];
   const size_t lrow = (size_t)slot * a.nQ + qt;
-  // list lengths and entries are clamped to the list row, so malformed lists cannot
-  // send a load outside the tensors
-  // (the lists come in as read-only, non-aliased arguments so that the uniform loads
-  // below are scalar loads and never wait on the vector-memory counter)
+  // List lengths and entries are clamped to the list row, so malformed lists cannot
+  // send a load outside the tensors.  The lists come in as read-only, non-aliased
+  // arguments so that these uniform loads are scalar loads that never wait on the
+  // vector-memory counter.
   const int nf = imin(imax(n_full_p[lrow], 0), a.nK);
   const int nb = imin(imax(n_bnd_p[lrow], 0), a.nK);
   const int32_t* full_list = full_idx_p + lrow * a.nK;
@@ -214,25 +216,35 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     return imin(imax(it < nf ? full_list[it] : bnd_list[it - nf], 0), a.nK - 1);
   };
 
-  // issue the K and V DMAs of key tile kt into stage buffer `stage`
-  auto issue = [&](int kt, char* stage) {
+  // DMA of the K (or V) rows of key tile kt into one ring buffer
+  auto issue = [&](int kt, char* buf, bool is_v) {
     const int c0 = kt * BK;
-    const uint16_t* kb = kp + base_bh + (size_t)c0 * tok_stride;
-    const uint16_t* vb = vp + base_bh + (size_t)c0 * tok_stride;
+    const uint16_t* src = (is_v ? vp : kp) + base_bh + (size_t)c0 * tok_stride;
     const bool tail = c0 + BK > S;
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) {
-      int ok = dma_k[i], ov = dma_v[i];
+      int off = is_v ? dma_v[i] : dma_k[i];
       if (tail) {  // rows past S read row S-1: those keys are masked, their data finite
         const int R = (wave * C::NI + i) * C::ROWS_PER_DMA + lane / C::CH;
         const int p = lane % C::CH;
-        const int rk = imin(swap_bits23(R), S - 1 - c0);
-        ok = rk * tok_stride + ((p ^ ksw<D, NW>(R)) * 8);
-        ov = imin(R, S - 1 - c0) * tok_stride + ((p ^ vsw<D, NW>(R)) * 8);
+        off = is_v ? imin(R, S - 1 - c0) * tok_stride + ((p ^ vsw<D, NW>(R)) * 8)
+                   : imin(swap_bits23(R), S - 1 - c0) * tok_stride + ((p ^ ksw<D, NW>(R)) * 8);
       }
-      const int dma = wave * C::NI + i;
-      dma16(kb + ok, lds_addr(stage + dma * 1024));
-      dma16(vb + ov, lds_addr(stage + C::TILE_B + dma * 1024));
+      dma16(src + off, lds_addr(buf + (wave * C::NI + i) * 1024));
+    }
+  };
+
+  // S^T (64 keys x this wave's 32 queries) = K Q^T from one K buffer
+  auto qk = [&](const char* kb_, f32x16* s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      u32x4 kf[KSTEPS];
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) kf[ks] = *(const u32x4*)(kb_ + kb * 32 * C::ROWB + kofs[ks]);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], s[kb], 0, 0, 0);
     }
   };
 
@@ -243,66 +255,51 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   float l_run = 0.f;        // this lane's share of the row sum
   const float c_log2 = a.scale * 1.4426950408889634f;
   const float lazy = kLazyLog2 / c_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // one key tile: prefetch the next tile into the other stage, wait for this one,
-  // then S^T, (mask,) softmax and O^T update from this stage
-  auto step = [&](auto stage_tag, auto bnd_tag, int it) {
-    constexpr int ST = decltype(stage_tag)::value;
+  // ---- software pipeline over the listed key tiles.  Step i: K(i+1) and V(i) are in
+  // LDS; the step prefetches K(i+2) and V(i+1), computes S(i+1) = K(i+1) Q^T on the
+  // matrix cores while the vector units turn S(i) into probabilities, then adds
+  // P(i) V(i).  One barrier per step: after it, every wave has finished the previous
+  // step (so its buffers may be refilled) and every DMA of this step's inputs landed.
+  f32x16 s_cur[2];
+  auto step = [&](auto par_tag, auto bnd_tag, int it) {
+    constexpr int P = decltype(par_tag)::value;     // it & 1
     constexpr bool BOUNDARY = decltype(bnd_tag)::value;
-    char* cur = ST == 0 ? smem0 : smem1;
-    char* nxt = ST == 0 ? smem1 : smem0;
+    char* k_use = P == 0 ? kbuf1 : kbuf0;   // K(it+1)
+    char* k_fill = P == 0 ? kbuf0 : kbuf1;  // <- K(it+2)
+    char* v_use = P == 0 ? vbuf0 : vbuf1;   // V(it)
+    char* v_fill = P == 0 ? vbuf1 : vbuf0;  // <- V(it+1)
     const int kt = tile_of(it);
-    if (it + 1 < n_tiles) {
-      issue(tile_of(it + 1), nxt);
-      wait_vmcnt<2 * C::NI>();  // this tile's DMAs (issued one step earlier) are done
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     barrier_lds();
-    const char* sk = cur;
-    const char* sv = cur + C::TILE_B;
+    if (it + 2 < n_tiles) issue(tile_of(it + 2), k_fill, false);
+    if (it + 1 < n_tiles) issue(tile_of(it + 1), v_fill, true);
 
-    // ---- S^T = K Q^T : two 32-key blocks ----
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      u32x4 kf[KSTEPS];
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) kf[ks] = *(const u32x4*)(sk + kb * 32 * C::ROWB + kofs[ks]);
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], s[kb], 0, 0, 0);
-    }
-    // ask the scheduler to issue each block's LDS reads ahead of its MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, KSTEPS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, KSTEPS / 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, KSTEPS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, KSTEPS + KSTEPS / 2, 0);
-
-    // ---- element mask (boundary tiles): register (kb, i) holds key kb*32 + (i>>3)*16 +
-    // 8*g2 + (i&7); gather those 32 bits of the 64-bit tile mask into one word ----
+    // element mask of this tile (boundary tiles): register (kb, i) holds key
+    // kb*32 + (i>>3)*16 + 8*g2 + (i&7); gather those 32 bits of the tile mask
+    uint32_t w = ~0u;
     if constexpr (BOUNDARY) {
       const uint64_t bits = tile_row_mask(g, m, qpos, kt * BK, BK);
       const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
-      const uint32_t w = ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
-                         (((hi >> (8 * g2)) & 0xffu) << 16) | (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
+      w = ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
+          (((hi >> (8 * g2)) & 0xffu) << 16) | (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int bit = kb * 16 + i;
           const uint32_t f = (uint32_t)((int32_t)(w << (31 - bit)) >> 31);  // all ones if kept
-          s[kb][i] = __uint_as_float((__float_as_uint(s[kb][i]) & f) | (0xff800000u & ~f));
+          s_cur[kb][i] = __uint_as_float((__float_as_uint(s_cur[kb][i]) & f) | (0xff800000u & ~f));
         }
     }
 
-    // ---- online softmax with lazy rescaling ----
-    float mt = fmaxf(s[0][0], s[0][1]);
+    // running max with lazy rescaling
+    float mt = fmaxf(s_cur[0][0], s_cur[0][1]);
 #pragma unroll
-    for (int i = 2; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
+    for (int i = 2; i < 16; ++i) mt = fmaxf(mt, s_cur[0][i]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s_cur[1][i]);
     mt = pair_max(mt);
     const bool grow = mt > m_run + lazy;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -316,20 +313,25 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
       m_run = m_new;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * c_log2;
+
+    // S(it+1) on the matrix cores, interleaved with the exponentials of S(it).  On the
+    // last tile the product runs on the stale buffer and is discarded: keeping it
+    // unconditional keeps it in one scheduling region with the exponentials.
+    f32x16 s_next[2];
+    qk(k_use, s_next);
     bf16x2 pk[2][8];
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_log2, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c_log2, -mc));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][i], c_log2, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][i + 1], c_log2, -mc));
         pk[kb][i >> 1] = pack_bf16x2(p0, p1);
         // the row sum adds exactly the rounded probabilities the PV product uses
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[kb][i >> 1], ones, l_run, false);
       }
 
-    // ---- O^T += V^T P^T : four 16-key steps ----
+    // O^T += V(it)^T P(it)^T : four 16-key steps
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int kb = j >> 1, hf = j & 1;
@@ -339,7 +341,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
       i16x4 v0[DB], v1[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char* base = sv + vofs[db] + j * 16 * C::ROWB;
+        const char* base = v_use + vofs[db] + j * 16 * C::ROWB;
         v0[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
         v1[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * C::ROWB));
       }
@@ -350,37 +352,47 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pf, acc[db], 0, 0, 0);
       }
     }
-    barrier_lds();  // every wave is done with this stage before it is refilled
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   using Full = std::integral_constant<bool, false>;
   using Bnd = std::integral_constant<bool, true>;
   // The query fragments must have landed before the first DMA is issued: the compiler
   // counts only its own loads, so a later wait for them would also wait for the DMAs.
   wait_vmcnt<0>();
-  if (n_tiles > 0) issue(tile_of(0), smem0);
-  // full tiles without any mask code, then boundary tiles; stages alternate throughout
+  if (n_tiles > 0) {
+    // prologue: S(0) from K(0) in kbuf0; K(1) -> kbuf1 and V(0) -> vbuf0, which is
+    // where step 0 expects them
+    issue(tile_of(0), kbuf0, false);
+    wait_vmcnt<0>();
+    barrier_lds();
+    if (n_tiles > 1) issue(tile_of(1), kbuf1, false);
+    issue(tile_of(0), vbuf0, true);
+    qk(kbuf0, s_cur);
+  }
+  // full tiles without any mask code, then boundary tiles; parity alternates throughout
   const int n_full_path = a.force_mask ? 0 : nf;
   int it = 0;
   for (; it + 1 < n_full_path; it += 2) {
-    step(S0{}, Full{}, it);
-    step(S1{}, Full{}, it + 1);
+    step(P0{}, Full{}, it);
+    step(P1{}, Full{}, it + 1);
   }
   if (it < n_full_path) {
-    step(S0{}, Full{}, it);
+    step(P0{}, Full{}, it);
     ++it;
     if (it < n_tiles) {
-      step(S1{}, Bnd{}, it);
+      step(P1{}, Bnd{}, it);
       ++it;
     }
   }
   for (; it + 1 < n_tiles; it += 2) {
-    step(S0{}, Bnd{}, it);
-    step(S1{}, Bnd{}, it + 1);
+    step(P0{}, Bnd{}, it);
+    step(P1{}, Bnd{}, it + 1);
   }
-  if (it < n_tiles) step(S0{}, Bnd{}, it);
+  if (it < n_tiles) step(P0{}, Bnd{}, it);
 
   // ---- epilogue: O = acc / l, lse = scale*m + ln(l) ----
   const float l_tot = pair_sum(l_run);
