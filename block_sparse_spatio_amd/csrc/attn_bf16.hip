@@ -90,12 +90,12 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// One wave-wide 16-byte-per-lane DMA from global memory into LDS at m0 + 16*lane
-// (global_load_lds_dwordx4).  Issued through asm so that the compiler does not guard
+// One wave-wide 16-byte-per-lane DMA from global memory (wave-uniform base + per-lane
+// 32-bit byte offset) into LDS at m0 + 16*lane (global_load_lds_dwordx4).  Issued through asm so that the compiler does not guard
 // every later LDS read with a wait for all DMAs in flight: the kernel waits for the
 // DMAs of a stage itself (wait_vmcnt) before the barrier that publishes the stage.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (whose release fence
@@ -194,8 +194,8 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     const int R = (wave * C::NI + i) * C::ROWS_PER_DMA + lane / C::CH;
     const int p = lane % C::CH;
     const int rk = swap_bits23(R);
-    dma_k[i] = rk * tok_stride + ((p ^ ksw<D, NW>(R)) * 8);
-    dma_v[i] = R * tok_stride + ((p ^ vsw<D, NW>(R)) * 8);
+    dma_k[i] = 2 * (rk * tok_stride + ((p ^ ksw<D, NW>(R)) * 8));  // bytes
+    dma_v[i] = 2 * (R * tok_stride + ((p ^ vsw<D, NW>(R)) * 8));
   }
   int kofs[KSTEPS];
 #pragma unroll
@@ -220,17 +220,19 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   auto issue = [&](int kt, char* buf, bool is_v) {
     const int c0 = kt * BK;
     const uint16_t* src = (is_v ? vp : kp) + base_bh + (size_t)c0 * tok_stride;
-    const bool tail = c0 + BK > S;
+    const uint32_t lds0 = lds_addr(buf + wave * C::NI * 1024);
+    if (c0 + BK <= S) {
 #pragma unroll
-    for (int i = 0; i < C::NI; ++i) {
-      int off = is_v ? dma_v[i] : dma_k[i];
-      if (tail) {  // rows past S read row S-1: those keys are masked, their data finite
+      for (int i = 0; i < C::NI; ++i) dma16(src, is_v ? dma_v[i] : dma_k[i], lds0 + i * 1024);
+    } else {  // tail tile: rows past S read row S-1 (those keys are masked, data finite)
+#pragma unroll
+      for (int i = 0; i < C::NI; ++i) {
         const int R = (wave * C::NI + i) * C::ROWS_PER_DMA + lane / C::CH;
         const int p = lane % C::CH;
-        off = is_v ? imin(R, S - 1 - c0) * tok_stride + ((p ^ vsw<D, NW>(R)) * 8)
-                   : imin(swap_bits23(R), S - 1 - c0) * tok_stride + ((p ^ ksw<D, NW>(R)) * 8);
+        const int off = is_v ? imin(R, S - 1 - c0) * tok_stride + ((p ^ vsw<D, NW>(R)) * 8)
+                             : imin(swap_bits23(R), S - 1 - c0) * tok_stride + ((p ^ ksw<D, NW>(R)) * 8);
+        dma16(src, 2 * off, lds0 + i * 1024);
       }
-      dma16(src + off, lds_addr(buf + (wave * C::NI + i) * 1024));
     }
   };
 
@@ -263,6 +265,8 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   // P(i) V(i).  One barrier per step: after it, every wave has finished the previous
   // step (so its buffers may be refilled) and every DMA of this step's inputs landed.
   f32x16 s_cur[2];
+  // key tiles it, it+1, it+2 (uniform); the index of it+3 is loaded one step ahead
+  int kt0 = 0, kt1 = 0, kt2 = 0;
   auto step = [&](auto par_tag, auto bnd_tag, int it) {
     constexpr int P = decltype(par_tag)::value;     // it & 1
     constexpr bool BOUNDARY = decltype(bnd_tag)::value;
@@ -270,11 +274,12 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     char* k_fill = P == 0 ? kbuf0 : kbuf1;  // <- K(it+2)
     char* v_use = P == 0 ? vbuf0 : vbuf1;   // V(it)
     char* v_fill = P == 0 ? vbuf1 : vbuf0;  // <- V(it+1)
-    const int kt = tile_of(it);
+    const int kt = kt0;
+    const int kt3 = it + 3 < n_tiles ? tile_of(it + 3) : 0;
     wait_vmcnt<0>();
     barrier_lds();
-    if (it + 2 < n_tiles) issue(tile_of(it + 2), k_fill, false);
-    if (it + 1 < n_tiles) issue(tile_of(it + 1), v_fill, true);
+    if (it + 2 < n_tiles) issue(kt2, k_fill, false);
+    if (it + 1 < n_tiles) issue(kt1, v_fill, true);
 
     // element mask of this tile (boundary tiles): register (kb, i) holds key
     // kb*32 + (i>>3)*16 + 8*g2 + (i&7); gather those 32 bits of the tile mask
@@ -354,6 +359,9 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     }
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
+    kt0 = kt1;
+    kt1 = kt2;
+    kt2 = kt3;
   };
 
   using P0 = std::integral_constant<int, 0>;
@@ -366,11 +374,14 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   if (n_tiles > 0) {
     // prologue: S(0) from K(0) in kbuf0; K(1) -> kbuf1 and V(0) -> vbuf0, which is
     // where step 0 expects them
-    issue(tile_of(0), kbuf0, false);
+    kt0 = tile_of(0);
+    kt1 = n_tiles > 1 ? tile_of(1) : 0;
+    kt2 = n_tiles > 2 ? tile_of(2) : 0;
+    issue(kt0, kbuf0, false);
     wait_vmcnt<0>();
     barrier_lds();
-    if (n_tiles > 1) issue(tile_of(1), kbuf1, false);
-    issue(tile_of(0), vbuf0, true);
+    if (n_tiles > 1) issue(kt1, kbuf1, false);
+    issue(kt0, vbuf0, true);
     qk(kbuf0, s_cur);
   }
   // full tiles without any mask code, then boundary tiles; parity alternates throughout
