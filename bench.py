@@ -232,9 +232,20 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream(dev)
 
+    # the sampled-query profiler is part of the step when the workload routes heads
+    profile = "candidates" in cfg
+    if profile:
+        sidx = torch.from_numpy(W.sample_rows(S, cfg["n_samples"], H, cfg["seed"] + 1)).to(dev)
+        pws = torch.empty(vsa.vsa_profile_workspace_bytes(B, S, H, D, cfg["n_samples"], len(cfg["candidates"])),
+                          dtype=torch.uint8, device=dev)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
+        if profile:
+            vsa.vsa_profile_heads(qd, kd, vd, g, layout, sidx, cfg["candidates"], workspace=pws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
         vsa.vsa_classify_tiles(g, layout, masks, Bq, Bk, out=tiles, stream=stream)
         if ev is not None:
             ev[1].record(stream)
@@ -245,7 +256,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -256,7 +267,8 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    cls_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    prof_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    cls_ms = [e[3].elapsed_time(e[1]) for e in evs]
     fwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
     attn_ms = float(np.mean(fwd_ms))
 
@@ -284,6 +296,25 @@ def main():
                  "dense_tflops": round(f_dense / (d_ms * 1e-3) / 1e12, 1)}
         del dt_tiles
 
+    extra = {}
+    if profile:
+        extra["profile_ms"] = round(float(np.mean(prof_ms)), 4)
+        extra["profile_kv_gbs"] = round(2.0 * B * S * H * D * 2 / (np.mean(prof_ms) * 1e-3) / 1e9, 1)
+    if layout == "tile":
+        # the tile-major reorder alone, on one tensor: HBM GB/s (read + write)
+        y = torch.empty_like(qd)
+        vsa.vsa_reorder_tokens(qd, g, dst=y, stream=stream)
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for _ in range(5):
+            vsa.vsa_reorder_tokens(qd, g, dst=y, stream=stream)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        r_ms = r0.elapsed_time(r1) / 5
+        extra["reorder_ms_per_tensor"] = round(r_ms, 4)
+        extra["reorder_gbs"] = round(2.0 * qd.numel() * qd.element_size() / (r_ms * 1e-3) / 1e9, 1)
+        del y
+
     khash = kernel_hash()
     traffic = traffic_from_profiles(khash, 1)
     rec = {
@@ -305,6 +336,7 @@ def main():
         "attn_ms_per_call": round(attn_ms, 4),
         "attn_ms_p10_p90": [round(float(np.percentile(fwd_ms, 10)), 4), round(float(np.percentile(fwd_ms, 90)), 4)],
         "classify_ms": round(float(np.mean(cls_ms)), 4),
+        **extra,
         "tflops_executed_attn": round(achieved, 2),
         "pct_of_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
         "tflops_kept": round(f_kept / (attn_ms * 1e-3) / 1e12, 2),
