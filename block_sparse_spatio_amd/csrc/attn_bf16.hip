@@ -11,8 +11,7 @@
 //  * One workgroup = one (b, h, query tile of Bq = 32*NW rows); NW waves of 64 lanes,
 //    each wave owns 32 query rows.  The kernel forms the transposed products
 //        S^T = K Q^T     (v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q in VGPRs)
-//        O^T += V^T P^T  (A = V columns read with ds_read_b64_tr_b16, B = P^T from the
-//                         S^T registers)
+//        O^T += V^T P^T  (A = V^T rows from LDS, B = P^T from the S^T registers)
 //    so each lane's accumulator column is one query row: the softmax row max and row sum
 //    are in-register reductions plus one v_permlane32_swap with the lane 32 apart, and
 //    P never leaves registers.
@@ -20,9 +19,10 @@
 //    staging), double-buffered: the loads of tile i+1 are in flight while tile i computes.
 //    K rows are stored with bits 2 and 3 of the row index swapped, so that the S^T output
 //    layout hands every lane 8 consecutive keys per register half: exactly the 8
-//    consecutive k-slots of the P^T operand.  V stays row-major; the transposing LDS read
-//    delivers the V^T operand.  16-byte chunks are XOR-swizzled per row so that the
-//    operand reads spread over all LDS banks (the DMA writes are contiguous anyway).
+//    consecutive k-slots of the P^T operand.  V arrives pre-transposed (V^T, written by
+//    transpose.hip once per call), so both operands are plain 16-byte LDS reads at full
+//    LDS bandwidth.  16-byte chunks are XOR-swizzled per row so that the operand reads
+//    spread over all LDS banks (the DMA writes are contiguous anyway).
 //  * The running max is refreshed lazily: the accumulator is rescaled only when a row's
 //    tile max exceeds the reference by more than 2^8 in exp2 units (any lane of the
 //    wave), which keeps every probability <= 256 and the result exact up to rounding.
@@ -40,10 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int BK = 64;
 constexpr float kLazyLog2 = 8.0f;  // rescale only when the max grows by more than 2^8
@@ -72,11 +69,9 @@ __device__ __forceinline__ int ksw(int row) {
   using C = Cfg<D, NW>;
   return (row / C::ROWS_PER_BANKLINE) & (C::CH - 1);
 }
-// V chunk swizzle: the 4 rows of one transposing read land on distinct 64-byte segments
-template <int D, int NW>
-__device__ __forceinline__ int vsw(int row) {
-  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
+// V^T chunk swizzle (rows of 64 keys = 128 bytes, two rows per 256-byte bank line): the
+// 16 channel rows read by one quarter-wave land on distinct banks
+__device__ __forceinline__ int vtsw(int row) { return (row >> 1) & 7; }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
@@ -113,7 +108,7 @@ __device__ __forceinline__ bf16x2 pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -188,6 +183,9 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   const QueryPos qpos = make_query(g, m, qrow_c);
 
   // ---- per-lane DMA sources (element offsets inside a tile) and LDS read offsets ----
+  // K tile: row R of LDS holds key swap_bits23(R), 16-byte chunks swizzled by ksw(R).
+  // V^T tile (one contiguous D x 64 block in global memory): row d of LDS holds channel d
+  // (64 keys, 128 bytes), chunks swizzled by vtsw(d).
   int dma_k[C::NI], dma_v[C::NI];
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
@@ -195,59 +193,82 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     const int p = lane % C::CH;
     const int rk = swap_bits23(R);
     dma_k[i] = 2 * (rk * tok_stride + ((p ^ ksw<D, NW>(R)) * 8));  // bytes
-    dma_v[i] = 2 * (R * tok_stride + ((p ^ vsw<D, NW>(R)) * 8));
+    const int d = (wave * C::NI + i) * 8 + lane / 8;                // 8 V^T rows per DMA
+    dma_v[i] = 2 * (d * BK + (((lane % 8) ^ vtsw(d)) * 8));
   }
   int kofs[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) kofs[s] = l32 * C::ROWB + (((2 * s + g2) ^ ksw<D, NW>(l32)) * 16);
-  int vofs[DB];
-  {
-    const int r4 = (lane & 15) >> 2;  // row within the 4-row group of one transposing read
-    const int gq = (lane >> 4) & 1;
-    const int c4 = lane & 3;
+  int vofs[4];  // PV operand of 16-key step j: channel row l32 (+32*db), keys 16j + 8*g2 ..
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int chunk = 4 * db + 2 * gq + (c4 >> 1);
-      vofs[db] = (8 * g2 + r4) * C::ROWB + ((chunk ^ vsw<D, NW>(r4)) * 16) + (c4 & 1) * 8;
-    }
-  }
+  for (int j = 0; j < 4; ++j) vofs[j] = l32 * (BK * 2) + (((2 * j + g2) ^ vtsw(l32)) * 16);
 
   auto tile_of = [&](int it) -> int {
     return imin(imax(it < nf ? full_list[it] : bnd_list[it - nf], 0), a.nK - 1);
   };
 
-  // DMA of the K (or V) rows of key tile kt into one ring buffer
+  // DMA of the K rows (or V^T rows) of key tile kt into one ring buffer
+  const uint16_t* vtp = (const uint16_t*)a.vt + ((size_t)b * H + h) * D * a.s_pad;  // [s_pad/64][D][64]
   auto issue = [&](int kt, char* buf, bool is_v) {
     const int c0 = kt * BK;
-    const uint16_t* src = (is_v ? vp : kp) + base_bh + (size_t)c0 * tok_stride;
     const uint32_t lds0 = lds_addr(buf + wave * C::NI * 1024);
+    if (is_v) {  // V^T is padded to a multiple of 64 keys with zeros: no tail case
+      const uint16_t* src = vtp + (size_t)c0 * D;
+#pragma unroll
+      for (int i = 0; i < C::NI; ++i) dma16(src, dma_v[i], lds0 + i * 1024);
+      return;
+    }
+    const uint16_t* src = kp + base_bh + (size_t)c0 * tok_stride;
     if (c0 + BK <= S) {
 #pragma unroll
-      for (int i = 0; i < C::NI; ++i) dma16(src, is_v ? dma_v[i] : dma_k[i], lds0 + i * 1024);
+      for (int i = 0; i < C::NI; ++i) dma16(src, dma_k[i], lds0 + i * 1024);
     } else {  // tail tile: rows past S read row S-1 (those keys are masked, data finite)
 #pragma unroll
       for (int i = 0; i < C::NI; ++i) {
         const int R = (wave * C::NI + i) * C::ROWS_PER_DMA + lane / C::CH;
         const int p = lane % C::CH;
-        const int off = is_v ? imin(R, S - 1 - c0) * tok_stride + ((p ^ vsw<D, NW>(R)) * 8)
-                             : imin(swap_bits23(R), S - 1 - c0) * tok_stride + ((p ^ ksw<D, NW>(R)) * 8);
+        const int off = imin(swap_bits23(R), S - 1 - c0) * tok_stride + ((p ^ ksw<D, NW>(R)) * 8);
         dma16(src, 2 * off, lds0 + i * 1024);
       }
     }
   };
 
-  // S^T (64 keys x this wave's 32 queries) = K Q^T from one K buffer
+  // S^T (64 keys x this wave's 32 queries) = K Q^T from one K buffer.  The two 32-key
+  // halves alternate, so consecutive MFMAs never depend on each other.
   auto qk = [&](const char* kb_, f32x16* s) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      u32x4 kf[KSTEPS];
+    for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) kf[ks] = *(const u32x4*)(kb_ + kb * 32 * C::ROWB + kofs[ks]);
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 kf = *(const u32x4*)(kb_ + kb * 32 * C::ROWB + kofs[ks]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[ks], s[kb], 0, 0, 0);
+      }
+  };
+  // Register (kb, i) of S^T holds key kb*32 + (i>>3)*16 + 8*g2 + (i&7) of the tile: gather
+  // those 32 bits of the tile's 64-bit row mask (one word per lane).
+  auto mask_word = [&](int kt) -> uint32_t {
+    const uint64_t bits = tile_row_mask(g, m, qpos, kt * BK, BK);
+    const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
+    return ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
+           (((hi >> (8 * g2)) & 0xffu) << 16) | (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
+  };
+  auto apply_mask = [&](f32x16* s, uint32_t w) {
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], s[kb], 0, 0, 0);
-    }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int bit = kb * 16 + i;
+        const uint32_t f = (uint32_t)((int32_t)(w << (31 - bit)) >> 31);  // all ones if kept
+        s[kb][i] = __uint_as_float((__float_as_uint(s[kb][i]) & f) | (0xff800000u & ~f));
+      }
+  };
+  auto row_max = [&](const f32x16* s) -> float {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mt = __builtin_elementwise_maximum(mt, s[i >> 4][i & 15]);
+    return pair_max(mt);
   };
 
   f32x16 acc[DB];
@@ -259,58 +280,52 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   const float lazy = kLazyLog2 / c_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // ---- software pipeline over the listed key tiles.  Step i: K(i+1) and V(i) are in
-  // LDS; the step prefetches K(i+2) and V(i+1), computes S(i+1) = K(i+1) Q^T on the
-  // matrix cores while the vector units turn S(i) into probabilities, then adds
-  // P(i) V(i).  One barrier per step: after it, every wave has finished the previous
-  // step (so its buffers may be refilled) and every DMA of this step's inputs landed.
+  // ---- software pipeline over the listed key tiles.  Entering step i, S(i) is in
+  // registers (masked) with its row max, K(i+1) and V(i) are in LDS.  The step
+  // prefetches K(i+2) and V(i+1), then runs two stages, each an even interleave of
+  // matrix-core work and vector work:
+  //   A: S(i+1) = K(i+1) Q^T   with   P(i) = exp2(S(i) - max), row sums
+  //   B: O^T += V(i)^T P(i)^T  with   the element mask and row max of S(i+1)
+  // One barrier per step: after it, every wave has finished the previous step (so its
+  // buffers may be refilled) and every DMA of this step's inputs has landed.
   f32x16 s_cur[2];
+  float mt_cur = -INFINITY;
   // key tiles it, it+1, it+2 (uniform); the index of it+3 is loaded one step ahead
   int kt0 = 0, kt1 = 0, kt2 = 0;
-  auto step = [&](auto par_tag, auto bnd_tag, int it) {
-    constexpr int P = decltype(par_tag)::value;     // it & 1
-    constexpr bool BOUNDARY = decltype(bnd_tag)::value;
+  constexpr int NQK = 2 * KSTEPS;  // MFMAs of stage A
+  constexpr int NPV = 4 * DB;      // MFMAs of stage B
+  constexpr int EA = 32 / NQK;     // scores per lane exponentiated per stage-A MFMA
+  constexpr int EB = 32 / NPV;     // scores per lane max-reduced per stage-B MFMA
+  static_assert(EA % 2 == 0 && EB % 2 == 0, "score pairs");
+  // LDS operand of stage-A MFMA i (key half i&1, k-step i>>1) and of stage-B MFMA i
+  // (16-key step i/DB, channel block i%DB)
+  auto kread = [&](const char* kb_, int i) -> u32x4 {
+    return *(const u32x4*)(kb_ + (i & 1) * 32 * C::ROWB + kofs[i >> 1]);
+  };
+  auto vread = [&](const char* vb_, int i) -> u32x4 {
+    return *(const u32x4*)(vb_ + (i % DB) * 32 * (BK * 2) + vofs[i / DB]);
+  };
+  auto step = [&](auto par_tag, auto nbnd_tag, int it) {
+    constexpr int P = decltype(par_tag)::value;      // it & 1
+    constexpr bool NEXT_BND = decltype(nbnd_tag)::value;  // tile it+1 needs the element mask
     char* k_use = P == 0 ? kbuf1 : kbuf0;   // K(it+1)
     char* k_fill = P == 0 ? kbuf0 : kbuf1;  // <- K(it+2)
     char* v_use = P == 0 ? vbuf0 : vbuf1;   // V(it)
     char* v_fill = P == 0 ? vbuf1 : vbuf0;  // <- V(it+1)
-    const int kt = kt0;
     const int kt3 = it + 3 < n_tiles ? tile_of(it + 3) : 0;
     wait_vmcnt<0>();
     barrier_lds();
     if (it + 2 < n_tiles) issue(kt2, k_fill, false);
     if (it + 1 < n_tiles) issue(kt1, v_fill, true);
-
-    // element mask of this tile (boundary tiles): register (kb, i) holds key
-    // kb*32 + (i>>3)*16 + 8*g2 + (i&7); gather those 32 bits of the tile mask
-    uint32_t w = ~0u;
-    if constexpr (BOUNDARY) {
-      const uint64_t bits = tile_row_mask(g, m, qpos, kt * BK, BK);
-      const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
-      w = ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
-          (((hi >> (8 * g2)) & 0xffu) << 16) | (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int bit = kb * 16 + i;
-          const uint32_t f = (uint32_t)((int32_t)(w << (31 - bit)) >> 31);  // all ones if kept
-          s_cur[kb][i] = __uint_as_float((__float_as_uint(s_cur[kb][i]) & f) | (0xff800000u & ~f));
-        }
-    }
+    uint32_t w_next = ~0u;
+    if constexpr (NEXT_BND) w_next = mask_word(kt1);
 
     // running max with lazy rescaling
-    float mt = fmaxf(s_cur[0][0], s_cur[0][1]);
-#pragma unroll
-    for (int i = 2; i < 16; ++i) mt = fmaxf(mt, s_cur[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s_cur[1][i]);
-    mt = pair_max(mt);
-    const bool grow = mt > m_run + lazy;
+    const bool grow = mt_cur > m_run + lazy;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       // lanes that do not grow keep their reference and scale by exactly 1 (their
       // reference may still be -inf, which must not meet a -inf - -inf)
-      const float m_new = grow ? mt : m_run;
+      const float m_new = grow ? mt_cur : m_run;
       const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c_log2) : 1.f;
       l_run *= alpha;
 #pragma unroll
@@ -318,44 +333,70 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
       m_run = m_new;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * c_log2;
+    __builtin_amdgcn_sched_barrier(0);
 
-    // S(it+1) on the matrix cores, interleaved with the exponentials of S(it).  On the
-    // last tile the product runs on the stale buffer and is discarded: keeping it
-    // unconditional keeps it in one scheduling region with the exponentials.
-    f32x16 s_next[2];
-    qk(k_use, s_next);
-    bf16x2 pk[2][8];
+    // stage A.  On the last tile the product runs on the stale buffer and is discarded:
+    // keeping it unconditional keeps the stage straight-line code.  Chunk i issues the
+    // operand read of MFMA i+2, MFMA i, and the exponentials of EA scores; scheduling
+    // fences between chunks keep that order, so every LDS read has two MFMAs to land.
+    f32x16 s_next[2] = {f32x16{}, f32x16{}};
+    bf16x2 pk[16];  // P(it): pk[v/2] holds scores v, v+1 (v = kb*16 + register)
+    {
+      u32x4 kr[3];
+      kr[0] = kread(k_use, 0);
+      kr[1] = kread(k_use, 1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < NQK; ++i) {
+        if (i + 2 < NQK) kr[(i + 2) % 3] = kread(k_use, i + 2);
+        s_next[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[i % 3]),
+                                                                qf[i >> 1], s_next[i & 1], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][i], c_log2, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][i + 1], c_log2, -mc));
-        pk[kb][i >> 1] = pack_bf16x2(p0, p1);
-        // the row sum adds exactly the rounded probabilities the PV product uses
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[kb][i >> 1], ones, l_run, false);
+        for (int e = 0; e < EA; e += 2) {
+          const int v = i * EA + e;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][v & 15], c_log2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][(v & 15) + 1], c_log2, -mc));
+          pk[v >> 1] = pack_bf16x2(p0, p1);
+          // the row sum adds exactly the rounded probabilities the PV product uses
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[v >> 1], ones, l_run, false);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
 
-    // O^T += V(it)^T P(it)^T : four 16-key steps
+    // stage B: O^T += V(it)^T P(it)^T in four 16-key steps of DB MFMAs; chunk i also
+    // masks (boundary successor) and max-reduces EB scores of S(it+1)
+    {
+      u32x4 vr[3];
+      vr[0] = vread(v_use, 0);
+      vr[1] = vread(v_use, 1);
+      float mx = -INFINITY;
+      const uint32_t w = w_next;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kb = j >> 1, hf = j & 1;
-      const bf16x8 pf = __builtin_bit_cast(
-          bf16x8, u32x4{__builtin_bit_cast(uint32_t, pk[kb][hf * 4 + 0]), __builtin_bit_cast(uint32_t, pk[kb][hf * 4 + 1]),
-                        __builtin_bit_cast(uint32_t, pk[kb][hf * 4 + 2]), __builtin_bit_cast(uint32_t, pk[kb][hf * 4 + 3])});
-      i16x4 v0[DB], v1[DB];
+      for (int i = 0; i < NPV; ++i) {
+        if (i + 2 < NPV) vr[(i + 2) % 3] = vread(v_use, i + 2);
+        const int j = i / DB, db = i % DB;
+        const bf16x8 pf = __builtin_bit_cast(
+            bf16x8, u32x4{__builtin_bit_cast(uint32_t, pk[4 * j + 0]), __builtin_bit_cast(uint32_t, pk[4 * j + 1]),
+                          __builtin_bit_cast(uint32_t, pk[4 * j + 2]), __builtin_bit_cast(uint32_t, pk[4 * j + 3])});
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i % 3]), pf, acc[db], 0, 0, 0);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const char* base = v_use + vofs[db] + j * 16 * C::ROWB;
-        v0[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-        v1[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * C::ROWB));
+        for (int e = 0; e < EB; e += 2) {
+          const int v = i * EB + e;
+          float x0 = s_next[v >> 4][v & 15], x1 = s_next[v >> 4][(v & 15) + 1];
+          if constexpr (NEXT_BND) {
+            const uint32_t f0 = (uint32_t)((int32_t)(w << (31 - v)) >> 31);  // all ones if kept
+            const uint32_t f1 = (uint32_t)((int32_t)(w << (30 - v)) >> 31);
+            x0 = __uint_as_float((__float_as_uint(x0) & f0) | (0xff800000u & ~f0));
+            x1 = __uint_as_float((__float_as_uint(x1) & f1) | (0xff800000u & ~f1));
+            s_next[v >> 4][v & 15] = x0;
+            s_next[v >> 4][(v & 15) + 1] = x1;
+          }
+          // NaN-propagating maximum: v_maximum3_f32, no operand canonicalisation
+          mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, x0), x1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        // concatenating the two halves lets both reads land in one register tuple
-        const i16x8 v = __builtin_shufflevector(v0[db], v1[db], 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pf, acc[db], 0, 0, 0);
-      }
+      mt_cur = pair_max(mx);
     }
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
@@ -366,8 +407,11 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  using Full = std::integral_constant<bool, false>;
-  using Bnd = std::integral_constant<bool, true>;
+  using NextFull = std::integral_constant<bool, false>;
+  using NextBnd = std::integral_constant<bool, true>;
+  // full tiles (listed first) take no element mask, unless every tile is forced through
+  // the masked path
+  const int n_full_path = a.force_mask ? 0 : nf;
   // The query fragments must have landed before the first DMA is issued: the compiler
   // counts only its own loads, so a later wait for them would also wait for the DMAs.
   wait_vmcnt<0>();
@@ -383,27 +427,40 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     if (n_tiles > 1) issue(kt1, kbuf1, false);
     issue(kt0, vbuf0, true);
     qk(kbuf0, s_cur);
+    if (n_full_path == 0) apply_mask(s_cur, mask_word(kt0));
+    mt_cur = row_max(s_cur);
   }
-  // full tiles without any mask code, then boundary tiles; parity alternates throughout
-  const int n_full_path = a.force_mask ? 0 : nf;
+  // steps [0, n_full_path - 1) are followed by a full tile, steps up to n_tiles - 2 by
+  // a boundary tile; the last step's successor is never used.  Parity alternates.
+  const int last = n_tiles - 1;
+  const int end_full = imin(imax(n_full_path - 1, 0), imax(last, 0));
   int it = 0;
-  for (; it + 1 < n_full_path; it += 2) {
-    step(P0{}, Full{}, it);
-    step(P1{}, Full{}, it + 1);
+  for (; it + 1 < end_full; it += 2) {
+    step(P0{}, NextFull{}, it);
+    step(P1{}, NextFull{}, it + 1);
   }
-  if (it < n_full_path) {
-    step(P0{}, Full{}, it);
+  if (it < end_full) {
+    step(P0{}, NextFull{}, it);
     ++it;
-    if (it < n_tiles) {
-      step(P1{}, Bnd{}, it);
-      ++it;
-    }
   }
-  for (; it + 1 < n_tiles; it += 2) {
-    step(P0{}, Bnd{}, it);
-    step(P1{}, Bnd{}, it + 1);
+  if ((it & 1) && it < last) {
+    step(P1{}, NextBnd{}, it);
+    ++it;
   }
-  if (it < n_tiles) step(P0{}, Bnd{}, it);
+  for (; it + 1 < last; it += 2) {
+    step(P0{}, NextBnd{}, it);
+    step(P1{}, NextBnd{}, it + 1);
+  }
+  if (it < last) {
+    step(P0{}, NextBnd{}, it);
+    ++it;
+  }
+  if (it == last) {
+    if (it & 1)
+      step(P1{}, NextFull{}, it);
+    else
+      step(P0{}, NextFull{}, it);
+  }
 
   // ---- epilogue: O = acc / l, lse = scale*m + ln(l) ----
   const float l_tot = pair_sum(l_run);

@@ -1,0 +1,72 @@
+// V -> blocked V^T: [B][S][H][D] bf16 -> [B][H][S_pad/64][D][64] bf16, keys past S
+// zero-filled.
+//
+// The attention kernel reads its PV operand as V^T fragments (8 consecutive keys of one
+// channel per lane).  Transposing V once per call lets those fragments be plain 16-byte
+// LDS reads instead of transposing LDS reads, which run at half the LDS bandwidth; the
+// transpose itself is one HBM read and one HBM write of V.  Each 64-key block of one
+// head is stored as one contiguous D x 64 tile, so the attention kernel fetches a key
+// tile's V^T as a single contiguous 2*64*D-byte block.
+//
+// One workgroup per (b, h, 64-key block): the 64 x D block is read with 16-byte
+// coalesced loads (one 2*D-byte row per key), staged in LDS, and written as D rows of
+// 64 keys (128 contiguous bytes each).
+#include "vsa_internal.h"
+
+namespace vsa {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKeys = 64;
+constexpr int kThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* __restrict__ v,
+                                                               uint16_t* __restrict__ vt, int S, int H,
+                                                               int s_pad) {
+  __shared__ uint16_t tile[kKeys][D + 2];  // +2: odd word stride keeps the column reads spread
+  const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int k0 = kb * kKeys;
+  constexpr int CH = D / 8;  // 16-byte chunks per key row
+  for (int e = threadIdx.x; e < kKeys * CH; e += kThreads) {
+    const int r = e / CH, c = e % CH;
+    const int key = k0 + r;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (key < S) x = *(const u32x4*)(v + (((size_t)b * S + key) * H + h) * D + c * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[r][c * 8 + 2 * j] = (uint16_t)(x[j] & 0xffffu);
+      tile[r][c * 8 + 2 * j + 1] = (uint16_t)(x[j] >> 16);
+    }
+  }
+  __syncthreads();
+  // D rows x 8 chunks of 8 keys
+  for (int e = threadIdx.x; e < D * (kKeys / 8); e += kThreads) {
+    const int d = e / (kKeys / 8), c = e % (kKeys / 8);
+    u32x4 y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      y[j] = (uint32_t)tile[c * 8 + 2 * j][d] | ((uint32_t)tile[c * 8 + 2 * j + 1][d] << 16);
+    *(u32x4*)(vt + ((((size_t)b * H + h) * (s_pad / kKeys) + kb) * D + d) * kKeys + c * 8) = y;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_transpose_v(const void* v, void* vt, int32_t B, int32_t S, int32_t H, int32_t D,
+                              int32_t s_pad, hipStream_t stream) {
+  dim3 grid(s_pad / kKeys, H, B);
+  if (D == 128)
+    hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(kThreads), 0, stream, (const uint16_t*)v,
+                       (uint16_t*)vt, S, H, s_pad);
+  else if (D == 64)
+    hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(kThreads), 0, stream, (const uint16_t*)v,
+                       (uint16_t*)vt, S, H, s_pad);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace vsa

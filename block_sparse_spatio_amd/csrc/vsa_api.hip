@@ -224,12 +224,22 @@ vsa_status vsa_classify_tiles(const vsa_grid* grid, vsa_layout layout, const vsa
   return ok();
 }
 
+// bf16: V^T [B][H][D][S rounded up to 64] (the PV operand, transposed once per call);
+// with VSA_FWD_REORDER_IO, tile-major copies of q, k and v before it.
+static size_t vt_pad(int32_t S) { return ((size_t)S + 63) / 64 * 64; }
+static size_t fwd_ws_bytes(int32_t B, int32_t S, int32_t H, int32_t D, vsa_dtype dtype, int32_t flags) {
+  const size_t eb = elem_size(dtype);
+  size_t n = (flags & VSA_FWD_REORDER_IO) ? 3ull * B * S * H * D * eb : 0;
+  if (dtype == VSA_BF16) n += (size_t)B * H * D * vt_pad(S) * eb;
+  return n;
+}
+
 vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D, vsa_dtype dtype, int32_t flags,
                                    size_t* bytes) {
   if (!bytes) return fail(VSA_ERR_INVALID_ARG, "bytes is NULL");
   if (B <= 0 || S <= 0 || H <= 0 || D <= 0) return fail(VSA_ERR_INVALID_ARG, "B, S, H, D must be positive");
   if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  *bytes = (flags & VSA_FWD_REORDER_IO) ? 3ull * B * S * H * D * elem_size(dtype) : 0;
+  *bytes = fwd_ws_bytes(B, S, H, D, dtype, flags);
   return ok();
 }
 
@@ -264,15 +274,16 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
     return fail(VSA_ERR_INVALID_ARG, "VSA_FWD_REORDER_IO needs the tile-major layout");
   const size_t eb = elem_size(dtype);
   const size_t nelem = (size_t)B * S * H * D;
-  if (reorder) {
-    if (!workspace || ws_bytes < 3 * nelem * eb)
-      return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, 3 * nelem * eb);
-  }
   vsa::MaskTable table;
   vsa::HeadMap hm;
   int32_t U = 0;
   st = build_table(masks, H, grid, &table, &hm, &U);
   if (st != VSA_OK) return st;
+  const size_t need = fwd_ws_bytes(B, S, H, D, dtype, flags);
+  if (need && (!workspace || ws_bytes < need))
+    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if (need && ((uintptr_t)workspace & 15))
+    return fail(VSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
 
   vsa::FwdArgs a;
   memset(&a, 0, sizeof a);
@@ -305,7 +316,17 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   } else {
     a.q = q; a.k = k; a.v = v; a.o = o;
   }
-  hipError_t e = dtype == VSA_BF16 ? vsa::launch_attn_bf16(a, table, hm, hs) : vsa::launch_attn_f32(a, table, hm, hs);
+  hipError_t e;
+  if (dtype == VSA_BF16) {
+    a.s_pad = (int32_t)vt_pad(S);
+    void* vt = ws + (reorder ? 3 * nelem * eb : 0);
+    if ((e = vsa::launch_transpose_v(a.v, vt, B, S, H, D, a.s_pad, hs)) != hipSuccess)
+      return hip_fail(e, "transpose v");
+    a.vt = vt;
+    e = vsa::launch_attn_bf16(a, table, hm, hs);
+  } else {
+    e = vsa::launch_attn_f32(a, table, hm, hs);
+  }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (reorder) {
     e = vsa::launch_reorder(ws, o, (int)eb, B, H, D, G, 1, hs);

@@ -48,6 +48,8 @@ struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
+  const void* vt;       // bf16 path: blocked V^T [B][H][s_pad/64][D][64] (launch_transpose_v)
+  int32_t s_pad;        // S rounded up to a multiple of 64
   void* o;
   float* lse;
   const int32_t* n_full;
@@ -68,6 +70,8 @@ hipError_t launch_attn_bf16(const FwdArgs& a, const MaskTable& masks, const Head
                             hipStream_t stream);
 hipError_t launch_attn_f32(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
                            hipStream_t stream);
+hipError_t launch_transpose_v(const void* v, void* vt, int32_t B, int32_t S, int32_t H, int32_t D,
+                              int32_t s_pad, hipStream_t stream);
 hipError_t launch_reorder(const void* src, void* dst, int32_t elem_bytes, int32_t B,
                           int32_t H, int32_t D, const Geom& g, int32_t inverse,
                           hipStream_t stream);

@@ -156,8 +156,10 @@ vsa_status vsa_classify_tiles(const vsa_grid* grid, vsa_layout layout,
                                  workspace, attend in tile-major order, reorder O back */
 #define VSA_FWD_WRITE_LSE 4   /* write lse (must then be non-NULL) */
 
-/* Workspace bytes vsa_sparse_attn_fwd needs for these arguments (0 without
- * VSA_FWD_REORDER_IO; 3*B*S*H*D elements of dtype with it). */
+/* Workspace bytes vsa_sparse_attn_fwd needs for these arguments: for bf16,
+ * B*H*D*S64 elements (S64 = S rounded up to a multiple of 64) that hold V
+ * transposed per 64-key block to [B][H][S64/64][D][64]; with VSA_FWD_REORDER_IO, 3*B*S*H*D elements of
+ * dtype more.  f32 without VSA_FWD_REORDER_IO needs none. */
 vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D,
                                    vsa_dtype dtype, int32_t flags, size_t* bytes);
 
@@ -171,8 +173,9 @@ vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D,
  *   Bq, Bk:   bf16: Bq in {64, 128, 256}, Bk = 64; f32: Bq in {32, 64, 128}, Bk in {32, 64}
  *   scale:    softmax scale; 0 selects 1/sqrt(D)
  *   flags:    VSA_FWD_* bits
- *   workspace, ws_bytes: device scratch, see vsa_fwd_workspace_bytes (may be NULL
- *             when 0 bytes are needed)
+ *   workspace, ws_bytes: device scratch, 16-byte aligned, owned by the caller and
+ *             free again once the stream has run the call; see
+ *             vsa_fwd_workspace_bytes (may be NULL when 0 bytes are needed)
  * Output rows whose query has no kept key are 0.  D must be 64 or 128.
  * The full tiles take an unmasked path and boundary tiles an element-masked path;
  * both feed one online softmax per query row, so the result does not depend on

@@ -49,9 +49,12 @@ def test_unique_masks_and_counts():
 
 
 def test_workspace_sizes():
-    assert vsa.vsa_fwd_workspace_bytes(1, 115200, 24, 128, vsa.VSA_BF16, 0) == 0
+    vt = 24 * 128 * 115200 * 2  # V^T, S already a multiple of 64
+    assert vsa.vsa_fwd_workspace_bytes(1, 115200, 24, 128, vsa.VSA_BF16, 0) == vt
+    assert vsa.vsa_fwd_workspace_bytes(2, 100, 3, 64, vsa.VSA_BF16, 0) == 2 * 3 * 64 * 128 * 2
+    assert vsa.vsa_fwd_workspace_bytes(2, 100, 3, 64, vsa.VSA_F32, 0) == 0
     assert vsa.vsa_fwd_workspace_bytes(1, 115200, 24, 128, vsa.VSA_BF16, vsa.VSA_FWD_REORDER_IO) \
-        == 3 * 115200 * 24 * 128 * 2
+        == 3 * 115200 * 24 * 128 * 2 + vt
     assert vsa.vsa_profile_workspace_bytes(2, 75600, 40, 128, 64, 3) > 0
 
 
@@ -76,7 +79,7 @@ def _call_fwd(**over):
     g = over.pop("grid", W.grid(4, 8, 8))
     masks = over.pop("masks", [W.mask_spatial(1), W.mask_temporal(1)])
     args = dict(q=0x1000, k=0x2000, v=0x3000, o=0x4000, lse=None, dtype=vsa.VSA_BF16, B=1, S=256, H=2, D=64,
-                layout=0, Bq=64, Bk=64, scale=0.0, flags=0, ws=None, ws_bytes=0)
+                layout=0, Bq=64, Bk=64, scale=0.0, flags=0, ws=0xA000, ws_bytes=1 << 40)
     args.update(over)
     lists = _lib.vsa_tile_lists(0x5000, 0x6000, 0x7000, 0x8000, 0x9000)
     arr = _lib.make_masks(masks)
@@ -98,7 +101,9 @@ def _call_fwd(**over):
     (dict(flags=64), -1, "flag"),
     (dict(flags=4), -1, "lse"),
     (dict(flags=2), -1, "tile-major"),
-    (dict(flags=2, layout=1, grid=W.grid(4, 8, 8, (2, 4, 4))), -3, "workspace"),
+    (dict(flags=2, layout=1, grid=W.grid(4, 8, 8, (2, 4, 4)), ws_bytes=1000), -3, "workspace"),
+    (dict(ws=None, ws_bytes=0), -3, "workspace"),
+    (dict(ws=0xA008), -1, "aligned"),
     (dict(grid=W.grid(4, 8, 8, (3, 4, 4)), layout=1), -1, "divide"),
     (dict(masks=[W.mask_stripe(1, 0, 0, 1, 0, 5), W.mask_all()]), -1, "period"),
     (dict(masks=[W.mask_sta(1, 1, 1), W.mask_all()]), -1, "tile"),
