@@ -186,13 +186,14 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   // K tile: row R of LDS holds key swap_bits23(R), 16-byte chunks swizzled by ksw(R).
   // V^T tile (one contiguous D x 64 block in global memory): row d of LDS holds channel d
   // (64 keys, 128 bytes), chunks swizzled by vtsw(d).
-  int dma_k[C::NI], dma_v[C::NI];
+  int dma_k[C::NI], dma_v[C::NI], krow[C::NI], kcol[C::NI];
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
     const int R = (wave * C::NI + i) * C::ROWS_PER_DMA + lane / C::CH;
     const int p = lane % C::CH;
-    const int rk = swap_bits23(R);
-    dma_k[i] = 2 * (rk * tok_stride + ((p ^ ksw<D, NW>(R)) * 8));  // bytes
+    krow[i] = swap_bits23(R);
+    kcol[i] = (p ^ ksw<D, NW>(R)) * 8;
+    dma_k[i] = 2 * (krow[i] * tok_stride + kcol[i]);  // bytes
     const int d = (wave * C::NI + i) * 8 + lane / 8;                // 8 V^T rows per DMA
     dma_v[i] = 2 * (d * BK + (((lane % 8) ^ vtsw(d)) * 8));
   }
@@ -294,6 +295,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   int kt0 = 0, kt1 = 0, kt2 = 0;
   constexpr int NQK = 2 * KSTEPS;  // MFMAs of stage A
   constexpr int NPV = 4 * DB;      // MFMAs of stage B
+  static_assert(NQK % C::NI == 0 && NPV % C::NI == 0, "DMA spread");
   constexpr int EA = 32 / NQK;     // scores per lane exponentiated per stage-A MFMA
   constexpr int EB = 32 / NPV;     // scores per lane max-reduced per stage-B MFMA
   static_assert(EA % 2 == 0 && EB % 2 == 0, "score pairs");
@@ -315,8 +317,23 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     const int kt3 = it + 3 < n_tiles ? tile_of(it + 3) : 0;
     wait_vmcnt<0>();
     barrier_lds();
-    if (it + 2 < n_tiles) issue(kt2, k_fill, false);
-    if (it + 1 < n_tiles) issue(kt1, v_fill, true);
+    // The prefetch of K(it+2) and V(it+1) is spread over the MFMA chunks below, one
+    // DMA every few MFMAs, instead of issued as one burst: a burst fills the
+    // vector-memory queue and stalls the issuing wave.  When no tile is left to
+    // prefetch, a listed tile is fetched again into the free buffer (never read).
+    const int ktf = it + 2 < n_tiles ? kt2 : kt0;
+    const int vtf = it + 1 < n_tiles ? kt1 : kt0;
+    const uint16_t* ksrc = kp + base_bh + (size_t)(ktf * BK) * tok_stride;
+    const uint16_t* vsrc = vtp + (size_t)(vtf * BK) * D;
+    const uint32_t kl0 = lds_addr(k_fill + wave * C::NI * 1024);
+    const uint32_t vl0 = lds_addr(v_fill + wave * C::NI * 1024);
+    int koff[C::NI];  // tail tile: rows past S read row S-1 (masked keys, finite data)
+    {
+      const bool tail = ktf * BK + BK > S;
+      const int lim = S - 1 - ktf * BK;
+#pragma unroll
+      for (int i = 0; i < C::NI; ++i) koff[i] = tail ? 2 * (imin(krow[i], lim) * tok_stride + kcol[i]) : dma_k[i];
+    }
     uint32_t w_next = ~0u;
     if constexpr (NEXT_BND) w_next = mask_word(kt1);
 
@@ -350,6 +367,10 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
         if (i + 2 < NQK) kr[(i + 2) % 3] = kread(k_use, i + 2);
         s_next[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[i % 3]),
                                                                 qf[i >> 1], s_next[i & 1], 0, 0, 0);
+        if (i % (NQK / C::NI) == 0) {
+          const int d = i / (NQK / C::NI);
+          dma16(ksrc, koff[d], kl0 + d * 1024);
+        }
 #pragma unroll
         for (int e = 0; e < EA; e += 2) {
           const int v = i * EA + e;
@@ -379,6 +400,10 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
             bf16x8, u32x4{__builtin_bit_cast(uint32_t, pk[4 * j + 0]), __builtin_bit_cast(uint32_t, pk[4 * j + 1]),
                           __builtin_bit_cast(uint32_t, pk[4 * j + 2]), __builtin_bit_cast(uint32_t, pk[4 * j + 3])});
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i % 3]), pf, acc[db], 0, 0, 0);
+        if (i % (NPV / C::NI) == 0) {
+          const int d = i / (NPV / C::NI);
+          dma16(vsrc, dma_v[d], vl0 + d * 1024);
+        }
 #pragma unroll
         for (int e = 0; e < EB; e += 2) {
           const int v = i * EB + e;
@@ -461,6 +486,8 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     else
       step(P0{}, NextFull{}, it);
   }
+
+  wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it ends
 
   // ---- epilogue: O = acc / l, lse = scale*m + ln(l) ----
   const float l_tot = pair_sum(l_run);
