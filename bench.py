@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no structured sparsity)
 PEAK_HBM_GBS = 8000.0
 METRIC = "sparse-attn ms/call + effective TFLOP/s at 75.6K tokens; % of bf16 MFMA peak"
-ATTN_SOURCES = ["attn_bf16.hip", "mfma_tile.h", "vsa_geom.h"]
+ATTN_SOURCES = ["attn_bf16.hip", "lds_pipe.h", "vsa_geom.h"]
 
 
 def kernel_hash():
