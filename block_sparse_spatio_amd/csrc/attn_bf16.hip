@@ -281,6 +281,10 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     // fences between chunks keep that order, so every LDS read has two MFMAs to land.
     f32x16 s_next[2] = {f32x16{}, f32x16{}};
     bf16x2 pk[16];  // P(it): pk[v/2] holds scores v, v+1 (v = kb*16 + register)
+    // Issue priority: the other wave on this SIMD is usually in the opposite stage, and
+    // letting stage A (exponentials between its MFMAs) issue first keeps both the
+    // vector unit and the matrix core fed while stage B streams MFMAs.
+    __builtin_amdgcn_s_setprio(1);
     {
       u32x4 kr[3];
       kr[0] = kread(k_use, 0);
@@ -309,6 +313,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 
     // stage B: O^T += V(it)^T P(it)^T in four 16-key steps of DB MFMAs; chunk i also
     // masks (boundary successor) and max-reduces EB scores of S(it+1)
+    __builtin_amdgcn_s_setprio(0);
     {
       u32x4 vr[3];
       vr[0] = vread(v_use, 0);
