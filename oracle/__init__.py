@@ -12,6 +12,7 @@ Contents
   attention  masked softmax attention written from its definition
   profile    the sampled-query head profiler and router
   reorder    the tile-major token permutation and its inverse
+  merge      merging partial results over disjoint key sets by their log-sum-exp
 
 Every function is pinned by tests under ``tests/`` (marked ``not gpu``) against
 numbers the pages print, closed forms, special cases and brute force on tiny
@@ -23,3 +24,4 @@ from .classify import classify, EMPTY, FULL, BOUNDARY  # noqa: F401
 from .attention import attention  # noqa: F401
 from .profile import profile_heads  # noqa: F401
 from .reorder import tile_major_permutation, reorder_tokens  # noqa: F401
+from .merge import merge_partials  # noqa: F401

@@ -376,6 +376,55 @@ def test_partial_results_merge_by_lse():
     assert np.abs(lm - l).max() < 1e-13
 
 
+def _dt_classes(g, parts):
+    """Stripe masks keeping key frames with dt = r (mod parts), r = 0..parts-1, no sink."""
+    return [W.mask_stripe(1, r, parts, 1, 0, 1, sink_frames=0) for r in range(parts)]
+
+
+def test_merge_partials_equals_attention_over_union():
+    """oracle.merge_partials over a partition of the keys (dt mod 3) equals attention
+    over all keys (DSA guide, section 18), for every row and head."""
+    g = W.grid(7, 3, 4)
+    S = W.seq_len(g)
+    q, k, v = (_rand((2, S, 2, 8), 50 + s) for s in range(3))
+    classes = _dt_classes(g, 3)
+    c = token_coords(g, "frame", np.arange(S))
+    keeps = [keep_matrix(m, g, c, c) for m in classes]
+    assert np.all(sum(kp.astype(int) for kp in keeps) == 1)  # a partition of all pairs
+    parts = [oracle.attention(q, k, v, g, "frame", [m, m]) for m in classes]
+    o, l = oracle.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    ref_o, ref_l = oracle.attention(q, k, v, g, "frame", [W.mask_all(), W.mask_all()])
+    assert np.abs(o - ref_o).max() < 1e-13 and np.abs(l - ref_l).max() < 1e-13
+    # any order of arrival gives the same result
+    o2, l2 = oracle.merge_partials([parts[i][0] for i in (2, 0, 1)], [parts[i][1] for i in (2, 0, 1)])
+    assert np.abs(o2 - o).max() < 1e-14 and np.abs(l2 - l).max() < 1e-14
+
+
+def test_merge_partials_special_cases():
+    rng = np.random.default_rng(7)
+    B, S, H, D = 1, 6, 2, 4
+    o1 = rng.standard_normal((B, S, H, D))
+    l1 = rng.standard_normal((B, H, S))
+    # one part: identity
+    o, l = oracle.merge_partials([o1], [l1])
+    assert np.array_equal(o, o1) and np.array_equal(l, l1)
+    # a part merged with itself: same output, lse + ln 2
+    o, l = oracle.merge_partials([o1, o1], [l1, l1])
+    assert np.abs(o - o1).max() < 1e-15 and np.abs(l - (l1 + math.log(2))).max() < 1e-15
+    # an empty part (lse = -inf) adds nothing, whatever its output holds
+    junk = np.full_like(o1, np.nan)
+    o, l = oracle.merge_partials([o1, junk], [l1, np.full_like(l1, -np.inf)])
+    assert np.array_equal(o, o1) and np.array_equal(l, l1)
+    # all parts empty: o = 0, lse = -inf
+    o, l = oracle.merge_partials([junk, junk], [np.full_like(l1, -np.inf)] * 2)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+    # two parts with known weights: lse 0 and ln 3 weigh 1 : 3
+    o2 = rng.standard_normal((B, S, H, D))
+    o, l = oracle.merge_partials([o1, o2], [np.zeros((B, H, S)), np.full((B, H, S), math.log(3))])
+    assert np.abs(o - (0.25 * o1 + 0.75 * o2)).max() < 1e-15
+    assert np.abs(l - math.log(4)).max() < 1e-15
+
+
 def test_tile_major_equals_frame_major_after_inverse():
     g = W.grid(4, 4, 6, (2, 2, 3))
     S = 96
