@@ -315,6 +315,26 @@ def main():
         extra["reorder_gbs"] = round(2.0 * qd.numel() * qd.element_size() / (r_ms * 1e-3) / 1e9, 1)
         del y
 
+    # merging two partial results of this shape (LSE merge): HBM GB/s of the
+    # algorithmic traffic (2 parts read + 1 output written, with their LSE rows)
+    pa = torch.randn_like(qd)
+    pb = torch.randn_like(qd)
+    la = torch.randn((B, H, S), dtype=torch.float32, device=dev)
+    lb = torch.randn((B, H, S), dtype=torch.float32, device=dev)
+    mo = torch.empty_like(qd)
+    ml = torch.empty_like(la)
+    vsa.vsa_merge_partials([pa, pb], [la, lb], o=mo, lse=ml, stream=stream)
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record(stream)
+    for _ in range(5):
+        vsa.vsa_merge_partials([pa, pb], [la, lb], o=mo, lse=ml, stream=stream)
+    m1.record(stream)
+    torch.cuda.synchronize()
+    m_ms = m0.elapsed_time(m1) / 5
+    extra["merge2_ms"] = round(m_ms, 4)
+    extra["merge2_gbs"] = round((3.0 * qd.numel() * qd.element_size() + 3.0 * la.numel() * 4) / (m_ms * 1e-3) / 1e9, 1)
+    del pa, pb, la, lb, mo, ml
+
     khash = kernel_hash()
     traffic = traffic_from_profiles(khash, 1)
     rec = {

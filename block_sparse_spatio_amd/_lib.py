@@ -63,6 +63,7 @@ _SIGNATURES = {
                                  ctypes.POINTER(vsa_mask_desc), ctypes.POINTER(vsa_tile_lists), _I, _I,
                                  ctypes.c_float, _I, _P, ctypes.c_size_t, _P]),
     "vsa_reorder_tokens": (_I, [_P, _P, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I, _P]),
+    "vsa_merge_partials": (_I, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _P, _P, _I, _I, _I, _I, _I, _P]),
     "vsa_profile_workspace_bytes": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
     "vsa_profile_heads": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I, _P, _I,
                                ctypes.POINTER(vsa_mask_desc), _I, _P, _P, ctypes.c_float, _P,
@@ -218,6 +219,27 @@ def vsa_sparse_attn_fwd(q, k, v, grid, layout, masks, tiles, scale=0.0, flags=0,
         _layout(layout), make_masks(masks), ctypes.byref(st), tiles["Bq"], tiles["Bk"], float(scale),
         flags, _ptr(workspace), ws_bytes, _stream(stream, q.device)))
     return o, (lse if flags & VSA_FWD_WRITE_LSE else None)
+
+
+def vsa_merge_partials(o_parts, lse_parts, o=None, lse=None, stream=None):
+    """Merge partial results over disjoint key subsets.  o_parts: list of [B, S, H, D]
+    device tensors (one dtype); lse_parts: list of float32 [B, H, S].  Returns (o, lse)."""
+    n = len(o_parts)
+    if n != len(lse_parts):
+        raise ValueError("o_parts and lse_parts differ in length")
+    B, S, H, D = o_parts[0].shape
+    for t in list(o_parts) + list(lse_parts):
+        if not t.is_contiguous():
+            raise ValueError("parts must be contiguous")
+    if o is None:
+        o = torch.empty_like(o_parts[0])
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=o_parts[0].device)
+    op = (_P * n)(*[_ptr(t) for t in o_parts])
+    lp = (_P * n)(*[_ptr(t) for t in lse_parts])
+    _check(load().vsa_merge_partials(op, lp, n, _ptr(o), _ptr(lse), _dtype(o_parts[0]), B, S, H, D,
+                                     _stream(stream, o_parts[0].device)))
+    return o, lse
 
 
 def vsa_reorder_tokens(src, grid, inverse=False, dst=None, stream=None):

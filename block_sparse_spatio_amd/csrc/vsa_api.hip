@@ -335,6 +335,39 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   return ok();
 }
 
+vsa_status vsa_merge_partials(const void* const* o_parts, const float* const* lse_parts, int32_t n_parts, void* o,
+                              float* lse, vsa_dtype dtype, int32_t B, int32_t S, int32_t H, int32_t D,
+                              void* stream) {
+  if (!o_parts || !lse_parts || !o) return fail(VSA_ERR_INVALID_ARG, "o_parts, lse_parts and o must be non-NULL");
+  if (n_parts < 1 || n_parts > VSA_MAX_MERGE_PARTS)
+    return fail(VSA_ERR_INVALID_ARG, "n_parts=%d (1..%d)", n_parts, VSA_MAX_MERGE_PARTS);
+  if (B <= 0 || S <= 0 || H <= 0) return fail(VSA_ERR_INVALID_ARG, "B, S, H must be positive");
+  if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (D != 64 && D != 128) return fail(VSA_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", D);
+  vsa::MergeArgs a;
+  memset(&a, 0, sizeof a);
+  for (int i = 0; i < n_parts; ++i) {
+    if (!o_parts[i] || !lse_parts[i]) return fail(VSA_ERR_INVALID_ARG, "part %d has a NULL pointer", i);
+    if (((uintptr_t)o_parts[i] & 15) || ((uintptr_t)lse_parts[i] & 3))
+      return fail(VSA_ERR_INVALID_ARG, "part %d is not aligned (o 16 bytes, lse 4 bytes)", i);
+    a.o[i] = o_parts[i];
+    a.lse[i] = lse_parts[i];
+  }
+  if ((uintptr_t)o & 15) return fail(VSA_ERR_INVALID_ARG, "o is not 16-byte aligned");
+  for (int i = n_parts; i < 16; ++i) {  // unused slots point at part 0 (never read)
+    a.o[i] = o_parts[0];
+    a.lse[i] = lse_parts[0];
+  }
+  a.out = o;
+  a.lse_out = lse;
+  a.n = n_parts;
+  a.B = B; a.S = S; a.H = H; a.D = D;
+  a.is_bf16 = dtype == VSA_BF16;
+  hipError_t e = vsa::launch_merge(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
 vsa_status vsa_reorder_tokens(const void* src, void* dst, vsa_dtype dtype, int32_t B, int32_t H, int32_t D,
                               const vsa_grid* grid, int32_t inverse, void* stream) {
   long long S;

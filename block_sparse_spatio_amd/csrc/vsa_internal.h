@@ -89,6 +89,15 @@ struct ProfArgs {
   int32_t is_bf16;
   Geom g;
 };
+struct MergeArgs {
+  const void* o[16];
+  const float* lse[16];
+  void* out;
+  float* lse_out;
+  int32_t n, B, S, H, D, is_bf16;
+};
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
 size_t profile_ws_floats(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand,
                          int32_t n_chunks);
 int32_t profile_chunks(int32_t B, int32_t S, int32_t H);

@@ -198,6 +198,29 @@ vsa_status vsa_reorder_tokens(const void* src, void* dst, vsa_dtype dtype, int32
                               int32_t H, int32_t D, const vsa_grid* grid,
                               int32_t inverse, void* stream);
 
+/* Merging partial results ------------------------------------------------------ */
+
+#define VSA_MAX_MERGE_PARTS 16
+
+/* Merge attention results computed over disjoint key subsets of the same queries
+ * (DSA study guide, section 18: online-softmax partials combine by their softmax
+ * statistics, in any order, into one softmax over the union).  Per row:
+ *   m' = max_i lse_i,  w_i = exp(lse_i - m')  (0 for a part with lse_i = -inf),
+ *   lse = m' + ln(sum_i w_i),  o = sum_i w_i o_i / sum_i w_i;
+ * a row where every part has lse = -inf gets o = 0 and lse = -inf.
+ *   o_parts:   host array [n_parts] of device pointers, each [B][S][H][D] of dtype
+ *              (normalised partial outputs, as vsa_sparse_attn_fwd writes them)
+ *   lse_parts: host array [n_parts] of device pointers, each float [B][H][S]
+ *              (natural log, as written with VSA_FWD_WRITE_LSE)
+ *   n_parts:   1 .. VSA_MAX_MERGE_PARTS
+ *   o:         device [B][S][H][D] of dtype (output; may be one of o_parts)
+ *   lse:       device float [B][H][S] (output, may be NULL; may be one of lse_parts)
+ * D must be 64 or 128.  Accumulation is fp32; bf16 output is rounded to nearest even.
+ * Asynchronous on stream; the caller owns every buffer. */
+vsa_status vsa_merge_partials(const void* const* o_parts, const float* const* lse_parts,
+                              int32_t n_parts, void* o, float* lse, vsa_dtype dtype,
+                              int32_t B, int32_t S, int32_t H, int32_t D, void* stream);
+
 /* Head profiler --------------------------------------------------------------- */
 
 /* Workspace bytes vsa_profile_heads needs. */

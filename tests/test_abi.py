@@ -161,3 +161,29 @@ def test_reorder_validation():
     g = _lib.make_grid(W.grid(4, 8, 8, (2, 4, 4)))
     st = lib.vsa_reorder_tokens(0x1, 0x1, vsa.VSA_BF16, 1, 2, 64, ctypes.byref(g), 0, None)
     assert st == -1 and "alias" in vsa.vsa_last_error()
+
+
+def _call_merge(n=2, o_ok=True, lse_ok=True, D=128, dtype=0, S=10, out=0x9000, misalign=False):
+    lib = vsa.load()
+    P = ctypes.c_void_p
+    op = (P * max(n, 1))(*([0x1000 + (8 if misalign else 0)] * max(n, 1) if o_ok else [None] * max(n, 1)))
+    lp = (P * max(n, 1))(*([0x2000] * max(n, 1) if lse_ok else [None] * max(n, 1)))
+    st = lib.vsa_merge_partials(op, lp, n, out, None, dtype, 1, S, 2, D, None)
+    return st, vsa.vsa_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(n=0), -1, "n_parts"),
+    (dict(n=17), -1, "n_parts"),
+    (dict(o_ok=False), -1, "NULL"),
+    (dict(lse_ok=False), -1, "NULL"),
+    (dict(D=96), -2, "D=96"),
+    (dict(dtype=5), -1, "dtype"),
+    (dict(S=0), -1, "positive"),
+    (dict(out=None), -1, "non-NULL"),
+    (dict(misalign=True), -1, "aligned"),
+])
+def test_merge_validation(kw, status, needle):
+    st, msg = _call_merge(**kw)
+    assert st == status, msg
+    assert needle in msg
