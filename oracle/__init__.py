@@ -21,6 +21,7 @@ inputs.  No function here is "parity unpinned".
 from .coords import token_coords, num_tiles  # noqa: F401
 from .masks import keep_matrix  # noqa: F401
 from .classify import classify, EMPTY, FULL, BOUNDARY  # noqa: F401
+from .classify import rounded_keep_rows  # noqa: F401
 from .attention import attention  # noqa: F401
 from .profile import profile_heads  # noqa: F401
 from .reorder import tile_major_permutation, reorder_tokens  # noqa: F401

@@ -25,6 +25,7 @@ from __future__ import annotations
 import numpy as np
 
 from .coords import token_coords
+from .classify import rounded_keep_rows
 from .masks import keep_matrix
 
 
@@ -48,12 +49,14 @@ def attention_rows(q, k, v, keep, scale):
     return o, lse
 
 
-def attention(q, k, v, grid, layout, masks, scale=None, rows=None, heads=None, block=128):
+def attention(q, k, v, grid, layout, masks, scale=None, rows=None, heads=None, block=128, round_tiles=None):
     """Masked attention for tensors q, k, v of shape [B, S, H, D] (any float dtype).
 
     masks: list of H descriptor dicts, one per head.
     rows:  optional int array of executed query positions (default: all S).
     heads: optional list of heads (default: all).
+    round_tiles: optional (Bq, Bk): attend under the tile-aligned (B3) rounding of each
+             mask (oracle.classify.rounded_keep_rows) instead of the exact mask.
     Returns o [B, len(rows), len(heads), D] fp64 and lse [B, len(heads), len(rows)] fp64."""
     B, S, H, D = q.shape
     if scale is None:
@@ -69,7 +72,10 @@ def attention(q, k, v, grid, layout, masks, scale=None, rows=None, heads=None, b
         qh = [_f64(q[b, :, h]) for b in range(B)]
         for r0 in range(0, len(rows), block):
             r = rows[r0:r0 + block]
-            keep = keep_matrix(masks[h], grid, token_coords(grid, layout, r), ck)
+            if round_tiles is None:
+                keep = keep_matrix(masks[h], grid, token_coords(grid, layout, r), ck)
+            else:
+                keep = rounded_keep_rows(grid, layout, masks[h], round_tiles[0], round_tiles[1], r)
             for b in range(B):
                 ob, lb = attention_rows(qh[b][r], kh[b], vh[b], keep, scale)
                 o[b, r0:r0 + len(r), hi] = ob

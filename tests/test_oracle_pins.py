@@ -425,6 +425,74 @@ def test_merge_partials_special_cases():
     assert np.abs(l - math.log(4)).max() < 1e-15
 
 
+def _brute_fraction(keep, S, Bq, Bk, qt, kt):
+    r = range(qt * Bq, min(S, (qt + 1) * Bq))
+    c = range(kt * Bk, min(S, (kt + 1) * Bk))
+    kept = sum(int(keep[i, j]) for i in r for j in c)
+    return kept, len(r) * len(c)
+
+
+@pytest.mark.parametrize("gi", range(3))
+def test_rounded_classes_follow_the_half_rule(gi):
+    """Tile-aligned rounding (B3): full and empty tiles stay; a boundary tile keeps all
+    of its real pairs iff at least half of them are kept; tiles reaching past S stay
+    boundary when kept.  Checked pair by pair on small grids."""
+    g, desc, Bq, Bk = [(W.grid(3, 5, 7), W.mask_box(1, 1, 2, sink_frames=1), 16, 16),
+                       (W.grid(4, 6, 5), W.mask_stripe(1, 0, 2, 2, 1, 6, sink_frames=0), 32, 16),
+                       (W.grid(2, 9, 9), W.mask_box(-1, 2, 2), 16, 32)][gi]
+    S = W.seq_len(g)
+    c = token_coords(g, "frame", np.arange(S))
+    keep = keep_matrix(desc, g, c, c)
+    exact = oracle.classify(g, "frame", desc, Bq, Bk)["cls"]
+    rnd = oracle.classify(g, "frame", desc, Bq, Bk, round_tiles=True)["cls"]
+    rk = oracle.rounded_keep_rows(g, "frame", desc, Bq, Bk, np.arange(S))
+    for qt in range(rnd.shape[0]):
+        for kt in range(rnd.shape[1]):
+            kept, real = _brute_fraction(keep, S, Bq, Bk, qt, kt)
+            padded = (qt + 1) * Bq > S or (kt + 1) * Bk > S
+            on = kept > 0 and 2 * kept >= real
+            want = (oracle.BOUNDARY if padded else oracle.FULL) if on else oracle.EMPTY
+            assert rnd[qt, kt] == want
+            if exact[qt, kt] != oracle.BOUNDARY:
+                assert rnd[qt, kt] == exact[qt, kt] or (padded and exact[qt, kt] == oracle.FULL)
+            block = rk[qt * Bq:min(S, (qt + 1) * Bq), kt * Bk:min(S, (kt + 1) * Bk)]
+            assert np.all(block == on)
+
+
+def test_rounding_threshold_is_one_half():
+    """On a 1-D grid the stripe |dx| mod 2 == 0 keeps exactly half of every 4 x 4 tile
+    (kept: rounds up); |dx| mod 3 == 0 keeps at most 6 of 16 (dropped)."""
+    g = W.grid(1, 1, 16)
+    half = W.mask_stripe(1, 0, 1, 1, 0, 2, sink_frames=0)
+    third = W.mask_stripe(1, 0, 1, 1, 0, 3, sink_frames=0)
+    c = token_coords(g, "frame", np.arange(16))
+    kh = keep_matrix(half, g, c, c)
+    assert all(kh[i * 4:(i + 1) * 4, j * 4:(j + 1) * 4].sum() == 8 for i in range(4) for j in range(4))
+    assert np.all(oracle.classify(g, "frame", half, 4, 4, round_tiles=True)["cls"] == oracle.FULL)
+    r3 = oracle.classify(g, "frame", third, 4, 4, round_tiles=True)["cls"]
+    k3 = keep_matrix(third, g, c, c)
+    for i in range(4):
+        for j in range(4):
+            n = k3[i * 4:(i + 1) * 4, j * 4:(j + 1) * 4].sum()
+            assert r3[i, j] == (oracle.FULL if 2 * n >= 16 else oracle.EMPTY)
+    assert np.all(r3 == oracle.EMPTY)  # no 4 x 4 tile keeps more than 6 of its 16 pairs
+
+
+def test_rounding_leaves_tile_aligned_masks_unchanged():
+    """A sliding-tile mask whose tiles coincide with the kernel tiles has no boundary
+    tile, so rounding changes neither classes nor the attention output."""
+    g = W.grid(4, 8, 8, (2, 4, 4))  # 32-token tiles, kernel tiles 32 x 32
+    desc = W.mask_sta(1, 1, 1)
+    ex = oracle.classify(g, "tile", desc, 32, 32)["cls"]
+    assert not np.any(ex == oracle.BOUNDARY)
+    assert np.array_equal(oracle.classify(g, "tile", desc, 32, 32, round_tiles=True)["cls"], ex)
+    S = W.seq_len(g)
+    q, k, v = (_rand((1, S, 1, 8), 60 + s) for s in range(3))
+    o1, l1 = oracle.attention(q, k, v, g, "tile", [desc])
+    o2, l2 = oracle.attention(q, k, v, g, "tile", [desc], round_tiles=(32, 32))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 def test_tile_major_equals_frame_major_after_inverse():
     g = W.grid(4, 4, 6, (2, 2, 3))
     S = 96
