@@ -181,6 +181,8 @@ def main():
     ap.add_argument("--config", default="wan_mixed")
     ap.add_argument("--Bq", type=int, default=None)
     ap.add_argument("--flags", type=int, default=0, help="extra VSA_FWD_* flags (e.g. 1 = B1 ablation)")
+    ap.add_argument("--round-tiles", action="store_true",
+                    help="tile-aligned rounding of the masks (B3): rounded lists, forward with VSA_FWD_TILE_ALIGNED")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-keep dense run")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -219,7 +221,7 @@ def main():
     Bq = args.Bq or cfg["Bq"]
     Bk = cfg["Bk"]
     reorder = layout == "tile"
-    flags = args.flags | (vsa.VSA_FWD_REORDER_IO if reorder else 0)
+    flags = args.flags | (vsa.VSA_FWD_REORDER_IO if reorder else 0) | (vsa.VSA_FWD_TILE_ALIGNED if args.round_tiles else 0)
     print(f"[bench] {args.config}: B={B} S={S} H={H} D={D} Bq={Bq} Bk={Bk} drawing inputs", file=sys.stderr,
           flush=True)
     q, k, v = W.qkv(B, S, H, D, cfg["dtype"], seed=cfg["seed"])
@@ -246,7 +248,7 @@ def main():
             vsa.vsa_profile_heads(qd, kd, vd, g, layout, sidx, cfg["candidates"], workspace=pws, stream=stream)
         if ev is not None:
             ev[3].record(stream)
-        vsa.vsa_classify_tiles(g, layout, masks, Bq, Bk, out=tiles, stream=stream)
+        vsa.vsa_classify_tiles(g, layout, masks, Bq, Bk, out=tiles, stream=stream, round_tiles=args.round_tiles)
         if ev is not None:
             ev[1].record(stream)
         vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles, flags=flags, o=o, workspace=ws, stream=stream)
@@ -273,6 +275,8 @@ def main():
     attn_ms = float(np.mean(fwd_ms))
 
     f_exec = 4.0 * D * executed_pairs(tiles, head_map, B, S)
+    n_full_tiles = int(tiles["n_full"][torch.as_tensor(head_map, device=dev).long()].sum())
+    n_bnd_tiles = int(tiles["n_bnd"][torch.as_tensor(head_map, device=dev).long()].sum())
     f_kept = 4.0 * D * kept_pairs(g, masks, B)
     f_dense = 4.0 * D * float(S) * S * H * B
     value = f_exec / (ms_step * 1e-3) / 1e12
@@ -352,10 +356,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "B": B, "S": S, "H": H, "D": D, "grid": [g["T"], g["Hg"], g["Wg"]],
                    "layout": layout, "Bq": Bq, "Bk": Bk, "masks": sorted({m["kind"] for m in masks}),
-                   "unique_masks": U, "flags": flags},
+                   "unique_masks": U, "flags": flags, "tile_rounding": bool(args.round_tiles)},
         "attn_ms_per_call": round(attn_ms, 4),
         "attn_ms_p10_p90": [round(float(np.percentile(fwd_ms, 10)), 4), round(float(np.percentile(fwd_ms, 90)), 4)],
         "classify_ms": round(float(np.mean(cls_ms)), 4),
+        "boundary_tile_frac": round(n_bnd_tiles / max(1, n_full_tiles + n_bnd_tiles), 5),
         **extra,
         "tflops_executed_attn": round(achieved, 2),
         "pct_of_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),

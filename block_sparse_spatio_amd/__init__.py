@@ -4,7 +4,8 @@ The compute lives in libvsa.so (HIP kernels for gfx950 behind the C ABI of
 include/vsa.h); this package is its ctypes binding.
 """
 from ._lib import (  # noqa: F401
-    VSA_BF16, VSA_F32, VSA_FWD_FORCE_MASK, VSA_FWD_REORDER_IO, VSA_FWD_WRITE_LSE,
+    VSA_BF16, VSA_F32, VSA_FWD_FORCE_MASK, VSA_FWD_REORDER_IO, VSA_FWD_WRITE_LSE, VSA_FWD_TILE_ALIGNED,
+    VSA_CLASSIFY_ROUND_TILES,
     VSA_LAYOUT_FRAME_MAJOR, VSA_LAYOUT_TILE_MAJOR, VSA_TILE_BOUNDARY, VSA_TILE_EMPTY, VSA_TILE_FULL,
     LIB_PATH, VsaError, alloc_tile_lists, default_scale, load, make_grid, make_masks,
     vsa_classify_tiles, vsa_fwd_workspace_bytes, vsa_last_error, vsa_profile_heads,

@@ -21,7 +21,8 @@ VSA_BF16, VSA_F32 = 0, 1
 VSA_LAYOUT_FRAME_MAJOR, VSA_LAYOUT_TILE_MAJOR = 0, 1
 VSA_MASK_ALL, VSA_MASK_BOX, VSA_MASK_STRIPE, VSA_MASK_STA = 0, 1, 2, 3
 VSA_TILE_EMPTY, VSA_TILE_FULL, VSA_TILE_BOUNDARY = 0, 1, 2
-VSA_FWD_FORCE_MASK, VSA_FWD_REORDER_IO, VSA_FWD_WRITE_LSE = 1, 2, 4
+VSA_FWD_FORCE_MASK, VSA_FWD_REORDER_IO, VSA_FWD_WRITE_LSE, VSA_FWD_TILE_ALIGNED = 1, 2, 4, 8
+VSA_CLASSIFY_ROUND_TILES = 1
 
 _KINDS = {"all": VSA_MASK_ALL, "box": VSA_MASK_BOX, "stripe": VSA_MASK_STRIPE, "sta": VSA_MASK_STA}
 _LAYOUTS = {"frame": VSA_LAYOUT_FRAME_MAJOR, "tile": VSA_LAYOUT_TILE_MAJOR}
@@ -58,6 +59,8 @@ _SIGNATURES = {
     "vsa_tile_counts": (_I, [ctypes.POINTER(vsa_grid), _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "vsa_classify_tiles": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(vsa_mask_desc), _I, _I, _I,
                                 ctypes.POINTER(vsa_tile_lists), _P]),
+    "vsa_classify_tiles_ex": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(vsa_mask_desc), _I, _I, _I, _I,
+                                   ctypes.POINTER(vsa_tile_lists), _P]),
     "vsa_fwd_workspace_bytes": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
     "vsa_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I,
                                  ctypes.POINTER(vsa_mask_desc), ctypes.POINTER(vsa_tile_lists), _I, _I,
@@ -178,15 +181,18 @@ def _lists_struct(t):
                             for n in ("cls", "n_full", "n_bnd", "full_idx", "bnd_idx")])
 
 
-def vsa_classify_tiles(grid, layout, masks, Bq, Bk, out=None, device="cuda", stream=None, with_cls=True):
-    """Classify tiles; returns the dict of device tensors (allocated when out is None)."""
+def vsa_classify_tiles(grid, layout, masks, Bq, Bk, out=None, device="cuda", stream=None, with_cls=True,
+                       round_tiles=False):
+    """Classify tiles; returns the dict of device tensors (allocated when out is None).
+    round_tiles: tile-aligned rounding (vsa_classify_tiles_ex, VSA_CLASSIFY_ROUND_TILES)."""
     if out is None:
         out = alloc_tile_lists(grid, masks, Bq, Bk, device, with_cls)
     dev = out["n_full"].device
     arr = make_masks(masks)
     st = _lists_struct(out)
-    _check(load().vsa_classify_tiles(ctypes.byref(make_grid(grid)), _layout(layout), arr, len(masks), Bq, Bk,
-                                     ctypes.byref(st), _stream(stream, dev)))
+    flags = VSA_CLASSIFY_ROUND_TILES if round_tiles else 0
+    _check(load().vsa_classify_tiles_ex(ctypes.byref(make_grid(grid)), _layout(layout), arr, len(masks), Bq, Bk,
+                                        flags, ctypes.byref(st), _stream(stream, dev)))
     return out
 
 

@@ -173,7 +173,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   // Register (kb, i) of S^T holds key kb*32 + (i>>3)*16 + 8*g2 + (i&7) of the tile: gather
   // those 32 bits of the tile's 64-bit row mask (one word per lane).
   auto mask_word = [&](int kt) -> uint32_t {
-    const uint64_t bits = tile_row_mask(g, m, qpos, kt * BK, BK);
+    const uint64_t bits = a.pad_only ? real_key_mask(g, kt * BK, BK) : tile_row_mask(g, m, qpos, kt * BK, BK);
     const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
     return ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
            (((hi >> (8 * g2)) & 0xffu) << 16) | (((hi >> (16 + 8 * g2)) & 0xffu) << 24);

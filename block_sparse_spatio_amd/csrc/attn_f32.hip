@@ -62,7 +62,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(FwdArgs a, MaskTable 
     }
     __syncthreads();
     uint64_t bits = ~0ull;
-    if (boundary) bits = tile_row_mask(g, m, qpos, c0, BKT);
+    if (boundary) bits = a.pad_only ? real_key_mask(g, c0, BKT) : tile_row_mask(g, m, qpos, c0, BKT);
     float s[BKT];
     float mt = -INFINITY;
 #pragma unroll

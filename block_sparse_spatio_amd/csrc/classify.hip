@@ -3,6 +3,11 @@
 // and boundary key tiles (Sparse VideoGen on TPU, "logical sparsity is not physical
 // sparsity"; video-DiT attention blog, section 7.3: the per-Q-block K-block table).
 //
+// With tile-aligned rounding (Sparse VideoGen on TPU, "aligning the sparse mask with
+// execution", B3) a boundary tile becomes full (or, if it reaches past S, a boundary
+// tile masked only at the padding) when at least half of its real pairs are kept,
+// and empty otherwise.
+//
 // One workgroup per (query tile, mask).  The query range's boxes are computed once;
 // each thread classifies key tiles with interval arithmetic (vsa_geom.h), and a
 // workgroup-wide prefix count keeps the lists in ascending key-tile order.
@@ -17,7 +22,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
 __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g, MaskTable masks, int Bq, int Bk,
-                                                            int nQ, int nK, uint8_t* __restrict__ cls,
+                                                            int round_tiles, int nQ, int nK, uint8_t* __restrict__ cls,
                                                             int32_t* __restrict__ n_full,
                                                             int32_t* __restrict__ n_bnd,
                                                             int32_t* __restrict__ full_idx,
@@ -49,7 +54,16 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g, MaskTable ma
       const int c1 = imin(c0 + Bk, g.S);
       Box C[11];
       const int nc = decompose(g, c0, c1, C);
-      c = tile_class(g, m, R, nr, C, nc, q_padded || (c0 + Bk) > g.S);
+      const bool padded = q_padded || (c0 + Bk) > g.S;
+      c = tile_class(g, m, R, nr, C, nc, padded);
+      if (round_tiles && c == VSA_TILE_BOUNDARY) {
+        // tile-aligned rounding: keep the tile's real pairs iff at least half are kept
+        // (per-row popcounts of the exact row masks; Bk <= 64)
+        long long kept = 0;
+        for (int r = r0; r < r1; ++r) kept += __popcll(tile_row_mask(g, m, make_query(g, m, r), c0, c1 - c0));
+        const long long real = (long long)(r1 - r0) * (c1 - c0);
+        c = 2 * kept >= real ? (padded ? VSA_TILE_BOUNDARY : VSA_TILE_FULL) : VSA_TILE_EMPTY;
+      }
       if (cls_row) cls_row[kt] = (uint8_t)c;
     }
     const uint64_t bf = __ballot(c == VSA_TILE_FULL);
@@ -81,10 +95,10 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g, MaskTable ma
 }  // namespace
 
 hipError_t launch_classify(const Geom& g, const MaskTable& masks, int32_t U, int32_t Bq,
-                           int32_t Bk, int32_t nQ, int32_t nK, const vsa_tile_lists& out,
-                           hipStream_t stream) {
+                           int32_t Bk, int32_t round_tiles, int32_t nQ, int32_t nK,
+                           const vsa_tile_lists& out, hipStream_t stream) {
   dim3 grid(nQ, U);
-  hipLaunchKernelGGL(classify_kernel, grid, dim3(kThreads), 0, stream, g, masks, Bq, Bk, nQ, nK,
+  hipLaunchKernelGGL(classify_kernel, grid, dim3(kThreads), 0, stream, g, masks, Bq, Bk, round_tiles, nQ, nK,
                      out.cls, out.n_full, out.n_bnd, out.full_idx, out.bnd_idx);
   return hipGetLastError();
 }

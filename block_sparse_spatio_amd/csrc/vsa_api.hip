@@ -206,19 +206,27 @@ vsa_status vsa_tile_counts(const vsa_grid* grid, int32_t Bq, int32_t Bk, int32_t
 
 vsa_status vsa_classify_tiles(const vsa_grid* grid, vsa_layout layout, const vsa_mask_desc* masks, int32_t H,
                               int32_t Bq, int32_t Bk, const vsa_tile_lists* out, void* stream) {
+  return vsa_classify_tiles_ex(grid, layout, masks, H, Bq, Bk, 0, out, stream);
+}
+
+vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout, const vsa_mask_desc* masks, int32_t H,
+                                 int32_t Bq, int32_t Bk, int32_t flags, const vsa_tile_lists* out, void* stream) {
   long long S;
   vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && any_sta(masks, H), &S);
   if (st != VSA_OK) return st;
   if (Bq < 1 || Bk < 1 || Bq > 4096 || Bk > 4096) return fail(VSA_ERR_INVALID_ARG, "tile sizes must be in 1..4096");
   if (!out || !out->n_full || !out->n_bnd || !out->full_idx || !out->bnd_idx)
     return fail(VSA_ERR_INVALID_ARG, "tile list arrays must be non-NULL (cls may be NULL)");
+  if (flags & ~VSA_CLASSIFY_ROUND_TILES) return fail(VSA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  const int32_t round_tiles = (flags & VSA_CLASSIFY_ROUND_TILES) ? 1 : 0;
+  if (round_tiles && Bk > 64) return fail(VSA_ERR_UNSUPPORTED, "tile rounding needs Bk <= 64 (Bk=%d)", Bk);
   vsa::MaskTable table;
   vsa::HeadMap hm;
   int32_t U = 0;
   st = build_table(masks, H, grid, &table, &hm, &U);
   if (st != VSA_OK) return st;
   const int32_t nQ = (int32_t)((S + Bq - 1) / Bq), nK = (int32_t)((S + Bk - 1) / Bk);
-  hipError_t e = vsa::launch_classify(make_geom(grid, layout), table, U, Bq, Bk, nQ, nK, *out,
+  hipError_t e = vsa::launch_classify(make_geom(grid, layout), table, U, Bq, Bk, round_tiles, nQ, nK, *out,
                                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "classify launch");
   return ok();
@@ -256,7 +264,7 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   if (S != S_grid) return fail(VSA_ERR_INVALID_ARG, "S=%d but grid gives T*Hg*Wg=%lld", S, S_grid);
   if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (D != 64 && D != 128) return fail(VSA_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", D);
-  if (flags & ~(VSA_FWD_FORCE_MASK | VSA_FWD_REORDER_IO | VSA_FWD_WRITE_LSE))
+  if (flags & ~(VSA_FWD_FORCE_MASK | VSA_FWD_REORDER_IO | VSA_FWD_WRITE_LSE | VSA_FWD_TILE_ALIGNED))
     return fail(VSA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if ((flags & VSA_FWD_WRITE_LSE) && !lse) return fail(VSA_ERR_INVALID_ARG, "VSA_FWD_WRITE_LSE needs lse");
   if (dtype == VSA_BF16) {
@@ -294,6 +302,7 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   a.nK = (S + Bk - 1) / Bk;
   a.scale = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
   a.force_mask = (flags & VSA_FWD_FORCE_MASK) ? 1 : 0;
+  a.pad_only = (flags & VSA_FWD_TILE_ALIGNED) ? 1 : 0;
   a.write_lse = (flags & VSA_FWD_WRITE_LSE) ? 1 : 0;
   a.lse_frame_major = reorder ? 1 : 0;
   a.lse = lse;

@@ -400,6 +400,12 @@ VSA_HD void run_advance(const Geom& g, RunCursor& c, int len) {
 }
 
 // Keep bits of keys [c0, min(c0 + nbits, S)) for query q (nbits <= 64).
+// keys [c0, c0 + nbits) that lie before S (the only element mask of a tile-aligned list)
+VSA_HD uint64_t real_key_mask(const Geom& g, int c0, int nbits) {
+  const int n = imin(c0 + nbits, g.S) - c0;
+  return n <= 0 ? 0ull : bit_range(0, n - 1);
+}
+
 VSA_HD uint64_t tile_row_mask(const Geom& g, const DevMask& m, const QueryPos& q, int c0,
                               int nbits) {
   int end = imin(c0 + nbits, g.S);

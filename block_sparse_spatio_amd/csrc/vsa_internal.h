@@ -41,8 +41,8 @@ struct HeadMap {
 
 // ---- launch wrappers (defined next to their kernels) ----
 hipError_t launch_classify(const Geom& g, const MaskTable& masks, int32_t U, int32_t Bq,
-                           int32_t Bk, int32_t nQ, int32_t nK, const vsa_tile_lists& out,
-                           hipStream_t stream);
+                           int32_t Bk, int32_t round_tiles, int32_t nQ, int32_t nK,
+                           const vsa_tile_lists& out, hipStream_t stream);
 
 struct FwdArgs {
   const void* q;
@@ -61,6 +61,7 @@ struct FwdArgs {
   int32_t Bq, Bk;
   float scale;
   int32_t force_mask;
+  int32_t pad_only;     // boundary tiles mask only keys past S (tile-aligned lists)
   int32_t write_lse;
   int32_t lse_frame_major;  // executed order is tile-major; write lse in frame-major order
   Geom g;

@@ -149,12 +149,28 @@ vsa_status vsa_classify_tiles(const vsa_grid* grid, vsa_layout layout,
                               const vsa_mask_desc* masks, int32_t H, int32_t Bq,
                               int32_t Bk, const vsa_tile_lists* out, void* stream);
 
+/* Tile-aligned rounding (Sparse VideoGen on TPU, "aligning the sparse mask with
+ * execution", configuration B3).  With VSA_CLASSIFY_ROUND_TILES each BOUNDARY tile is
+ * rounded to all-or-nothing on its real pairs (both positions < S): kept when at least
+ * half of them are kept by the mask, else dropped.  A kept tile is FULL, or BOUNDARY if
+ * it reaches past S (then only the padding is masked).  FULL and EMPTY tiles are
+ * unchanged.  The rounded lists define a slightly different mask; run the forward on
+ * them with VSA_FWD_TILE_ALIGNED.  Needs Bk <= 64.  Otherwise as vsa_classify_tiles
+ * (which is vsa_classify_tiles_ex with flags = 0). */
+#define VSA_CLASSIFY_ROUND_TILES 1
+vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout,
+                                 const vsa_mask_desc* masks, int32_t H, int32_t Bq,
+                                 int32_t Bk, int32_t flags, const vsa_tile_lists* out,
+                                 void* stream);
+
 /* Attention forward ----------------------------------------------------------- */
 
 #define VSA_FWD_FORCE_MASK 1  /* ablation: run every listed tile through the masked path */
 #define VSA_FWD_REORDER_IO 2  /* TILE_MAJOR only: q/k/v/o are frame-major; reorder into the
                                  workspace, attend in tile-major order, reorder O back */
 #define VSA_FWD_WRITE_LSE 4   /* write lse (must then be non-NULL) */
+#define VSA_FWD_TILE_ALIGNED 8  /* listed BOUNDARY tiles mask only keys past S: the
+                                   forward of lists from VSA_CLASSIFY_ROUND_TILES */
 
 /* Workspace bytes vsa_sparse_attn_fwd needs for these arguments: for bf16,
  * B*H*D*S64 elements (S64 = S rounded up to a multiple of 64) that hold V

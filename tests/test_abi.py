@@ -187,3 +187,14 @@ def test_merge_validation(kw, status, needle):
     st, msg = _call_merge(**kw)
     assert st == status, msg
     assert needle in msg
+
+
+def test_classify_ex_validation():
+    lib = vsa.load()
+    arr = _lib.make_masks([W.mask_spatial(1)])
+    lists = _lib.vsa_tile_lists(0x10, 0x20, 0x30, 0x40, 0x50)
+    g = ctypes.byref(_lib.make_grid(W.grid(4, 8, 8)))
+    st = lib.vsa_classify_tiles_ex(g, 0, arr, 1, 64, 64, 2, ctypes.byref(lists), None)
+    assert st == -1 and "flag" in vsa.vsa_last_error()
+    st = lib.vsa_classify_tiles_ex(g, 0, arr, 1, 64, 128, vsa.VSA_CLASSIFY_ROUND_TILES, ctypes.byref(lists), None)
+    assert st == -2 and "Bk <= 64" in vsa.vsa_last_error()

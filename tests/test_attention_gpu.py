@@ -139,6 +139,28 @@ def test_sta_reorder_io_matches_frame_major(gpu_lib):
     assert_close(o2, oracle.attention(q2, k2, v2, g2, "frame", masks2)[0], "bf16", "sta straddling")
 
 
+@pytest.mark.parametrize("case", [0, 1, 2, 5])
+def test_tile_aligned_forward(gpu_lib, case):
+    """Rounded lists (B3) with VSA_FWD_TILE_ALIGNED equal the oracle's attention under
+    the rounded mask (padding masked only), bf16 and fp32."""
+    g, layout, masks, D, B = SMALL_CASES[case]
+    S = W.seq_len(g)
+    for dtype, Bq, Bk in (("bf16", 128, 64), ("f32", 64, 32)):
+        q, k, v = W.qkv(B, S, len(masks), D, dtype, seed=200 + case)
+        say(f"tile-aligned case={case} {dtype} Bq={Bq} Bk={Bk}")
+        d = dev()
+        tiles = vsa.vsa_classify_tiles(g, layout, masks, Bq, Bk, device=d, round_tiles=True)
+        o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, layout, masks, tiles,
+                                         flags=vsa.VSA_FWD_TILE_ALIGNED | vsa.VSA_FWD_WRITE_LSE)
+        torch.cuda.synchronize()
+        ref_o, ref_lse = oracle.attention(q, k, v, g, layout, masks, round_tiles=(Bq, Bk))
+        assert_close(o, ref_o, dtype, f"tile-aligned case {case} {dtype}")
+        fin = np.isfinite(ref_lse)
+        got = lse.cpu().numpy()
+        assert np.array_equal(np.isneginf(got), ~fin)
+        assert np.abs(got[fin] - ref_lse[fin]).max() <= (5e-3 if dtype == "bf16" else 1e-5)
+
+
 # ---------------------------------------------------------------------------
 # full-size configurations, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------

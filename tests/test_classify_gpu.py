@@ -99,3 +99,55 @@ def test_classify_null_cls(gpu_lib):
     ref = oracle.classify(g, "frame", masks[0], 32, 16)
     t["cls"] = None
     check_lists_against(t, 0, ref["q_tiles"], ref["cls"])
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_classify_rounded_random_small(gpu_lib, seed):
+    """Tile-aligned rounding (B3) on the GPU equals the oracle's rounded classes."""
+    rng = np.random.default_rng(1000 + seed)
+    layout = "tile" if seed % 3 == 2 else "frame"
+    if layout == "tile":
+        tile = tuple(int(x) for x in rng.integers(1, 4, 3))
+        g = W.grid(tile[0] * int(rng.integers(1, 4)), tile[1] * int(rng.integers(1, 4)),
+                   tile[2] * int(rng.integers(1, 5)), tile)
+    else:
+        g = W.grid(int(rng.integers(1, 7)), int(rng.integers(1, 9)), int(rng.integers(1, 12)))
+    H = int(rng.integers(1, 4))
+    masks = [_random_desc(rng, layout) for _ in range(H)]
+    Bq = int(rng.choice([1, 8, 16, 32, 64, 128]))
+    Bk = int(rng.choice([1, 5, 16, 32, 64]))
+    say(f"classify rounded seed={seed} grid={g} layout={layout} Bq={Bq} Bk={Bk} masks={masks}")
+    tiles = gpu_lib.vsa_classify_tiles(g, layout, masks, Bq, Bk, device=dev(), round_tiles=True)
+    torch.cuda.synchronize()
+    hm, U = gpu_lib.vsa_unique_masks(masks)
+    for h, desc in enumerate(masks):
+        ref = oracle.classify(g, layout, desc, Bq, Bk, round_tiles=True)
+        check_lists_against(tiles, hm[h], ref["q_tiles"], ref["cls"])
+
+
+@pytest.mark.parametrize("name,Bq", [("wan_single", 128), ("wan_mixed", 128)])
+def test_classify_rounded_full_configs(gpu_lib, name, Bq):
+    cfg = W.config(name)
+    g, layout, masks = cfg["grid"], cfg["layout"], cfg["masks"]
+    say(f"classify rounded full config {name} Bq={Bq}")
+    tiles = gpu_lib.vsa_classify_tiles(g, layout, masks, Bq, cfg["Bk"], device=dev(), round_tiles=True)
+    exact = gpu_lib.vsa_classify_tiles(g, layout, masks, Bq, cfg["Bk"], device=dev())
+    torch.cuda.synchronize()
+    hm, U = gpu_lib.vsa_unique_masks(masks)
+    rng = np.random.default_rng(8)
+    seen = set()
+    for h, desc in enumerate(masks):
+        u = hm[h]
+        if u in seen:
+            continue
+        seen.add(u)
+        qts = _sampled_q_tiles(tiles["nQ"], rng, 3)
+        ref = oracle.classify(g, layout, desc, Bq, cfg["Bk"], q_tiles=qts, round_tiles=True)
+        check_lists_against(tiles, u, qts, ref["cls"])
+    # rounding touches only boundary tiles, and boundary tiles remain only at the tail
+    ce, cr = exact["cls"].cpu(), tiles["cls"].cpu()
+    assert torch.equal(ce[ce != 2], cr[ce != 2])
+    S = W.seq_len(g)
+    nK = cr.shape[-1]
+    if S % cfg["Bk"] == 0 and S % Bq:
+        assert torch.all(cr[:, :-1] != 2)
