@@ -6,7 +6,7 @@ CPU-baseline leg may import it.  It shares no code with the HIP library and
 imports nothing from it; the product path never calls into it.
 
 Contents
-  coords     token coordinates of an executed position (frame-major / tile-major)
+  coords     token coordinates of an executed position (frame-, tile-, position-major)
   masks      the boolean keep-predicate of each mask kind
   classify   per-(query-tile, key-tile) full / boundary / empty classes and lists
   attention  masked softmax attention written from its definition
@@ -24,5 +24,5 @@ from .classify import classify, EMPTY, FULL, BOUNDARY  # noqa: F401
 from .classify import rounded_keep_rows  # noqa: F401
 from .attention import attention  # noqa: F401
 from .profile import profile_heads  # noqa: F401
-from .reorder import tile_major_permutation, reorder_tokens  # noqa: F401
+from .reorder import layout_permutation, tile_major_permutation, reorder_tokens  # noqa: F401
 from .merge import merge_partials  # noqa: F401

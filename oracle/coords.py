@@ -13,6 +13,15 @@ tokens.  Two orders are used:
   ordered row-major over the tile grid, and tokens row-major inside a tile.
   The pages fix only that tiles are contiguous; the row-major orders are the
   plain reading.
+* position-major: the temporal order of Sparse VideoGen on TPU ("arranging tokens
+  for temporal access"): tokens are permuted from (frame, row, column) to (row,
+  column, frame), so that one spatial position's tokens across frames are
+  contiguous and a temporal head's diagonal stripes become contiguous bands
+  (video-DiT attention blog, section 7.2, the (h, w, t) reorder).  Frame 0 is kept
+  as a leading block in frame-major order, so that the first-frame sink keys stay
+  contiguous: positions [0, Hg*Wg) are frame 0 row-major, and position
+  Hg*Wg + s*(T-1) + (t-1) holds frame t >= 1 at spatial index s = y*Wg + x.  The
+  leading sink block is this implementation's reading; the page permutes all frames.
 """
 from __future__ import annotations
 
@@ -31,7 +40,7 @@ def _check_tile(grid):
 def token_coords(grid, layout, pos):
     """Return (t, y, x) int64 arrays for executed positions ``pos`` (any int array).
 
-    layout is "frame" or "tile"."""
+    layout is "frame", "tile" or "position"."""
     pos = np.asarray(pos, dtype=np.int64)
     T, Hg, Wg = grid["T"], grid["Hg"], grid["Wg"]
     if layout == "frame":
@@ -47,6 +56,14 @@ def token_coords(grid, layout, pos):
         tau_t, tau_h, tau_w = tau // (nH * nW), (tau // nW) % nH, tau % nW
         i_t, i_h, i_w = iota // (bh * bw), (iota // bw) % bh, iota % bw
         return tau_t * bt + i_t, tau_h * bh + i_h, tau_w * bw + i_w
+    if layout == "position":
+        HW = Hg * Wg
+        head = pos < HW
+        q = np.where(head, 0, pos - HW)
+        T1 = max(T - 1, 1)
+        s = np.where(head, pos, q // T1)
+        t = np.where(head, 0, 1 + q % T1)
+        return t, s // Wg, s % Wg
     raise ValueError(f"unknown layout {layout!r}")
 
 

@@ -493,6 +493,59 @@ def test_rounding_leaves_tile_aligned_masks_unchanged():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def test_position_major_order_by_hand():
+    """Position-major order on a 3 x 2 x 2 grid: frame 0 first (row-major), then for
+    each spatial position its frames 1 and 2 (written out from the definition)."""
+    g = W.grid(3, 2, 2)
+    perm = oracle.layout_permutation(g, "position")
+    assert list(perm) == [0, 1, 2, 3, 4, 8, 5, 9, 6, 10, 7, 11]
+
+
+@pytest.mark.parametrize("T,Hg,Wg", [(1, 3, 5), (2, 4, 3), (5, 3, 7), (21, 2, 3)])
+def test_position_major_is_a_permutation(T, Hg, Wg):
+    g = W.grid(T, Hg, Wg)
+    S = T * Hg * Wg
+    perm = oracle.layout_permutation(g, "position")
+    assert np.array_equal(np.sort(perm), np.arange(S))
+    if T <= 2:  # the frame-0 block followed by one frame in spatial order is frame-major
+        assert np.array_equal(perm, np.arange(S))
+    t, y, x = oracle.token_coords(g, "position", np.arange(S))
+    assert np.all(t[: Hg * Wg] == 0)
+    if T > 1:  # after the leading block, consecutive positions step through frames
+        tt = t[Hg * Wg:].reshape(Hg * Wg, T - 1)
+        assert np.all(tt == np.arange(1, T)[None, :])
+
+
+def test_position_major_attention_matches_frame_major():
+    """Attention depends on coordinates only: permuting inputs into position-major
+    order and attending there gives the permuted frame-major result."""
+    g = W.grid(4, 3, 3)
+    S = W.seq_len(g)
+    q, k, v = (_rand((1, S, 2, 8), 70 + s) for s in range(3))
+    masks = [W.mask_temporal(1), W.mask_stripe(1, 0, 2, 2, 1, 4)]
+    ref, ref_l = oracle.attention(q, k, v, g, "frame", masks)
+    perm = oracle.layout_permutation(g, "position")
+    o, l = oracle.attention(q[:, perm], k[:, perm], v[:, perm], g, "position", masks)
+    assert np.abs(o - ref[:, perm]).max() < 1e-13
+    assert np.abs(l - ref_l[:, :, perm]).max() < 1e-13
+
+
+def test_position_major_turns_temporal_stripes_into_full_tiles():
+    """A temporal head (same position across frames, plus the frame-0 sink) has a
+    boundary tile per frame in every query tile in frame-major order, and none outside
+    the sink block's query tiles in position-major order (Sparse VideoGen on TPU,
+    arranging tokens for temporal access)."""
+    g = W.grid(9, 4, 8)  # 32 positions x 8 frames after the sink block
+    desc = W.mask_box(-1, 0, 0, sink_frames=1)
+    fr = oracle.classify(g, "frame", desc, 8, 8)["cls"]
+    po = oracle.classify(g, "position", desc, 8, 8)["cls"]
+    assert np.all((fr == oracle.BOUNDARY).sum(axis=1) == 8)  # 8 frames, one partial tile each
+    # in position-major order every query tile (8 frames of one position) keeps the
+    # sink block (4 full tiles) and its own 8-frame tile: full tiles only
+    assert not np.any(po[4:] == oracle.BOUNDARY)
+    assert np.all((po[4:] == oracle.FULL).sum(axis=1) == 5)
+
+
 def test_tile_major_equals_frame_major_after_inverse():
     g = W.grid(4, 4, 6, (2, 2, 3))
     S = 96
