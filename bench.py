@@ -183,6 +183,9 @@ def main():
     ap.add_argument("--flags", type=int, default=0, help="extra VSA_FWD_* flags (e.g. 1 = B1 ablation)")
     ap.add_argument("--round-tiles", action="store_true",
                     help="tile-aligned rounding of the masks (B3): rounded lists, forward with VSA_FWD_TILE_ALIGNED")
+    ap.add_argument("--temporal-layout", choices=("frame", "position"), default="frame",
+                    help="executed order of the temporal heads of wan_mixed: position = each spatial "
+                         "position's frames contiguous, reordered inside the call (frame-major I/O)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-keep dense run")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -216,11 +219,18 @@ def main():
         return 0
     cfg = W.config(args.config)
     g, layout, masks = cfg["grid"], cfg["layout"], cfg["masks"]
+    if args.temporal_layout == "position":
+        if "position_masks" not in cfg:
+            print(f"--temporal-layout position needs a workload with temporal heads (wan_mixed), not {args.config}",
+                  file=sys.stderr)
+            return 2
+        masks = cfg["position_masks"]
     B, H, D = cfg["B"], cfg["H"], cfg["D"]
     S = W.seq_len(g)
     Bq = args.Bq or cfg["Bq"]
     Bk = cfg["Bk"]
-    reorder = layout == "tile"
+    head_lays = W.head_layouts(masks, layout)
+    reorder = any(x != "frame" for x in head_lays)
     flags = args.flags | (vsa.VSA_FWD_REORDER_IO if reorder else 0) | (vsa.VSA_FWD_TILE_ALIGNED if args.round_tiles else 0)
     print(f"[bench] {args.config}: B={B} S={S} H={H} D={D} Bq={Bq} Bk={Bk} drawing inputs", file=sys.stderr,
           flush=True)
@@ -285,14 +295,16 @@ def main():
     dense = {}
     if not args.no_dense:
         all_masks = [W.mask_all()] * H
+        # dense attention in the call's layout (a frame-major call needs no reorder)
+        dflags = flags & ~vsa.VSA_FWD_REORDER_IO if layout == "frame" else flags
         dt_tiles = vsa.vsa_classify_tiles(g, layout, all_masks, Bq, Bk, device=dev, with_cls=False)
         for _ in range(2):
-            vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, all_masks, dt_tiles, flags=flags, o=o, workspace=ws)
+            vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, all_masks, dt_tiles, flags=dflags, o=o, workspace=ws)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         n_dense = 3
         e0.record(stream)
         for _ in range(n_dense):
-            vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, all_masks, dt_tiles, flags=flags, o=o, workspace=ws)
+            vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, all_masks, dt_tiles, flags=dflags, o=o, workspace=ws)
         e1.record(stream)
         torch.cuda.synchronize()
         d_ms = e0.elapsed_time(e1) / n_dense
@@ -304,14 +316,14 @@ def main():
     if profile:
         extra["profile_ms"] = round(float(np.mean(prof_ms)), 4)
         extra["profile_kv_gbs"] = round(2.0 * B * S * H * D * 2 / (np.mean(prof_ms) * 1e-3) / 1e9, 1)
-    if layout == "tile":
-        # the tile-major reorder alone, on one tensor: HBM GB/s (read + write)
+    if reorder:
+        # the per-head token reorder alone, on one tensor: HBM GB/s (read + write)
         y = torch.empty_like(qd)
-        vsa.vsa_reorder_tokens(qd, g, dst=y, stream=stream)
+        vsa.vsa_reorder_heads(qd, g, head_lays, dst=y, stream=stream)
         r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         r0.record(stream)
         for _ in range(5):
-            vsa.vsa_reorder_tokens(qd, g, dst=y, stream=stream)
+            vsa.vsa_reorder_heads(qd, g, head_lays, dst=y, stream=stream)
         r1.record(stream)
         torch.cuda.synchronize()
         r_ms = r0.elapsed_time(r1) / 5
@@ -356,7 +368,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "B": B, "S": S, "H": H, "D": D, "grid": [g["T"], g["Hg"], g["Wg"]],
                    "layout": layout, "Bq": Bq, "Bk": Bk, "masks": sorted({m["kind"] for m in masks}),
-                   "unique_masks": U, "flags": flags, "tile_rounding": bool(args.round_tiles)},
+                   "unique_masks": U, "flags": flags, "tile_rounding": bool(args.round_tiles),
+                   "head_layouts": {x: head_lays.count(x) for x in sorted(set(head_lays))}},
         "attn_ms_per_call": round(attn_ms, 4),
         "attn_ms_p10_p90": [round(float(np.percentile(fwd_ms, 10)), 4), round(float(np.percentile(fwd_ms, 90)), 4)],
         "classify_ms": round(float(np.mean(cls_ms)), 4),
@@ -374,7 +387,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd_bf16_kernel", "kernel_hash": khash},
     }
-    if not args.no_cpu and layout == "frame":
+    if not args.no_cpu and not reorder:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, tiles, head_map)
     print(json.dumps(rec), flush=True)

@@ -18,16 +18,19 @@ LIB_PATH = os.path.join(_HERE, "libvsa.so")
 
 VSA_OK, VSA_ERR_INVALID_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_WORKSPACE, VSA_ERR_HIP = 0, -1, -2, -3, -4
 VSA_BF16, VSA_F32 = 0, 1
-VSA_LAYOUT_FRAME_MAJOR, VSA_LAYOUT_TILE_MAJOR = 0, 1
+VSA_LAYOUT_FRAME_MAJOR, VSA_LAYOUT_TILE_MAJOR, VSA_LAYOUT_POSITION_MAJOR = 0, 1, 2
+VSA_HEAD_LAYOUT_CALL, VSA_HEAD_LAYOUT_FRAME, VSA_HEAD_LAYOUT_TILE, VSA_HEAD_LAYOUT_POSITION = 0, 1, 2, 3
 VSA_MASK_ALL, VSA_MASK_BOX, VSA_MASK_STRIPE, VSA_MASK_STA = 0, 1, 2, 3
 VSA_TILE_EMPTY, VSA_TILE_FULL, VSA_TILE_BOUNDARY = 0, 1, 2
 VSA_FWD_FORCE_MASK, VSA_FWD_REORDER_IO, VSA_FWD_WRITE_LSE, VSA_FWD_TILE_ALIGNED = 1, 2, 4, 8
 VSA_CLASSIFY_ROUND_TILES = 1
 
 _KINDS = {"all": VSA_MASK_ALL, "box": VSA_MASK_BOX, "stripe": VSA_MASK_STRIPE, "sta": VSA_MASK_STA}
-_LAYOUTS = {"frame": VSA_LAYOUT_FRAME_MAJOR, "tile": VSA_LAYOUT_TILE_MAJOR}
+_LAYOUTS = {"frame": VSA_LAYOUT_FRAME_MAJOR, "tile": VSA_LAYOUT_TILE_MAJOR, "position": VSA_LAYOUT_POSITION_MAJOR}
+_HEAD_LAYOUTS = {"call": VSA_HEAD_LAYOUT_CALL, "frame": VSA_HEAD_LAYOUT_FRAME, "tile": VSA_HEAD_LAYOUT_TILE,
+                 "position": VSA_HEAD_LAYOUT_POSITION}
 _MASK_FIELDS = ("kind", "sink_frames", "rt", "rh", "rw", "Tw", "To", "Ts", "Sw", "So", "Ss",
-                "win_t", "win_h", "win_w")
+                "win_t", "win_h", "win_w", "head_layout")
 
 
 class vsa_grid(ctypes.Structure):
@@ -66,6 +69,7 @@ _SIGNATURES = {
                                  ctypes.POINTER(vsa_mask_desc), ctypes.POINTER(vsa_tile_lists), _I, _I,
                                  ctypes.c_float, _I, _P, ctypes.c_size_t, _P]),
     "vsa_reorder_tokens": (_I, [_P, _P, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I, _P]),
+    "vsa_reorder_heads": (_I, [_P, _P, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), ctypes.POINTER(_I), _I, _P]),
     "vsa_merge_partials": (_I, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _P, _P, _I, _I, _I, _I, _I, _P]),
     "vsa_profile_workspace_bytes": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
     "vsa_profile_heads": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I, _P, _I,
@@ -115,6 +119,8 @@ def make_masks(masks):
         vals = dict(m)
         kind = vals["kind"]
         vals["kind"] = _KINDS[kind] if isinstance(kind, str) else int(kind)
+        hl = vals.get("head_layout", 0)
+        vals["head_layout"] = _HEAD_LAYOUTS[hl] if isinstance(hl, str) else int(hl)
         arr[i] = vsa_mask_desc(*[int(vals.get(f, 0)) for f in _MASK_FIELDS])
     return arr
 
@@ -256,6 +262,21 @@ def vsa_reorder_tokens(src, grid, inverse=False, dst=None, stream=None):
         dst = torch.empty_like(src)
     _check(load().vsa_reorder_tokens(_ptr(src), _ptr(dst), _dtype(src), B, H, D, ctypes.byref(make_grid(grid)),
                                      1 if inverse else 0, _stream(stream, src.device)))
+    return dst
+
+
+def vsa_reorder_heads(src, grid, layouts, inverse=False, dst=None, stream=None):
+    """Per-head reorder of src [B, S, H, D]; layouts: H layout names or VSA_LAYOUT_* values."""
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous [B, S, H, D]")
+    B, S, H, D = src.shape
+    if len(layouts) != H:
+        raise ValueError(f"{len(layouts)} layouts for {H} heads")
+    if dst is None:
+        dst = torch.empty_like(src)
+    lay = (_I * H)(*[_layout(x) for x in layouts])
+    _check(load().vsa_reorder_heads(_ptr(src), _ptr(dst), _dtype(src), B, H, D, ctypes.byref(make_grid(grid)),
+                                    lay, 1 if inverse else 0, _stream(stream, src.device)))
     return dst
 
 

@@ -53,7 +53,6 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   __shared__ __attribute__((aligned(1024))) char vbuf0[C::TILE_B];
   __shared__ __attribute__((aligned(1024))) char vbuf1[C::TILE_B];
 
-  const Geom& g = a.g;
   const int S = a.S, H = a.H;
   const int Bq = 32 * NW;
 
@@ -71,6 +70,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 
   const int slot = hm.slot[h];
   const DevMask m = masks.m[slot];
+  const Geom g = head_geom(a.g, m);
   const size_t lrow = (size_t)slot * a.nQ + qt;
   // List lengths and entries are clamped to the list row, so malformed lists cannot
   // send a load outside the tensors.  The lists come in as read-only, non-aliased

@@ -16,13 +16,13 @@ template <int D, int BKT>
 __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(FwdArgs a, MaskTable masks, HeadMap hm) {
   __shared__ float ks[BKT][D];
   __shared__ float vs[BKT][D];
-  const Geom& g = a.g;
   const int S = a.S, H = a.H;
   const int qt = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int slot = hm.slot[h];
   const DevMask m = masks.m[slot];
+  const Geom g = head_geom(a.g, m);
   const size_t lrow = (size_t)slot * a.nQ + qt;
   const int nf = imin(imax(a.n_full[lrow], 0), a.nK);
   const int nb = imin(imax(a.n_bnd[lrow], 0), a.nK);

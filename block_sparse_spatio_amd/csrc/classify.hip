@@ -21,7 +21,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-__global__ __launch_bounds__(kThreads) void classify_kernel(Geom g, MaskTable masks, int Bq, int Bk,
+__global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTable masks, int Bq, int Bk,
                                                             int round_tiles, int nQ, int nK, uint8_t* __restrict__ cls,
                                                             int32_t* __restrict__ n_full,
                                                             int32_t* __restrict__ n_bnd,
@@ -30,6 +30,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g, MaskTable ma
   const int qt = blockIdx.x;
   const int u = blockIdx.y;
   const DevMask m = masks.m[u];
+  const Geom g = head_geom(g_call, m);
   const int r0 = qt * Bq;
   const int r1 = imin(r0 + Bq, g.S);
   const bool q_padded = (r0 + Bq) > g.S;

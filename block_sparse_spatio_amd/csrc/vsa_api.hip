@@ -44,7 +44,7 @@ vsa_status check_grid(const vsa_grid* g, vsa_layout layout, bool need_tile, long
     return fail(VSA_ERR_UNSUPPORTED, "grid dimensions above 32767 are not supported");
   const long long s = (long long)g->T * g->Hg * g->Wg;
   if (s > kMaxS) return fail(VSA_ERR_UNSUPPORTED, "sequence length %lld above 2^30", s);
-  if (layout != VSA_LAYOUT_FRAME_MAJOR && layout != VSA_LAYOUT_TILE_MAJOR)
+  if (layout != VSA_LAYOUT_FRAME_MAJOR && layout != VSA_LAYOUT_TILE_MAJOR && layout != VSA_LAYOUT_POSITION_MAJOR)
     return fail(VSA_ERR_INVALID_ARG, "unknown layout %d", (int)layout);
   const bool tile_set = g->tile_t > 0 || g->tile_h > 0 || g->tile_w > 0;
   if (layout == VSA_LAYOUT_TILE_MAJOR || need_tile || tile_set) {
@@ -77,9 +77,13 @@ bool fits16(long long v) { return v >= -32768 && v <= 32767; }
 
 // Validate one descriptor and convert it to the kernels' 16-bit form.  Periods, widths,
 // radii and windows beyond what the grid can reach are clamped to an equivalent value.
-vsa_status normalise(const vsa_mask_desc& d, const vsa_grid* g, int index, vsa::DevMask* out) {
+// `layout` is the call's layout, which heads with head_layout = VSA_HEAD_LAYOUT_CALL use.
+vsa_status normalise(const vsa_mask_desc& d, const vsa_grid* g, vsa_layout layout, int index, vsa::DevMask* out) {
   memset(out, 0, sizeof *out);
   if (d.sink_frames < 0) return fail(VSA_ERR_INVALID_ARG, "mask %d: sink_frames < 0", index);
+  if (d.head_layout < VSA_HEAD_LAYOUT_CALL || d.head_layout > VSA_HEAD_LAYOUT_POSITION)
+    return fail(VSA_ERR_INVALID_ARG, "mask %d: unknown head_layout %d", index, d.head_layout);
+  out->layout = (int16_t)(d.head_layout == VSA_HEAD_LAYOUT_CALL ? (int)layout : d.head_layout - 1);
   out->kind = (int16_t)d.kind;
   out->sink = (int16_t)(d.sink_frames < g->T ? d.sink_frames : g->T);
   const bool box_unused = d.rt == 0 && d.rh == 0 && d.rw == 0;
@@ -134,15 +138,17 @@ vsa_status normalise(const vsa_mask_desc& d, const vsa_grid* g, int index, vsa::
   return VSA_OK;
 }
 
-bool any_sta(const vsa_mask_desc* m, int n) {
+// Whether the grid's 3D tile must be set: some mask is sliding-tile, or some head runs
+// in the tile-major order.
+bool needs_tile(const vsa_mask_desc* m, int n) {
   for (int i = 0; i < n; ++i)
-    if (m[i].kind == VSA_MASK_STA) return true;
+    if (m[i].kind == VSA_MASK_STA || m[i].head_layout == VSA_HEAD_LAYOUT_TILE) return true;
   return false;
 }
 
 // Dedupe + normalise H descriptors into a table.  head_map[h] = slot.
-vsa_status build_table(const vsa_mask_desc* masks, int32_t H, const vsa_grid* g, vsa::MaskTable* table,
-                       vsa::HeadMap* hm, int32_t* U) {
+vsa_status build_table(const vsa_mask_desc* masks, int32_t H, const vsa_grid* g, vsa_layout layout,
+                       vsa::MaskTable* table, vsa::HeadMap* hm, int32_t* U) {
   if (!masks) return fail(VSA_ERR_INVALID_ARG, "masks is NULL");
   if (H <= 0) return fail(VSA_ERR_INVALID_ARG, "H must be positive");
   if (H > VSA_MAX_HEADS) return fail(VSA_ERR_UNSUPPORTED, "H=%d above VSA_MAX_HEADS", H);
@@ -157,7 +163,7 @@ vsa_status build_table(const vsa_mask_desc* masks, int32_t H, const vsa_grid* g,
     if (slot < 0) {
       if (u == VSA_MAX_UNIQUE_MASKS)
         return fail(VSA_ERR_UNSUPPORTED, "more than %d distinct masks", VSA_MAX_UNIQUE_MASKS);
-      vsa_status st = normalise(masks[h], g, h, &table->m[u]);
+      vsa_status st = normalise(masks[h], g, layout, h, &table->m[u]);
       if (st != VSA_OK) return st;
       first[u] = h;
       slot = u++;
@@ -212,7 +218,7 @@ vsa_status vsa_classify_tiles(const vsa_grid* grid, vsa_layout layout, const vsa
 vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout, const vsa_mask_desc* masks, int32_t H,
                                  int32_t Bq, int32_t Bk, int32_t flags, const vsa_tile_lists* out, void* stream) {
   long long S;
-  vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && any_sta(masks, H), &S);
+  vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && needs_tile(masks, H), &S);
   if (st != VSA_OK) return st;
   if (Bq < 1 || Bk < 1 || Bq > 4096 || Bk > 4096) return fail(VSA_ERR_INVALID_ARG, "tile sizes must be in 1..4096");
   if (!out || !out->n_full || !out->n_bnd || !out->full_idx || !out->bnd_idx)
@@ -223,7 +229,7 @@ vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout, const 
   vsa::MaskTable table;
   vsa::HeadMap hm;
   int32_t U = 0;
-  st = build_table(masks, H, grid, &table, &hm, &U);
+  st = build_table(masks, H, grid, layout, &table, &hm, &U);
   if (st != VSA_OK) return st;
   const int32_t nQ = (int32_t)((S + Bq - 1) / Bq), nK = (int32_t)((S + Bk - 1) / Bk);
   hipError_t e = vsa::launch_classify(make_geom(grid, layout), table, U, Bq, Bk, round_tiles, nQ, nK, *out,
@@ -256,7 +262,7 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
                                const vsa_mask_desc* masks, const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk,
                                float scale, int32_t flags, void* workspace, size_t ws_bytes, void* stream) {
   long long S_grid;
-  vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && any_sta(masks, H), &S_grid);
+  vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && needs_tile(masks, H), &S_grid);
   if (st != VSA_OK) return st;
   if (!q || !k || !v || !o) return fail(VSA_ERR_INVALID_ARG, "q, k, v, o must be non-NULL");
   if (o == q || o == k || o == v) return fail(VSA_ERR_INVALID_ARG, "o must not alias q, k or v");
@@ -278,15 +284,22 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
     return fail(VSA_ERR_INVALID_ARG, "tile lists must be non-NULL");
   if (!isfinite(scale)) return fail(VSA_ERR_INVALID_ARG, "scale is not finite");
   const bool reorder = (flags & VSA_FWD_REORDER_IO) != 0;
-  if (reorder && layout != VSA_LAYOUT_TILE_MAJOR)
-    return fail(VSA_ERR_INVALID_ARG, "VSA_FWD_REORDER_IO needs the tile-major layout");
   const size_t eb = elem_size(dtype);
   const size_t nelem = (size_t)B * S * H * D;
   vsa::MaskTable table;
   vsa::HeadMap hm;
   int32_t U = 0;
-  st = build_table(masks, H, grid, &table, &hm, &U);
+  st = build_table(masks, H, grid, layout, &table, &hm, &U);
   if (st != VSA_OK) return st;
+  vsa::HeadLayouts hl;
+  memset(&hl, 0, sizeof hl);
+  bool any_permuted = false;
+  for (int h = 0; h < H; ++h) {
+    hl.lay[h] = (uint8_t)table.m[hm.slot[h]].layout;
+    any_permuted = any_permuted || hl.lay[h] != VSA_LAYOUT_FRAME_MAJOR;
+  }
+  if (reorder && !any_permuted)
+    return fail(VSA_ERR_INVALID_ARG, "VSA_FWD_REORDER_IO needs a head whose layout is not frame-major");
   const size_t need = fwd_ws_bytes(B, S, H, D, dtype, flags);
   if (need && (!workspace || ws_bytes < need))
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
@@ -316,9 +329,9 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
     void* wk = ws + nelem * eb;
     void* wv = ws + 2 * nelem * eb;
     hipError_t e;
-    if ((e = vsa::launch_reorder(q, wq, (int)eb, B, H, D, G, 0, hs)) != hipSuccess) return hip_fail(e, "reorder q");
-    if ((e = vsa::launch_reorder(k, wk, (int)eb, B, H, D, G, 0, hs)) != hipSuccess) return hip_fail(e, "reorder k");
-    if ((e = vsa::launch_reorder(v, wv, (int)eb, B, H, D, G, 0, hs)) != hipSuccess) return hip_fail(e, "reorder v");
+    if ((e = vsa::launch_reorder(q, wq, (int)eb, B, H, D, G, hl, 0, hs)) != hipSuccess) return hip_fail(e, "reorder q");
+    if ((e = vsa::launch_reorder(k, wk, (int)eb, B, H, D, G, hl, 0, hs)) != hipSuccess) return hip_fail(e, "reorder k");
+    if ((e = vsa::launch_reorder(v, wv, (int)eb, B, H, D, G, hl, 0, hs)) != hipSuccess) return hip_fail(e, "reorder v");
     // each workgroup reads its own query rows before writing the same output rows, so
     // the output may overwrite the reordered queries in place
     a.q = wq; a.k = wk; a.v = wv; a.o = wq;
@@ -338,7 +351,7 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (reorder) {
-    e = vsa::launch_reorder(ws, o, (int)eb, B, H, D, G, 1, hs);
+    e = vsa::launch_reorder(ws, o, (int)eb, B, H, D, G, hl, 1, hs);
     if (e != hipSuccess) return hip_fail(e, "inverse reorder o");
   }
   return ok();
@@ -377,21 +390,44 @@ vsa_status vsa_merge_partials(const void* const* o_parts, const float* const* ls
   return ok();
 }
 
-vsa_status vsa_reorder_tokens(const void* src, void* dst, vsa_dtype dtype, int32_t B, int32_t H, int32_t D,
-                              const vsa_grid* grid, int32_t inverse, void* stream) {
+vsa_status vsa_reorder_heads(const void* src, void* dst, vsa_dtype dtype, int32_t B, int32_t H, int32_t D,
+                             const vsa_grid* grid, const int32_t* layouts, int32_t inverse, void* stream) {
+  if (!layouts) return fail(VSA_ERR_INVALID_ARG, "layouts is NULL");
+  if (H <= 0 || H > VSA_MAX_HEADS) return fail(VSA_ERR_INVALID_ARG, "H must be in 1..%d", VSA_MAX_HEADS);
+  vsa::HeadLayouts hl;
+  memset(&hl, 0, sizeof hl);
+  bool any_tile = false, uniform = true;
+  for (int h = 0; h < H; ++h) {
+    if (layouts[h] != VSA_LAYOUT_FRAME_MAJOR && layouts[h] != VSA_LAYOUT_TILE_MAJOR &&
+        layouts[h] != VSA_LAYOUT_POSITION_MAJOR)
+      return fail(VSA_ERR_INVALID_ARG, "head %d: unknown layout %d", h, layouts[h]);
+    hl.lay[h] = (uint8_t)layouts[h];
+    any_tile = any_tile || layouts[h] == VSA_LAYOUT_TILE_MAJOR;
+    uniform = uniform && layouts[h] == layouts[0];
+  }
   long long S;
-  vsa_status st = check_grid(grid, VSA_LAYOUT_TILE_MAJOR, true, &S);
+  vsa_status st = check_grid(grid, any_tile ? VSA_LAYOUT_TILE_MAJOR : VSA_LAYOUT_FRAME_MAJOR, any_tile, &S);
   if (st != VSA_OK) return st;
   if (!src || !dst) return fail(VSA_ERR_INVALID_ARG, "src and dst must be non-NULL");
   if (src == dst) return fail(VSA_ERR_INVALID_ARG, "src and dst must not alias");
   if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  if (B <= 0 || H <= 0 || D <= 0) return fail(VSA_ERR_INVALID_ARG, "B, H, D must be positive");
+  if (B <= 0 || D <= 0) return fail(VSA_ERR_INVALID_ARG, "B, H, D must be positive");
   if (((long long)H * D * elem_size(dtype)) % 16)
     return fail(VSA_ERR_UNSUPPORTED, "token row of H*D elements must be a multiple of 16 bytes");
-  hipError_t e = vsa::launch_reorder(src, dst, elem_size(dtype), B, H, D, make_geom(grid, VSA_LAYOUT_TILE_MAJOR),
-                                     inverse ? 1 : 0, (hipStream_t)stream);
+  if (!uniform && ((long long)D * elem_size(dtype)) % 16)
+    return fail(VSA_ERR_UNSUPPORTED, "heads with different layouts need D*element size a multiple of 16 bytes");
+  hipError_t e = vsa::launch_reorder(src, dst, elem_size(dtype), B, H, D, make_geom(grid, VSA_LAYOUT_FRAME_MAJOR),
+                                     hl, inverse ? 1 : 0, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "reorder launch");
   return ok();
+}
+
+vsa_status vsa_reorder_tokens(const void* src, void* dst, vsa_dtype dtype, int32_t B, int32_t H, int32_t D,
+                              const vsa_grid* grid, int32_t inverse, void* stream) {
+  if (H <= 0 || H > VSA_MAX_HEADS) return fail(VSA_ERR_INVALID_ARG, "H must be in 1..%d", VSA_MAX_HEADS);
+  int32_t layouts[VSA_MAX_HEADS];
+  for (int h = 0; h < H; ++h) layouts[h] = VSA_LAYOUT_TILE_MAJOR;
+  return vsa_reorder_heads(src, dst, dtype, B, H, D, grid, layouts, inverse, stream);
 }
 
 vsa_status vsa_profile_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n_samples,
@@ -409,7 +445,7 @@ vsa_status vsa_profile_heads(const void* q, const void* k, const void* v, vsa_dt
                              int32_t n_cand, float* err, int32_t* route, float scale, void* workspace,
                              size_t ws_bytes, void* stream) {
   long long S_grid;
-  vsa_status st = check_grid(grid, layout, cands && n_cand > 0 && n_cand <= 4 && any_sta(cands, n_cand), &S_grid);
+  vsa_status st = check_grid(grid, layout, cands && n_cand > 0 && n_cand <= 4 && needs_tile(cands, n_cand), &S_grid);
   if (st != VSA_OK) return st;
   if (!q || !k || !v || !sample_idx || !err || !route)
     return fail(VSA_ERR_INVALID_ARG, "q, k, v, sample_idx, err, route must be non-NULL");
@@ -424,8 +460,10 @@ vsa_status vsa_profile_heads(const void* q, const void* k, const void* v, vsa_dt
   vsa::MaskTable table;
   memset(&table, 0, sizeof table);
   for (int c = 0; c < n_cand; ++c) {
-    st = normalise(cands[c], grid, c, &table.m[c]);
+    st = normalise(cands[c], grid, layout, c, &table.m[c]);
     if (st != VSA_OK) return st;
+    if (table.m[c].layout != (int16_t)layout)
+      return fail(VSA_ERR_UNSUPPORTED, "candidate %d: the profiler scores every candidate in the call's layout", c);
   }
   vsa::ProfArgs a;
   memset(&a, 0, sizeof a);

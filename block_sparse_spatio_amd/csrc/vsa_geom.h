@@ -4,15 +4,18 @@
 //  1. Tile classification (full / boundary / empty) without an element loop.  A
 //     contiguous range of executed positions is a union of at most 2n-1 "boxes",
 //     products of coordinate intervals (n = 3 digits (t,y,x) in frame-major order,
-//     6 digits (tile t,h,w, in-tile t,h,w) in tile-major order).  Every mask kind is
+//     6 digits (tile t,h,w, in-tile t,h,w) in tile-major order; in position-major
+//     order the frame-0 block (digits y,x) and the rest (digits y,x,t-1) each give
+//     at most 5).  Every mask kind is
 //     a product of per-axis predicates of a coordinate difference (or of tile
 //     coordinates, for sliding tiles), OR-ed with the key-only sink predicate.  Over
 //     a pair of boxes each difference takes every value of an interval, independently
 //     per axis, so "all pairs kept" and "some pair kept" reduce to interval tests:
 //     a band |d| <= r, or a counting function for the periodic stripe predicate.
 //  2. The element mask of a boundary tile for one query row: the key range is cut
-//     into runs of constant (t, y) and contiguous x; in each run the kept keys of a
-//     box, stripe or sliding-tile mask form a few contiguous bit ranges.
+//     into runs of constant (t, y) and contiguous x (or, past the frame-0 block of
+//     position-major order, constant (y, x) and contiguous t); in each run the kept
+//     keys of a box, stripe or sliding-tile mask form a few contiguous bit ranges.
 //
 // Mask definitions: Sparse VideoGen on TPU ("how to accelerate attention": spatial
 // and temporal heads, frame-F00 sink); PSA notes, key design 1 (six-tuple stripes);
@@ -44,6 +47,18 @@ VSA_HD void pos_coords(const Geom& g, int p, int& t, int& y, int& x) {
     int r = p - t * g.HW;
     y = r / g.Wg;
     x = r - y * g.Wg;
+  } else if (g.layout == VSA_LAYOUT_POSITION_MAJOR) {
+    int s;
+    if (p < g.HW) {
+      t = 0;
+      s = p;
+    } else {
+      const int T1 = g.T - 1, q = p - g.HW;
+      s = q / T1;
+      t = 1 + (q - s * T1);
+    }
+    y = s / g.Wg;
+    x = s - y * g.Wg;
   } else {
     int vol = g.bt * g.bh * g.bw;
     int tau = p / vol, io = p - tau * vol;
@@ -100,8 +115,55 @@ VSA_HD Box level_box(const Geom& g, int n, const int* radix, const int* W, int c
   return b;
 }
 
-// Split positions [lo, end) into at most 2n-1 boxes (mixed-radix range decomposition).
-VSA_HD int decompose(const Geom& g, int lo, int end, Box* out) {
+// Position-major: [lo, end) inside the part after the frame-0 block, as boxes of the
+// digits (y, x, t-1) with radices (Hg, Wg, T-1), at most 5.
+VSA_HD Box pm_box(const Geom& g, const int* W, int cur, int j, int cnt) {
+  const int radix[3] = {g.Hg, g.Wg, g.T - 1};
+  int lo[3], hi[3];
+  for (int k = 0; k < 3; ++k) {
+    int d = (cur / W[k + 1]) % radix[k];
+    if (k < j) { lo[k] = d; hi[k] = d; }
+    else if (k == j) { lo[k] = d; hi[k] = d + cnt - 1; }
+    else { lo[k] = 0; hi[k] = radix[k] - 1; }
+  }
+  Box b;
+  b.y0 = lo[0]; b.y1 = hi[0]; b.x0 = lo[1]; b.x1 = hi[1];
+  b.t0 = lo[2] + 1; b.t1 = hi[2] + 1;
+  return b;
+}
+
+VSA_HD int decompose_pm_rest(const Geom& g, int lo, int end, Box* out) {
+  const int radix[3] = {g.Hg, g.Wg, g.T - 1};
+  int W[4];
+  W[3] = 1;
+  for (int k = 2; k >= 0; --k) W[k] = W[k + 1] * radix[k];
+  int nb = 0, cur = lo;
+  if (cur >= end) return 0;
+  int j = 2;
+  for (; j >= 0; --j) {
+    int blk = W[j];
+    int next = ((cur + blk - 1) / blk) * blk;
+    if (next > end) break;
+    if (next > cur) {
+      out[nb++] = pm_box(g, W, cur, j, (next - cur) / W[j + 1]);
+      cur = next;
+    }
+    if (cur == end) return nb;
+  }
+  if (j < 0) j = 0;
+  for (; j < 3 && cur < end; ++j) {
+    int cnt = (end - cur) / W[j + 1];
+    if (cnt > 0) {
+      out[nb++] = pm_box(g, W, cur, j, cnt);
+      cur += cnt * W[j + 1];
+    }
+  }
+  return nb;
+}
+
+// Split positions [lo, end) of a frame- or tile-major order into at most 2n-1 boxes
+// (mixed-radix range decomposition).
+VSA_HD int decompose_mixed(const Geom& g, int lo, int end, Box* out) {
   int radix[6];
   int n = order_digits(g, radix);
   int W[7];
@@ -130,6 +192,20 @@ VSA_HD int decompose(const Geom& g, int lo, int end, Box* out) {
       cur += cnt * W[j + 1];
     }
   }
+  return nb;
+}
+
+// Split executed positions [lo, end) into boxes: at most 2n-1 for frame- and
+// tile-major orders, at most 10 for position-major (frame-0 block, then the rest).
+VSA_HD int decompose(const Geom& g, int lo, int end, Box* out) {
+  if (g.layout != VSA_LAYOUT_POSITION_MAJOR) return decompose_mixed(g, lo, end, out);
+  int nb = 0;
+  if (lo < g.HW) {
+    Geom f = g;
+    f.layout = VSA_LAYOUT_FRAME_MAJOR;  // positions below HW are frame 0 in frame-major order
+    nb = decompose_mixed(f, lo, imin(end, g.HW), out);
+  }
+  if (end > g.HW) nb += decompose_pm_rest(g, imax(lo, g.HW) - g.HW, end - g.HW, out + nb);
   return nb;
 }
 
@@ -285,6 +361,27 @@ VSA_HD uint64_t bit_range(int lo, int hi) {  // bits lo..hi inclusive, 0 <= lo <
   return ones << lo;
 }
 
+// Bits off + (u - ua) for the u in [ua, ub] with (|u| mod P) < w (the stripe predicate
+// along one run of keys).
+VSA_HD uint64_t periodic_bits(int ua, int ub, int P, int w, int off) {
+  uint64_t bits = 0;
+  if (ub >= 0) {
+    int lo = imax(ua, 0);
+    for (int j = lo / P; j <= ub / P; ++j) {
+      int a = imax(lo, j * P), b = imin(ub, j * P + w - 1);
+      if (a <= b) bits |= bit_range(off + a - ua, off + b - ua);
+    }
+  }
+  if (ua < 0) {
+    int lo = imax(-ub, 1), hi = -ua;  // |u| in [lo, hi]
+    for (int j = lo / P; j <= hi / P; ++j) {
+      int a = imax(lo, j * P), b = imin(hi, j * P + w - 1);
+      if (a <= b) bits |= bit_range(off - b - ua, off - a - ua);
+    }
+  }
+  return bits;
+}
+
 // kept keys of a run (fixed t, y; x in [x0, x1]; bit of x0 is off) for query q
 VSA_HD uint64_t run_mask(const Geom& g, const DevMask& m, const QueryPos& q, int t, int y, int x0,
                          int x1, int off) {
@@ -300,24 +397,8 @@ VSA_HD uint64_t run_mask(const Geom& g, const DevMask& m, const QueryPos& q, int
     case VSA_MASK_STRIPE: {
       if ((iabs(t - q.t - m.To) % m.Ts) >= m.Tw) return 0;
       // u = s_k - s_q - So over the run; kept where (|u| mod Ss) < Sw
-      int ubase = y * g.Wg - q.s - m.So;  // u = x + ubase
-      int ua = x0 + ubase, ub = x1 + ubase;
-      uint64_t bits = 0;
-      if (ub >= 0) {
-        int lo = imax(ua, 0);
-        for (int j = lo / m.Ss; j <= ub / m.Ss; ++j) {
-          int a = imax(lo, j * m.Ss), b = imin(ub, j * m.Ss + m.Sw - 1);
-          if (a <= b) bits |= bit_range(off + a - ubase - x0, off + b - ubase - x0);
-        }
-      }
-      if (ua < 0) {
-        int lo = imax(-ub, 1), hi = -ua;  // |u| in [lo, hi]
-        for (int j = lo / m.Ss; j <= hi / m.Ss; ++j) {
-          int a = imax(lo, j * m.Ss), b = imin(hi, j * m.Ss + m.Sw - 1);
-          if (a <= b) bits |= bit_range(off - b - ubase - x0, off - a - ubase - x0);
-        }
-      }
-      return bits;
+      const int ubase = y * g.Wg - q.s - m.So;  // u = x + ubase
+      return periodic_bits(x0 + ubase, x1 + ubase, m.Ss, m.Sw, off);
     }
     case VSA_MASK_STA: {
       int at = t / g.bt, ay = y / g.bh;
@@ -328,6 +409,45 @@ VSA_HD uint64_t run_mask(const Geom& g, const DevMask& m, const QueryPos& q, int
     }
     default:
       return 0;
+  }
+}
+
+// kept keys of a frame run of position-major order (fixed y, x; t in [t0, t1]; bit of
+// t0 is off) for query q
+VSA_HD uint64_t run_mask_t(const Geom& g, const DevMask& m, const QueryPos& q, int t0, int t1, int y,
+                           int x, int off) {
+  uint64_t bits = 0;
+  if (t0 < m.sink) {  // sink frames are kept for every query
+    const int hi = imin(t1, m.sink - 1);
+    bits = bit_range(off, off + hi - t0);
+    if (hi == t1) return bits;
+    off += hi + 1 - t0;
+    t0 = hi + 1;
+  }
+  switch (m.kind) {
+    case VSA_MASK_ALL:
+      return bits | bit_range(off, off + t1 - t0);
+    case VSA_MASK_BOX: {
+      if (m.rh >= 0 && iabs(y - q.y) > m.rh) return bits;
+      if (m.rw >= 0 && iabs(x - q.x) > m.rw) return bits;
+      int lo = t0, hi = t1;
+      if (m.rt >= 0) { lo = imax(lo, q.t - m.rt); hi = imin(hi, q.t + m.rt); }
+      return lo <= hi ? bits | bit_range(off + lo - t0, off + hi - t0) : bits;
+    }
+    case VSA_MASK_STRIPE: {
+      if ((iabs(y * g.Wg + x - q.s - m.So) % m.Ss) >= m.Sw) return bits;
+      // v = t_k - t_q - To over the run; kept where (|v| mod Ts) < Tw
+      const int vbase = -q.t - m.To;
+      return bits | periodic_bits(t0 + vbase, t1 + vbase, m.Ts, m.Tw, off);
+    }
+    case VSA_MASK_STA: {
+      const int ay = y / g.bh, ax = x / g.bw;
+      if (ay < q.sh || ay >= q.sh + m.wh || ax < q.sw || ax >= q.sw + m.ww) return bits;
+      const int lo = imax(t0, q.st * g.bt), hi = imin(t1, (q.st + m.wt) * g.bt - 1);
+      return lo <= hi ? bits | bit_range(off + lo - t0, off + hi - t0) : bits;
+    }
+    default:
+      return bits;
   }
 }
 
@@ -342,7 +462,7 @@ struct RunCursor {
 VSA_HD RunCursor run_begin(const Geom& g, int p) {
   RunCursor c;
   c.p = p;
-  if (g.layout == VSA_LAYOUT_FRAME_MAJOR) {
+  if (g.layout != VSA_LAYOUT_TILE_MAJOR) {
     pos_coords(g, p, c.t, c.y, c.x);
     c.tt = c.th = c.tw = c.it = c.ih = c.iw = 0;
   } else {
@@ -364,13 +484,12 @@ VSA_HD RunCursor run_begin(const Geom& g, int p) {
   return c;
 }
 
-// length of the run starting at the cursor, capped by end
-VSA_HD int run_len(const Geom& g, const RunCursor& c, int end) {
-  int room = (g.layout == VSA_LAYOUT_FRAME_MAJOR) ? g.Wg - c.x : g.bw - c.iw;
-  return imin(room, end - c.p);
+// Frame- and tile-major orders: every run is along x.
+VSA_HD int run_len_ft(const Geom& g, const RunCursor& c, int end) {
+  return imin(g.layout == VSA_LAYOUT_TILE_MAJOR ? g.bw - c.iw : g.Wg - c.x, end - c.p);
 }
 
-VSA_HD void run_advance(const Geom& g, RunCursor& c, int len) {
+VSA_HD void run_advance_ft(const Geom& g, RunCursor& c, int len) {
   c.p += len;
   if (g.layout == VSA_LAYOUT_FRAME_MAJOR) {
     c.x += len;
@@ -399,24 +518,70 @@ VSA_HD void run_advance(const Geom& g, RunCursor& c, int len) {
   }
 }
 
-// Keep bits of keys [c0, min(c0 + nbits, S)) for query q (nbits <= 64).
+// Position-major order: runs along x inside the frame-0 block, then along t (frames
+// 1 .. T-1 of one spatial position).
+VSA_HD bool run_along_t(const Geom& g, const RunCursor& c) { return c.p >= g.HW; }
+
+VSA_HD int run_len_pm(const Geom& g, const RunCursor& c, int end) {
+  return imin(run_along_t(g, c) ? g.T - c.t : g.Wg - c.x, end - c.p);
+}
+
+VSA_HD void run_advance_pm(const Geom& g, RunCursor& c, int len) {
+  if (run_along_t(g, c)) {
+    c.t += len;
+    if (c.t >= g.T) {
+      c.t = 1;
+      if (++c.x >= g.Wg) { c.x = 0; ++c.y; }
+    }
+  } else {
+    c.x += len;
+    if (c.x >= g.Wg) {
+      c.x = 0;
+      if (++c.y >= g.Hg) { c.y = 0; c.t = 1; }  // frame-0 block done: position 0, frame 1
+    }
+  }
+  c.p += len;
+}
+
 // keys [c0, c0 + nbits) that lie before S (the only element mask of a tile-aligned list)
 VSA_HD uint64_t real_key_mask(const Geom& g, int c0, int nbits) {
   const int n = imin(c0 + nbits, g.S) - c0;
   return n <= 0 ? 0ull : bit_range(0, n - 1);
 }
 
-VSA_HD uint64_t tile_row_mask(const Geom& g, const DevMask& m, const QueryPos& q, int c0,
-                              int nbits) {
-  int end = imin(c0 + nbits, g.S);
+// Keep bits of keys [c0, min(c0 + nbits, S)) for query q (nbits <= 64): one loop for
+// the frame- and tile-major orders, one for position-major, chosen once per call so that
+// neither carries the other's per-run tests.
+VSA_HD uint64_t tile_row_mask_ft(const Geom& g, const DevMask& m, const QueryPos& q, int c0, int nbits) {
+  const int end = imin(c0 + nbits, g.S);
   uint64_t bits = 0;
   RunCursor c = run_begin(g, c0);
   while (c.p < end) {
-    int len = run_len(g, c, end);
+    const int len = run_len_ft(g, c, end);
     bits |= run_mask(g, m, q, c.t, c.y, c.x, c.x + len - 1, c.p - c0);
-    run_advance(g, c, len);
+    run_advance_ft(g, c, len);
   }
   return bits;
+}
+
+VSA_HD uint64_t tile_row_mask_pm(const Geom& g, const DevMask& m, const QueryPos& q, int c0, int nbits) {
+  const int end = imin(c0 + nbits, g.S);
+  uint64_t bits = 0;
+  RunCursor c = run_begin(g, c0);
+  while (c.p < end) {
+    const int len = run_len_pm(g, c, end);
+    if (run_along_t(g, c))
+      bits |= run_mask_t(g, m, q, c.t, c.t + len - 1, c.y, c.x, c.p - c0);
+    else
+      bits |= run_mask(g, m, q, c.t, c.y, c.x, c.x + len - 1, c.p - c0);
+    run_advance_pm(g, c, len);
+  }
+  return bits;
+}
+
+VSA_HD uint64_t tile_row_mask(const Geom& g, const DevMask& m, const QueryPos& q, int c0, int nbits) {
+  return g.layout == VSA_LAYOUT_POSITION_MAJOR ? tile_row_mask_pm(g, m, q, c0, nbits)
+                                               : tile_row_mask_ft(g, m, q, c0, nbits);
 }
 
 }  // namespace vsa

@@ -18,7 +18,8 @@ struct DevMask {
   int16_t rt, rh, rw;
   int16_t Tw, To, Ts, Sw, So, Ss;
   int16_t wt, wh, ww;
-  int16_t pad0, pad1;
+  int16_t layout;  // executed token order of the heads using this descriptor (VSA_LAYOUT_*)
+  int16_t pad1;
 };
 static_assert(sizeof(DevMask) == 32, "DevMask layout");
 
@@ -28,8 +29,15 @@ struct Geom {
   int32_t bt, bh, bw;    // 3D tile (tile-major layout and STA masks), else 1
   int32_t nT, nH, nW;    // tile grid
   int32_t S, HW;
-  int32_t layout;        // VSA_LAYOUT_*
+  int32_t layout;        // VSA_LAYOUT_* (kernels take it per head from DevMask::layout)
 };
+
+// The geometry of one head: the grid with that head's executed order.
+__host__ __device__ inline Geom head_geom(const Geom& g, const DevMask& m) {
+  Geom r = g;
+  r.layout = m.layout;
+  return r;
+}
 
 struct MaskTable {
   DevMask m[VSA_MAX_UNIQUE_MASKS];
@@ -37,6 +45,11 @@ struct MaskTable {
 
 struct HeadMap {
   uint8_t slot[VSA_MAX_HEADS];
+};
+
+// Executed token order (VSA_LAYOUT_*) of every head, for the token reorder.
+struct HeadLayouts {
+  uint8_t lay[VSA_MAX_HEADS];
 };
 
 // ---- launch wrappers (defined next to their kernels) ----
@@ -74,8 +87,8 @@ hipError_t launch_attn_f32(const FwdArgs& a, const MaskTable& masks, const HeadM
 hipError_t launch_transpose_v(const void* v, void* vt, int32_t B, int32_t S, int32_t H, int32_t D,
                               int32_t s_pad, hipStream_t stream);
 hipError_t launch_reorder(const void* src, void* dst, int32_t elem_bytes, int32_t B,
-                          int32_t H, int32_t D, const Geom& g, int32_t inverse,
-                          hipStream_t stream);
+                          int32_t H, int32_t D, const Geom& g, const HeadLayouts& hl,
+                          int32_t inverse, hipStream_t stream);
 
 struct ProfArgs {
   const void* q;

@@ -57,7 +57,22 @@ typedef enum { VSA_BF16 = 0, VSA_F32 = 1 } vsa_dtype;
  *     tiles are ordered row-major over the tile grid and the tokens row-major inside
  *     a tile, so every tile is contiguous (Sliding Tile Attention explainer, method
  *     section 3; PSA notes, key design 2).  T, Hg, Wg must be multiples of the tile. */
-typedef enum { VSA_LAYOUT_FRAME_MAJOR = 0, VSA_LAYOUT_TILE_MAJOR = 1 } vsa_layout;
+/* Executed token order of a head.
+ *   FRAME_MAJOR:    (t, y, x) row-major, the natural order.
+ *   TILE_MAJOR:     3D tiles of tile_t x tile_h x tile_w tokens contiguous, tiles and
+ *                   in-tile tokens row-major (Sliding Tile Attention explainer, method
+ *                   section 3).
+ *   POSITION_MAJOR: frame 0 first in frame-major order, then for every spatial
+ *                   position s = y*Wg + x (ascending) its frames 1 .. T-1: position
+ *                   Hg*Wg + s*(T-1) + (t-1).  The temporal order of Sparse VideoGen on
+ *                   TPU ("arranging tokens for temporal access": (F,H,W) -> (H,W,F)),
+ *                   with the first frame kept as a leading block so that the
+ *                   first-frame sink stays contiguous. */
+typedef enum {
+  VSA_LAYOUT_FRAME_MAJOR = 0,
+  VSA_LAYOUT_TILE_MAJOR = 1,
+  VSA_LAYOUT_POSITION_MAJOR = 2
+} vsa_layout;
 
 /* Latent grid.  S = T*Hg*Wg.  tile_* is the 3D token tile used by TILE_MAJOR and by
  * STA masks (0 when unused). */
@@ -85,14 +100,23 @@ typedef enum {
  *           start <= b < start + w on all three axes; the window is shifted inward
  *           at the edges and keeps its size (Sliding Tile Attention explainer,
  *           method section 3).  Requires grid tile_* > 0 dividing T, Hg, Wg.
+ * head_layout: executed token order of this head; VSA_HEAD_LAYOUT_CALL (0) takes the
+ *           call's layout argument, VSA_HEAD_LAYOUT_(FRAME|TILE|POSITION) set it for
+ *           this head alone (Sparse VideoGen on TPU, "dynamic routing with fixed tensor
+ *           shapes": per-head flags choose the original or the permuted order).
  * Unused fields must be zero.  Descriptors that compare equal field by field share
  * one classification. */
+#define VSA_HEAD_LAYOUT_CALL 0
+#define VSA_HEAD_LAYOUT_FRAME 1
+#define VSA_HEAD_LAYOUT_TILE 2
+#define VSA_HEAD_LAYOUT_POSITION 3
 typedef struct {
   int32_t kind;
   int32_t sink_frames;
   int32_t rt, rh, rw;
   int32_t Tw, To, Ts, Sw, So, Ss;
   int32_t win_t, win_h, win_w;
+  int32_t head_layout;
 } vsa_mask_desc;
 
 /* Tile classes stored in vsa_tile_lists.cls. */
@@ -139,7 +163,8 @@ vsa_status vsa_tile_counts(const vsa_grid* grid, int32_t Bq, int32_t Bk, int32_t
  * sparsity"; video-DiT attention blog, section 7.3: a per-Q-block table of the K
  * blocks it computes).  The result is exact: it equals counting kept pairs of the
  * materialised mask in each tile.
- *   grid, layout:  token grid and sequence order of the positions
+ *   grid, layout:  token grid and sequence order of the positions (a descriptor's
+ *                  head_layout overrides the order for the heads that use it)
  *   masks:         host [H] descriptors (deduplicated internally)
  *   Bq, Bk:        query / key tile sizes in positions, 1..4096
  *   out:           device arrays sized for U unique masks (see vsa_tile_lists)
@@ -166,21 +191,25 @@ vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout,
 /* Attention forward ----------------------------------------------------------- */
 
 #define VSA_FWD_FORCE_MASK 1  /* ablation: run every listed tile through the masked path */
-#define VSA_FWD_REORDER_IO 2  /* TILE_MAJOR only: q/k/v/o are frame-major; reorder into the
-                                 workspace, attend in tile-major order, reorder O back */
+#define VSA_FWD_REORDER_IO 2  /* q/k/v/o are frame-major; each head's tokens are reordered
+                                 into its executed layout (the call's, or its descriptor's
+                                 head_layout) in the workspace, attention runs there and
+                                 O is reordered back (Sparse VideoGen on TPU, "layout
+                                 transforms on local heads"); needs a head not frame-major */
 #define VSA_FWD_WRITE_LSE 4   /* write lse (must then be non-NULL) */
 #define VSA_FWD_TILE_ALIGNED 8  /* listed BOUNDARY tiles mask only keys past S: the
                                    forward of lists from VSA_CLASSIFY_ROUND_TILES */
 
 /* Workspace bytes vsa_sparse_attn_fwd needs for these arguments: for bf16,
  * B*H*D*S64 elements (S64 = S rounded up to a multiple of 64) that hold V
- * transposed per 64-key block to [B][H][S64/64][D][64]; with VSA_FWD_REORDER_IO, 3*B*S*H*D elements of
- * dtype more.  f32 without VSA_FWD_REORDER_IO needs none. */
+ * transposed per 64-key block to [B][H][S64/64][D][64]; with VSA_FWD_REORDER_IO,
+ * 3*B*S*H*D elements of dtype more (q, k, v in each head's executed order).  f32 without VSA_FWD_REORDER_IO needs none. */
 vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D,
                                    vsa_dtype dtype, int32_t flags, size_t* bytes);
 
 /* Block-sparse masked attention forward.
- *   q, k, v:  device [B][S][H][D], dtype, contiguous
+ *   q, k, v:  device [B][S][H][D], dtype, contiguous; position p of head h is that
+ *             head's executed position (its layout) unless VSA_FWD_REORDER_IO
  *   o:        device [B][S][H][D], dtype (output; must not alias q/k/v)
  *   lse:      device float [B][H][S] = m + ln(l), natural log (written only with
  *             VSA_FWD_WRITE_LSE; -inf for a row with no kept key)
@@ -204,12 +233,22 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
                                float scale, int32_t flags, void* workspace,
                                size_t ws_bytes, void* stream);
 
-/* Tile-major reorder ---------------------------------------------------------- */
+/* Token reorder ---------------------------------------------------------------- */
 
-/* Permute the sequence axis of src [B][S][H][D] into dst (no aliasing):
- * inverse = 0: frame-major -> tile-major; inverse != 0: tile-major -> frame-major.
- * grid tile_* must divide T, Hg, Wg (Sliding Tile Attention explainer, method
- * section 3: tokens of a tile are contiguous). */
+/* Permute the sequence axis of src [B][S][H][D] into dst (no aliasing), each head h
+ * into its own order layouts[h] (VSA_LAYOUT_*, host array [H]):
+ * inverse = 0: frame-major -> layouts[h]; inverse != 0: layouts[h] -> frame-major.
+ * Tile-major heads need grid tile_* dividing T, Hg, Wg (Sliding Tile Attention
+ * explainer, method section 3: tokens of a tile are contiguous); position-major heads
+ * gather each spatial position's frames (Sparse VideoGen on TPU, "arranging tokens for
+ * temporal access").  H*D*element size must be a multiple of 16 bytes, and D*element
+ * size too when the layouts differ.  Asynchronous on stream; the caller owns both
+ * buffers. */
+vsa_status vsa_reorder_heads(const void* src, void* dst, vsa_dtype dtype, int32_t B,
+                             int32_t H, int32_t D, const vsa_grid* grid,
+                             const int32_t* layouts, int32_t inverse, void* stream);
+
+/* vsa_reorder_heads with every head tile-major. */
 vsa_status vsa_reorder_tokens(const void* src, void* dst, vsa_dtype dtype, int32_t B,
                               int32_t H, int32_t D, const vsa_grid* grid,
                               int32_t inverse, void* stream);
@@ -250,7 +289,10 @@ vsa_status vsa_profile_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t 
  *   q, k, v:     device [B][S][H][D], dtype
  *   sample_idx:  device int32 [H][n_samples], positions in [0, S), shared across b
  *   cands:       host [n_cand] descriptors, cands[0] is the reference (normally ALL);
- *                2 <= n_cand <= 4
+ *                2 <= n_cand <= 4; all are scored in the call's layout, so a
+ *                head_layout naming another order is UNSUPPORTED (the routed
+ *                result is the same in any order, since attention commutes with a
+ *                permutation of the tokens applied to q, k, v and o alike)
  *   err:         device float [H][n_cand]: sqrt(sum over b, samples, channels of
  *                (o_c - o_0)^2); err[h][0] = 0
  *   route:       device int32 [H]: argmin over c >= 1 of err[h][c], lowest c on ties

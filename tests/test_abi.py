@@ -36,7 +36,7 @@ def test_header_compiles_as_c(tmp_path):
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(_lib.vsa_grid) == 24
-    assert ctypes.sizeof(_lib.vsa_mask_desc) == 56
+    assert ctypes.sizeof(_lib.vsa_mask_desc) == 60
     assert ctypes.sizeof(_lib.vsa_tile_lists) == 40
 
 
@@ -100,7 +100,11 @@ def _call_fwd(**over):
     (dict(o=0x1000), -1, "alias"),
     (dict(flags=64), -1, "flag"),
     (dict(flags=4), -1, "lse"),
-    (dict(flags=2), -1, "tile-major"),
+    (dict(flags=2), -1, "not frame-major"),
+    (dict(flags=2, masks=[W.mask_spatial(1), dict(W.mask_temporal(1), head_layout="position")], ws_bytes=1000),
+     -3, "workspace"),
+    (dict(masks=[dict(W.mask_all(), head_layout=7), W.mask_all()]), -1, "head_layout"),
+    (dict(masks=[dict(W.mask_all(), head_layout="tile"), W.mask_all()]), -1, "tile"),
     (dict(flags=2, layout=1, grid=W.grid(4, 8, 8, (2, 4, 4)), ws_bytes=1000), -3, "workspace"),
     (dict(ws=None, ws_bytes=0), -3, "workspace"),
     (dict(ws=0xA008), -1, "aligned"),
@@ -151,6 +155,10 @@ def test_profile_validation():
     st = lib.vsa_profile_heads(0x1, 0x2, 0x3, vsa.VSA_BF16, 1, 256, 2, 64, ctypes.byref(g), 0, 0x4, 300,
                                cands, 3, err, 0x5, 0.0, 0x6, 1 << 30, None)
     assert st == -1
+    moved = _lib.make_masks([W.mask_all(), W.mask_spatial(1), dict(W.mask_temporal(1), head_layout="position")])
+    st = lib.vsa_profile_heads(0x1, 0x2, 0x3, vsa.VSA_BF16, 1, 256, 2, 64, ctypes.byref(g), 0, 0x4, 8,
+                               moved, 3, err, 0x5, 0.0, 0x6, 1 << 30, None)
+    assert st == -2 and "call's layout" in vsa.vsa_last_error()
 
 
 def test_reorder_validation():
@@ -161,6 +169,17 @@ def test_reorder_validation():
     g = _lib.make_grid(W.grid(4, 8, 8, (2, 4, 4)))
     st = lib.vsa_reorder_tokens(0x1, 0x1, vsa.VSA_BF16, 1, 2, 64, ctypes.byref(g), 0, None)
     assert st == -1 and "alias" in vsa.vsa_last_error()
+    I4 = ctypes.c_int32 * 4
+    g = _lib.make_grid(W.grid(4, 8, 8))
+    st = lib.vsa_reorder_heads(0x1, 0x2, vsa.VSA_BF16, 1, 4, 64, ctypes.byref(g), I4(0, 2, 5, 0), 0, None)
+    assert st == -1 and "unknown layout" in vsa.vsa_last_error()
+    st = lib.vsa_reorder_heads(0x1, 0x2, vsa.VSA_BF16, 1, 4, 64, ctypes.byref(g), I4(0, 2, 1, 0), 0, None)
+    assert st == -1 and "tile" in vsa.vsa_last_error()
+    # 4 heads of 4 bf16 channels: a 16-byte chunk holds two heads, fine only when they move alike
+    st = lib.vsa_reorder_heads(0x1, 0x2, vsa.VSA_BF16, 1, 4, 4, ctypes.byref(g), I4(0, 2, 2, 0), 0, None)
+    assert st == -2 and "D*element" in vsa.vsa_last_error()
+    st = lib.vsa_reorder_heads(0x1, 0x2, vsa.VSA_BF16, 1, 4, 64, ctypes.byref(g), None, 0, None)
+    assert st == -1 and "layouts" in vsa.vsa_last_error()
 
 
 def _call_merge(n=2, o_ok=True, lse_ok=True, D=128, dtype=0, S=10, out=0x9000, misalign=False):

@@ -201,3 +201,66 @@ def test_full_config_sampled_rows(gpu_lib, name, Bq, which):
     got = o[:, rows][:, :, heads]
     assert_close(got, ref_o, "bf16", f"{name} sampled rows")
     assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3
+
+
+def _head_layout_case(dtype):
+    """Grid, masks and inputs with heads in frame-, position- and tile-major order."""
+    g = W.grid(6, 16, 16, (2, 8, 8))
+    masks = [W.mask_spatial(1),
+             W.with_head_layout(W.mask_temporal(2), "position"),
+             W.with_head_layout(W.mask_sta(2, 1, 1, sink_frames=1), "tile"),
+             W.with_head_layout(W.mask_stripe(1, 0, 2, 3, 0, 16), "position"),
+             W.mask_temporal(1)]
+    q, k, v = W.qkv(2, W.seq_len(g), len(masks), 64 if dtype == "f32" else 128, dtype, seed=21)
+    return g, masks, q, k, v
+
+
+@pytest.mark.parametrize("dtype,Bq,Bk", [("bf16", 64, 64), ("bf16", 128, 64), ("bf16", 256, 64),
+                                         ("f32", 64, 32)])
+def test_head_layouts_reorder_io(gpu_lib, dtype, Bq, Bk):
+    """Frame-major I/O with every head attended in its own order (the reorder inside the
+    call) equals frame-major attention with the same coordinate masks: o and lse."""
+    g, masks, q, k, v = _head_layout_case(dtype)
+    say(f"head layouts reorder io {dtype} Bq={Bq} Bk={Bk}")
+    o, lse, _ = run_attention(q, k, v, g, "frame", masks, Bq, Bk, reorder_io=True, flags=vsa.VSA_FWD_WRITE_LSE)
+    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks)
+    assert_close(o, ref_o, dtype, "per-head layouts, reorder inside")
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= (5e-3 if dtype == "bf16" else 1e-5)
+
+
+def test_head_layouts_in_place(gpu_lib):
+    """Without the reorder flag each head's q, k, v and o are in that head's order: inputs
+    gathered per head by the oracle's permutation give the permuted frame-major result."""
+    g, masks, q, k, v = _head_layout_case("bf16")
+    lays = W.head_layouts(masks, "frame")
+    perms = [torch.from_numpy(oracle.layout_permutation(g, lay)) for lay in lays]
+    qp, kp, vp = (torch.stack([x[:, perms[h], h] for h in range(len(lays))], dim=2) for x in (q, k, v))
+    say(f"head layouts in place {lays}")
+    o, lse, _ = run_attention(qp, kp, vp, g, "frame", masks, 128, 64, flags=vsa.VSA_FWD_WRITE_LSE)
+    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks)
+    o, lse = o.cpu(), lse.cpu().numpy()
+    for h, p in enumerate(perms):
+        assert_close(o[:, :, h], ref_o[:, p.numpy(), h], "bf16", f"head {h} ({lays[h]})")
+        assert np.abs(lse[:, h] - ref_lse[:, h][:, p.numpy()]).max() <= 5e-3
+
+
+def test_full_config_position_major_sampled_rows(gpu_lib):
+    """Wan 2.1 720p mixed heads, temporal heads position-major with the reorder inside
+    the call (the launch configuration the benchmark times): sampled frame-major rows
+    against the oracle."""
+    name = "wan_mixed"
+    cfg, (q, k, v) = _full_inputs(name)
+    g, masks, Bq = cfg["grid"], cfg["position_masks"], cfg["Bq"]
+    S = W.seq_len(g)
+    say(f"full config {name} position-major temporal heads Bq={Bq}")
+    d = dev()
+    tiles = vsa.vsa_classify_tiles(g, "frame", masks, Bq, cfg["Bk"], device=d, with_cls=False)
+    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "frame", masks, tiles,
+                                     flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    rows = sample_rows_per_tile(S, Bq, seed=4, per_tile=0, max_tiles=24)
+    heads = [0, 7, 19, 20, 27, 39]
+    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
+    assert_close(o[:, rows][:, :, heads], ref_o, "bf16", f"{name} position-major sampled rows")
+    assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3

@@ -151,3 +151,64 @@ def test_classify_rounded_full_configs(gpu_lib, name, Bq):
     nK = cr.shape[-1]
     if S % cfg["Bk"] == 0 and S % Bq:
         assert torch.all(cr[:, :-1] != 2)
+
+
+@pytest.mark.parametrize("seed", range(36))
+def test_classify_random_head_layouts(gpu_lib, seed):
+    """Heads in their own token orders (frame-, tile- or position-major): every head's
+    classes equal the oracle's in that head's order, exact and rounded."""
+    rng = np.random.default_rng(2000 + seed)
+    tiled = seed % 2 == 1
+    if tiled:
+        tile = tuple(int(x) for x in rng.integers(1, 4, 3))
+        g = W.grid(tile[0] * int(rng.integers(1, 4)), tile[1] * int(rng.integers(1, 4)),
+                   tile[2] * int(rng.integers(1, 5)), tile)
+    else:
+        g = W.grid(int(rng.integers(1, 9)), int(rng.integers(1, 9)), int(rng.integers(1, 12)))
+    orders = ["frame", "position"] + (["tile"] if tiled else [])
+    layout = orders[rng.integers(len(orders))]
+    H = int(rng.integers(1, 6))
+    masks = []
+    for _ in range(H):
+        m = _random_desc(rng, "tile" if tiled else "frame")
+        pick = int(rng.integers(len(orders) + 1))
+        masks.append(m if pick == len(orders) else W.with_head_layout(m, orders[pick]))
+    Bq = int(rng.choice([1, 3, 8, 16, 32, 64, 128]))
+    Bk = int(rng.choice([1, 5, 16, 32, 64]))
+    round_tiles = seed % 3 == 0
+    say(f"classify head layouts seed={seed} grid={g} layout={layout} Bq={Bq} Bk={Bk} round={round_tiles} "
+        f"masks={masks}")
+    tiles = gpu_lib.vsa_classify_tiles(g, layout, masks, Bq, Bk, device=dev(), round_tiles=round_tiles)
+    torch.cuda.synchronize()
+    hm, U = gpu_lib.vsa_unique_masks(masks)
+    for h, (desc, lay) in enumerate(zip(masks, W.head_layouts(masks, layout))):
+        ref = oracle.classify(g, lay, desc, Bq, Bk, round_tiles=round_tiles)
+        check_lists_against(tiles, hm[h], ref["q_tiles"], ref["cls"])
+
+
+def test_classify_position_major_full_config(gpu_lib):
+    """Wan 2.1 720p mixed heads with the temporal heads position-major: sampled query
+    tiles bit-exact, and far fewer executed tiles than the same heads frame-major."""
+    cfg = W.config("wan_mixed")
+    g, Bq, Bk = cfg["grid"], cfg["Bq"], cfg["Bk"]
+    masks = cfg["position_masks"]
+    say("classify position-major full config wan_mixed")
+    tiles = gpu_lib.vsa_classify_tiles(g, "frame", masks, Bq, Bk, device=dev())
+    frame = gpu_lib.vsa_classify_tiles(g, "frame", cfg["masks"], Bq, Bk, device=dev(), with_cls=False)
+    torch.cuda.synchronize()
+    hm, U = gpu_lib.vsa_unique_masks(masks)
+    assert U == 2
+    rng = np.random.default_rng(9)
+    for u, h in ((hm[0], 0), (hm[-1], len(masks) - 1)):
+        qts = _sampled_q_tiles(tiles["nQ"], rng, 6)
+        lay = W.head_layouts(masks, "frame")[h]
+        ref = oracle.classify(g, lay, masks[h], Bq, Bk, q_tiles=qts)
+        check_lists_against(tiles, u, qts, ref["cls"])
+    cls = tiles["cls"].cpu()
+    assert torch.equal((cls == 1).sum(-1).int(), tiles["n_full"].cpu())
+    assert torch.equal((cls == 2).sum(-1).int(), tiles["n_bnd"].cpu())
+    n_pos = int(tiles["n_full"][hm[-1]].sum() + tiles["n_bnd"][hm[-1]].sum())
+    hmf, _ = gpu_lib.vsa_unique_masks(cfg["masks"])
+    n_frame = int(frame["n_full"][hmf[-1]].sum() + frame["n_bnd"][hmf[-1]].sum())
+    say(f"temporal head executed tiles: position-major {n_pos}, frame-major {n_frame}")
+    assert n_pos < n_frame / 2

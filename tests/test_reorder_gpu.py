@@ -26,3 +26,24 @@ def test_reorder_matches_permutation(gpu_lib, g, dtype, H, D):
     perm = torch.from_numpy(oracle.tile_major_permutation(g))
     assert torch.equal(y.cpu(), x[:, perm])
     assert torch.equal(z.cpu(), x)
+
+
+@pytest.mark.parametrize("g,dtype,layouts,D", [
+    (W.grid(4, 8, 8, (2, 4, 4)), "bf16", ["frame", "position", "tile", "position"], 64),
+    (W.grid(5, 6, 7), "f32", ["position", "frame", "position"], 128),
+    (W.grid(1, 6, 7), "bf16", ["position", "frame"], 64),  # one frame: position-major is frame order
+    (W.grid(21, 45, 80), "bf16", ["frame"] * 4 + ["position"] * 4, 128),
+])
+def test_reorder_heads_matches_permutation(gpu_lib, g, dtype, layouts, D):
+    S, H = W.seq_len(g), len(layouts)
+    say(f"reorder heads grid={g} {dtype} layouts={layouts} D={D}")
+    x = W.qkv(1, S, H, D, dtype, seed=5)[0]
+    xd = x.to(dev())
+    y = gpu_lib.vsa_reorder_heads(xd, g, layouts)
+    z = gpu_lib.vsa_reorder_heads(y, g, layouts, inverse=True)
+    torch.cuda.synchronize()
+    y = y.cpu()
+    for h, lay in enumerate(layouts):
+        perm = torch.from_numpy(oracle.layout_permutation(g, lay))
+        assert torch.equal(y[:, :, h], x[:, perm, h]), (h, lay)
+    assert torch.equal(z.cpu(), x)

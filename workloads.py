@@ -67,6 +67,19 @@ def mask_sta(win_t, win_h, win_w, sink_frames=0):
     return _desc("sta", win_t=win_t, win_h=win_h, win_w=win_w, sink_frames=sink_frames)
 
 
+def with_head_layout(mask, layout):
+    """The same mask on a head that runs in its own token order: "frame", "tile" or
+    "position" (the library's head_layout; the mask itself is defined on coordinates)."""
+    if layout not in ("frame", "tile", "position"):
+        raise ValueError(f"unknown layout {layout!r}")
+    return dict(mask, head_layout=layout)
+
+
+def head_layouts(masks, layout):
+    """Executed order of every head: its own head_layout, else the call's layout."""
+    return [m.get("head_layout", layout) for m in masks]
+
+
 def grid(T, Hg, Wg, tile=(0, 0, 0)):
     return {"T": int(T), "Hg": int(Hg), "Wg": int(Wg),
             "tile_t": int(tile[0]), "tile_h": int(tile[1]), "tile_w": int(tile[2])}
@@ -101,7 +114,11 @@ def config(name):
         H = 40
         return dict(name="wan_mixed", seed=1001, B=1, grid=grid(21, 45, 80), layout="frame",
                     H=H, D=128, dtype="bf16", Bq=128, Bk=64,
-                    masks=[mask_spatial(rt=1)] * 20 + [mask_temporal(r=4)] * 20)
+                    masks=[mask_spatial(rt=1)] * 20 + [mask_temporal(r=4)] * 20,
+                    # temporal heads gathered position-major (each position's frames
+                    # contiguous), spatial heads in frame order
+                    position_masks=[mask_spatial(rt=1)] * 20
+                    + [with_head_layout(mask_temporal(r=4), "position")] * 20)
     if name == "wan_single":
         H = 10
         return dict(name="wan_single", seed=1002, B=1, grid=grid(21, 45, 80), layout="frame",
