@@ -187,7 +187,8 @@ def main():
                     help="executed order of the temporal heads of wan_mixed: position = each spatial "
                          "position's frames contiguous, reordered inside the call (frame-major I/O)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--no-dense", action="store_true", help="skip the all-keep dense run")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the comparison runs (all-keep dense; position-major temporal heads)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run the tile-major reorder (a plain row copy) over a MIB-sized tensor, "
                          "5 times: the known-size kernel that calibrates HBM byte counters")
@@ -330,6 +331,38 @@ def main():
         extra["reorder_ms_per_tensor"] = round(r_ms, 4)
         extra["reorder_gbs"] = round(2.0 * qd.numel() * qd.element_size() / (r_ms * 1e-3) / 1e9, 1)
         del y
+
+    if "position_masks" in cfg and args.temporal_layout == "frame" and not args.round_tiles and not args.no_dense:
+        # the same layer with its temporal heads attended position-major (reorder of
+        # q, k, v and o inside the call): classify + forward per step, and the forward alone
+        pm = cfg["position_masks"]
+        pm_tiles = vsa.alloc_tile_lists(g, pm, Bq, Bk, dev, with_cls=False)
+        pm_flags = flags | vsa.VSA_FWD_REORDER_IO
+        pm_ws = torch.empty(vsa.vsa_fwd_workspace_bytes(B, S, H, D, vsa.VSA_BF16, pm_flags), dtype=torch.uint8,
+                            device=dev)
+
+        def pm_step():
+            vsa.vsa_classify_tiles(g, layout, pm, Bq, Bk, out=pm_tiles, stream=stream)
+            vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, pm, pm_tiles, flags=pm_flags, o=o, workspace=pm_ws,
+                                    stream=stream)
+
+        for _ in range(2):
+            pm_step()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_pm = 5
+        p0.record(stream)
+        for _ in range(n_pm):
+            pm_step()
+        p1.record(stream)
+        torch.cuda.synchronize()
+        pm_ms = p0.elapsed_time(p1) / n_pm
+        hm_pm, _ = vsa.vsa_unique_masks(pm)
+        pm_exec = 4.0 * D * executed_pairs(pm_tiles, hm_pm, B, S)
+        extra["temporal_heads_position_major"] = {
+            "ms_per_step": round(pm_ms, 4), "speedup_vs_frame_major": round(ms_step / pm_ms, 3),
+            "executed_tflop": round(pm_exec / 1e12, 3),
+            "note": "heads 20-39 attended in position-major order, q/k/v/o reordered inside the call"}
+        del pm_tiles, pm_ws
 
     # merging two partial results of this shape (LSE merge): HBM GB/s of the
     # algorithmic traffic (2 parts read + 1 output written, with their LSE rows)

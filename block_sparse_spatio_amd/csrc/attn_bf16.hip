@@ -69,8 +69,17 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   const int b = bh / H;
 
   const int slot = hm.slot[h];
-  const DevMask m = masks.m[slot];
-  const Geom g = head_geom(a.g, m);
+  const DevMask m_head = masks.m[slot];
+  // The body is instantiated for the common (order, mask kind) pairs with both fixed at
+  // compile time, so that the per-tile mask arithmetic of a boundary tile carries no
+  // other case and stays in straight-line code, plus one generic instance.
+  auto run = [&](auto order_tag, auto kind_tag) __attribute__((always_inline)) {
+  constexpr int ORDER = decltype(order_tag)::value;  // token order fixed at compile time, or -1
+  constexpr int KIND = decltype(kind_tag)::value;    // mask kind fixed at compile time, or -1
+  DevMask m = m_head;
+  if constexpr (KIND >= 0) m.kind = KIND;
+  Geom g = head_geom(a.g, m);
+  if constexpr (ORDER >= 0) g.layout = ORDER;
   const size_t lrow = (size_t)slot * a.nQ + qt;
   // List lengths and entries are clamped to the list row, so malformed lists cannot
   // send a load outside the tensors.  The lists come in as read-only, non-aliased
@@ -436,6 +445,21 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
       a.lse[((size_t)b * H + h) * S + lpos] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
     }
   }
+  };
+  using Any = std::integral_constant<int, -1>;
+  using Box = std::integral_constant<int, VSA_MASK_BOX>;
+  using Stripe = std::integral_constant<int, VSA_MASK_STRIPE>;
+  using Frame = std::integral_constant<int, VSA_LAYOUT_FRAME_MAJOR>;
+  using Position = std::integral_constant<int, VSA_LAYOUT_POSITION_MAJOR>;
+  using AnyOrder = std::integral_constant<int, -1>;
+  if (m_head.layout == VSA_LAYOUT_FRAME_MAJOR && m_head.kind == VSA_MASK_BOX)
+    run(Frame{}, Box{});
+  else if (m_head.layout == VSA_LAYOUT_FRAME_MAJOR && m_head.kind == VSA_MASK_STRIPE)
+    run(Frame{}, Stripe{});
+  else if (m_head.layout == VSA_LAYOUT_POSITION_MAJOR && m_head.kind == VSA_MASK_BOX)
+    run(Position{}, Box{});
+  else
+    run(AnyOrder{}, Any{});
 }
 
 template <int D, int NW>
