@@ -6,19 +6,20 @@ CPU-baseline leg may import it.  It shares no code with the HIP library and
 imports nothing from it; the product path never calls into it.
 
 Contents
-  coords     token coordinates of an executed position (frame-, tile-, position-major)
+  coords     token coordinates of an executed position (frame-, tile-, position-major,
+             tile-major over a grid padded to whole tiles)
   masks      the boolean keep-predicate of each mask kind
   classify   per-(query-tile, key-tile) full / boundary / empty classes and lists
   attention  masked softmax attention written from its definition
   profile    the sampled-query head profiler and router
-  reorder    the tile-major token permutation and its inverse
+  reorder    the token permutations of the executed orders and their inverses
   merge      merging partial results over disjoint key sets by their log-sum-exp
 
 Every function is pinned by tests under ``tests/`` (marked ``not gpu``) against
 numbers the pages print, closed forms, special cases and brute force on tiny
 inputs.  No function here is "parity unpinned".
 """
-from .coords import token_coords, num_tiles  # noqa: F401
+from .coords import token_coords, num_tiles, seq_len, padded_dims, is_real  # noqa: F401
 from .masks import keep_matrix  # noqa: F401
 from .classify import classify, EMPTY, FULL, BOUNDARY  # noqa: F401
 from .classify import rounded_keep_rows  # noqa: F401

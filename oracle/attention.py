@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .coords import token_coords
+from .coords import is_real, token_coords
 from .classify import rounded_keep_rows
 from .masks import keep_matrix
 
@@ -53,6 +53,8 @@ def attention(q, k, v, grid, layout, masks, scale=None, rows=None, heads=None, b
     """Masked attention for tensors q, k, v of shape [B, S, H, D] (any float dtype).
 
     masks: list of H descriptor dicts, one per head.
+    layout: the order of the positions of q, k, v (for "padded", S is the padded length
+             and padding keys are never kept; padding rows are computed like the others).
     rows:  optional int array of executed query positions (default: all S).
     heads: optional list of heads (default: all).
     round_tiles: optional (Bq, Bk): attend under the tile-aligned (B3) rounding of each
@@ -64,6 +66,7 @@ def attention(q, k, v, grid, layout, masks, scale=None, rows=None, heads=None, b
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
     heads = list(range(H)) if heads is None else list(heads)
     ck = token_coords(grid, layout, np.arange(S))
+    real_k = is_real(grid, *ck)  # padding keys of the padded layout are never kept
     o = np.zeros((B, len(rows), len(heads), D), dtype=np.float64)
     lse = np.zeros((B, len(heads), len(rows)), dtype=np.float64)
     for hi, h in enumerate(heads):
@@ -73,7 +76,7 @@ def attention(q, k, v, grid, layout, masks, scale=None, rows=None, heads=None, b
         for r0 in range(0, len(rows), block):
             r = rows[r0:r0 + block]
             if round_tiles is None:
-                keep = keep_matrix(masks[h], grid, token_coords(grid, layout, r), ck)
+                keep = keep_matrix(masks[h], grid, token_coords(grid, layout, r), ck) & real_k[None, :]
             else:
                 keep = rounded_keep_rows(grid, layout, masks[h], round_tiles[0], round_tiles[1], r)
             for b in range(B):

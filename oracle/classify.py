@@ -12,7 +12,8 @@ method section 2 and its Table 1):
 When S is not a multiple of the tile size, positions past S are padding.  Padding
 must contribute exactly zero weight (Sparse VideoGen on TPU, "aligning the sparse
 mask with execution"), so padding counts as "not kept": a tile that reaches past S
-is never FULL.
+is never FULL.  The padding tokens of the padded layout (PSA notes, key design 2,
+3D padding) are treated the same way, wherever they fall in the sequence.
 
 The classification is computed from its definition: materialise the explicit
 boolean mask of one query tile against all keys, count kept pairs per key tile, and
@@ -36,33 +37,41 @@ from __future__ import annotations
 
 import numpy as np
 
-from .coords import num_tiles, token_coords
+from .coords import is_real, num_tiles, seq_len, token_coords
 from .masks import keep_matrix
 
 EMPTY, FULL, BOUNDARY = 0, 1, 2
 
 
+def _real(grid, layout, pos):
+    return is_real(grid, *token_coords(grid, layout, pos))
+
+
 def _qtile_keep(grid, layout, desc, S, Bq, qt):
+    """Keep rows of query tile qt against all keys; padding rows and keys are not kept."""
     rows = np.arange(qt * Bq, min(S, (qt + 1) * Bq))
     cols = np.arange(S)
-    return keep_matrix(desc, grid, token_coords(grid, layout, rows), token_coords(grid, layout, cols))
+    m = keep_matrix(desc, grid, token_coords(grid, layout, rows), token_coords(grid, layout, cols))
+    return m & _real(grid, layout, rows)[:, None] & _real(grid, layout, cols)[None, :]
 
 
-def _tile_counts(m, S, Bq, Bk):
-    """Kept pairs and real pairs (both positions < S) of every key tile of one query
-    tile whose exact keep rows are m [rows, S]."""
+def _tile_counts(grid, layout, m, S, Bq, Bk, qt):
+    """Kept pairs and real pairs (both positions real tokens) of every key tile of query
+    tile qt whose keep rows are m [rows, S]."""
     nK = num_tiles(S, Bk)
     padded = np.zeros((Bq, nK * Bk), dtype=bool)
     padded[: m.shape[0], : m.shape[1]] = m
     kept = padded.reshape(Bq, nK, Bk).sum(axis=(0, 2))
-    cols_real = np.minimum(Bk, S - np.arange(nK) * Bk)
-    return kept, m.shape[0] * cols_real
+    col_real = np.zeros(nK * Bk, dtype=np.int64)
+    col_real[:S] = _real(grid, layout, np.arange(S))
+    rows_real = int(_real(grid, layout, np.arange(qt * Bq, min(S, (qt + 1) * Bq))).sum())
+    return kept, rows_real * col_real.reshape(nK, Bk).sum(axis=1)
 
 
 def classify_qtile(grid, layout, desc, S, Bq, Bk, qt, round_tiles=False):
     """Class of every key tile for query tile ``qt``: uint8 array [nK]."""
     m = _qtile_keep(grid, layout, desc, S, Bq, qt)
-    kept, real = _tile_counts(m, S, Bq, Bk)
+    kept, real = _tile_counts(grid, layout, m, S, Bq, Bk, qt)
     cls = np.full(len(kept), BOUNDARY, dtype=np.uint8)
     cls[kept == 0] = EMPTY
     cls[kept == Bq * Bk] = FULL
@@ -77,18 +86,19 @@ def rounded_keep_rows(grid, layout, desc, Bq, Bk, rows):
     """Keep rows of the tile-aligned (B3) mask for executed query positions ``rows``:
     bool [len(rows), S], every (query tile, key tile) block all-kept or all-dropped on
     its real pairs."""
-    S = grid["T"] * grid["Hg"] * grid["Wg"]
+    S = seq_len(grid, layout)
     rows = np.asarray(rows, dtype=np.int64)
     out = np.zeros((len(rows), S), dtype=bool)
+    col_real = _real(grid, layout, np.arange(S))
     for qt in np.unique(rows // Bq):
         m = _qtile_keep(grid, layout, desc, S, Bq, int(qt))
-        kept, real = _tile_counts(m, S, Bq, Bk)
+        kept, real = _tile_counts(grid, layout, m, S, Bq, Bk, int(qt))
         keep_tile = 2 * kept >= real
         keep_tile[kept == 0] = False
-        cols = np.repeat(keep_tile, Bk)[:S]
+        cols = np.repeat(keep_tile, Bk)[:S] & col_real
         sel = np.flatnonzero(rows // Bq == qt)
         out[sel] = cols[None, :]
-    return out
+    return out & _real(grid, layout, rows)[:, None]
 
 
 def classify(grid, layout, desc, Bq, Bk, q_tiles=None, round_tiles=False):
@@ -100,7 +110,7 @@ def classify(grid, layout, desc, Bq, Bk, q_tiles=None, round_tiles=False):
       bnd      list of int32 arrays (ascending BOUNDARY key-tile indices per query tile)
       q_tiles  the query tiles classified (default: all).
     round_tiles: classes of the tile-aligned (B3) mask instead of the exact one."""
-    S = grid["T"] * grid["Hg"] * grid["Wg"]
+    S = seq_len(grid, layout)
     nQ = num_tiles(S, Bq)
     if q_tiles is None:
         q_tiles = np.arange(nQ)

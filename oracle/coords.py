@@ -22,6 +22,13 @@ tokens.  Two orders are used:
   contiguous: positions [0, Hg*Wg) are frame 0 row-major, and position
   Hg*Wg + s*(T-1) + (t-1) holds frame t >= 1 at spatial index s = y*Wg + x.  The
   leading sink block is this implementation's reading; the page permutes all frames.
+* padded (tile-major with 3D padding, PSA notes, key design 2): each axis is padded up
+  to the smallest multiple of the tile (T' = ceil(T / bt) * bt, likewise H' and W'),
+  and the padded grid is laid out tile-major as above.  Positions whose coordinates
+  fall outside the real grid are padding tokens: they are never kept as keys, and a
+  padding query's output is not part of the result.  The executed length is
+  T' * H' * W' (``seq_len``).  With tiles that divide the grid it is the tile-major
+  order.
 """
 from __future__ import annotations
 
@@ -37,10 +44,32 @@ def _check_tile(grid):
     return bt, bh, bw
 
 
+def padded_dims(grid):
+    """(T', H', W'): every axis rounded up to a multiple of the grid's tile."""
+    bt, bh, bw = grid["tile_t"], grid["tile_h"], grid["tile_w"]
+    if min(bt, bh, bw) <= 0:
+        raise ValueError("the padded layout needs a positive tile size")
+    return (-(-grid["T"] // bt) * bt, -(-grid["Hg"] // bh) * bh, -(-grid["Wg"] // bw) * bw)
+
+
+def seq_len(grid, layout):
+    """Executed sequence length: T*Hg*Wg, or T'*H'*W' for the padded layout."""
+    if layout == "padded":
+        Tp, Hp, Wp = padded_dims(grid)
+        return Tp * Hp * Wp
+    return grid["T"] * grid["Hg"] * grid["Wg"]
+
+
+def is_real(grid, t, y, x):
+    """True where (t, y, x) is a token of the grid (not padding)."""
+    return (np.asarray(t) < grid["T"]) & (np.asarray(y) < grid["Hg"]) & (np.asarray(x) < grid["Wg"])
+
+
 def token_coords(grid, layout, pos):
     """Return (t, y, x) int64 arrays for executed positions ``pos`` (any int array).
 
-    layout is "frame", "tile" or "position"."""
+    layout is "frame", "tile", "position" or "padded" (coordinates of padding
+    positions lie outside the grid)."""
     pos = np.asarray(pos, dtype=np.int64)
     T, Hg, Wg = grid["T"], grid["Hg"], grid["Wg"]
     if layout == "frame":
@@ -48,9 +77,12 @@ def token_coords(grid, layout, pos):
         y = (pos // Wg) % Hg
         x = pos % Wg
         return t, y, x
-    if layout == "tile":
-        bt, bh, bw = _check_tile(grid)
-        nH, nW = Hg // bh, Wg // bw
+    if layout in ("tile", "padded"):
+        if layout == "tile":
+            _check_tile(grid)
+        bt, bh, bw = grid["tile_t"], grid["tile_h"], grid["tile_w"]
+        Tp, Hp, Wp = padded_dims(grid)
+        nH, nW = Hp // bh, Wp // bw
         vol = bt * bh * bw
         tau, iota = pos // vol, pos % vol
         tau_t, tau_h, tau_w = tau // (nH * nW), (tau // nW) % nH, tau % nW

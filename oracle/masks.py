@@ -20,7 +20,9 @@ Kinds (descriptor dicts as produced by ``workloads``):
 * ``sta``: tile-granular sliding window (Sliding Tile Attention explainer, method
   section 3): with tile coordinates a (query) and b (key) along an axis of n tiles
   and a window of w tiles, the window starts at clamp(a - floor(w/2), 0, n - w) and
-  the pair is kept iff start <= b < start + w on all three axes.  The window keeps
+  the pair is kept iff start <= b < start + w on all three axes.  n counts the tiles
+  of the axis padded up to a whole number of tiles (PSA notes, key design 2), which is
+  the plain tile count when the tile divides the grid.  The window keeps
   its size and is shifted inward at the grid edges; that reading reproduces the
   sparsities the explainer prints (91.00%, 58.33%, 75.00%), a truncated window
   would not.
@@ -73,9 +75,9 @@ def keep_matrix(desc, grid, cq, ck):
         if min(bt, bh, bw) <= 0:
             raise ValueError("sta mask needs the grid's tile size")
         m = np.ones((tq.shape[0], tk.shape[1]), dtype=bool)
-        for cq_ax, ck_ax, b, n, w in ((tq, tk, bt, grid["T"] // bt, desc["win_t"]),
-                                      (yq, yk, bh, grid["Hg"] // bh, desc["win_h"]),
-                                      (xq, xk, bw, grid["Wg"] // bw, desc["win_w"])):
+        for cq_ax, ck_ax, b, n, w in ((tq, tk, bt, -(-grid["T"] // bt), desc["win_t"]),
+                                      (yq, yk, bh, -(-grid["Hg"] // bh), desc["win_h"]),
+                                      (xq, xk, bw, -(-grid["Wg"] // bw), desc["win_w"])):
             if w < 1:
                 raise ValueError("sta window must be >= 1 tile")
             start = _sta_start(cq_ax // b, w, n)

@@ -12,14 +12,16 @@ from __future__ import annotations
 
 import numpy as np
 
-from .coords import token_coords
+from .coords import is_real, seq_len, token_coords
 
 
 def layout_permutation(grid, layout):
-    """perm[p'] = frame-major index of the token at executed position p' of layout."""
-    S = grid["T"] * grid["Hg"] * grid["Wg"]
+    """perm[p'] = frame-major index of the token at executed position p' of layout, or -1
+    where p' is a padding position (padded layout)."""
+    S = seq_len(grid, layout)
     t, y, x = token_coords(grid, layout, np.arange(S))
-    return (t * grid["Hg"] + y) * grid["Wg"] + x
+    frame = (t * grid["Hg"] + y) * grid["Wg"] + x
+    return np.where(is_real(grid, t, y, x), frame, -1)
 
 
 def tile_major_permutation(grid):
@@ -28,11 +30,16 @@ def tile_major_permutation(grid):
 
 
 def reorder_tokens(x, grid, inverse=False, layout="tile"):
-    """Permute axis 1 of x [B, S, ...]: frame-major -> layout, or back when inverse."""
+    """Permute axis 1 of x [B, S, ...]: frame-major -> layout (padding positions zero),
+    or back when inverse (padding positions dropped)."""
     perm = layout_permutation(grid, layout)
     x = np.asarray(x)
+    real = perm >= 0
     if not inverse:
-        return x[:, perm]
-    out = np.empty_like(x)
-    out[:, perm] = x
+        out = np.zeros((x.shape[0], len(perm)) + x.shape[2:], dtype=x.dtype)
+        out[:, real] = x[:, perm[real]]
+        return out
+    S = grid["T"] * grid["Hg"] * grid["Wg"]
+    out = np.empty((x.shape[0], S) + x.shape[2:], dtype=x.dtype)
+    out[:, perm[real]] = x[:, real]
     return out

@@ -596,3 +596,151 @@ def test_profiler_iid_inputs_prefer_spatial_and_ties():
     _, route = oracle.profile_heads(q, k, v, g, "frame", idx,
                                     [W.mask_all(), W.mask_temporal(2), W.mask_temporal(2)])
     assert route[0] == 1
+
+
+# ---------------------------------------------------------------------------
+# 3D padding (PSA notes, key design 2 and the worked example)
+# ---------------------------------------------------------------------------
+def test_padded_dims_of_the_psa_example():
+    """The worked example pads Wan 2.1's 21 x 45 x 80 latent to 21 x 48 x 80 for a
+    3 x 8 x 16 block (only H changes: 45 -> 48)."""
+    g = W.grid(21, 45, 80, (3, 8, 16))
+    assert oracle.padded_dims(g) == (21, 48, 80)
+    assert oracle.seq_len(g, "padded") == 21 * 48 * 80
+    assert oracle.seq_len(g, "frame") == 75600
+
+
+def test_padded_order_by_hand():
+    """1 x 3 x 3 grid, 1 x 2 x 2 tiles: padded to 1 x 4 x 4 and cut into 2 x 2 tiles,
+    tiles row-major, tokens row-major inside a tile; -1 marks padding (written out
+    from the definition)."""
+    g = W.grid(1, 3, 3, (1, 2, 2))
+    perm = oracle.layout_permutation(g, "padded")
+    assert list(perm) == [0, 1, 3, 4, 2, -1, 5, -1, 6, 7, -1, -1, 8, -1, -1, -1]
+
+
+@pytest.mark.parametrize("T,Hg,Wg,tile", [(3, 5, 7, (2, 2, 4)), (4, 4, 6, (2, 2, 3)), (1, 3, 3, (1, 2, 2)),
+                                          (5, 9, 2, (3, 4, 1))])
+def test_padded_order_is_an_injection(T, Hg, Wg, tile):
+    g = W.grid(T, Hg, Wg, tile)
+    perm = oracle.layout_permutation(g, "padded")
+    S = T * Hg * Wg
+    real = perm[perm >= 0]
+    assert np.array_equal(np.sort(real), np.arange(S))
+    assert len(perm) - len(real) == oracle.seq_len(g, "padded") - S
+    if T % tile[0] == 0 and Hg % tile[1] == 0 and Wg % tile[2] == 0:
+        assert np.array_equal(perm, oracle.layout_permutation(g, "tile"))
+    # round trip through the padded order, padding rows zero
+    x = _rand((2, S, 3), 90)
+    y = oracle.reorder_tokens(x, g, layout="padded")
+    assert np.all(y[:, perm < 0] == 0)
+    assert np.array_equal(oracle.reorder_tokens(y, g, inverse=True, layout="padded"), x)
+
+
+def _padded_order_brute(g):
+    """(t, y, x) of the padded order by nested loops: tiles row-major over the padded
+    tile grid, tokens row-major inside a tile."""
+    bt, bh, bw = g["tile_t"], g["tile_h"], g["tile_w"]
+    nT, nH, nW = (-(-g["T"] // bt), -(-g["Hg"] // bh), -(-g["Wg"] // bw))
+    out = []
+    for a, b, c in itertools.product(range(nT), range(nH), range(nW)):
+        for i, j, l in itertools.product(range(bt), range(bh), range(bw)):
+            out.append((a * bt + i, b * bh + j, c * bw + l))
+    return out
+
+
+@pytest.mark.parametrize("desc", [W.mask_box(1, 1, 2, sink_frames=1), W.mask_all(), W.mask_sta(1, 2, 1),
+                                  W.mask_stripe(1, 0, 2, 2, 1, 5)])
+def test_padded_classes_by_brute_force(desc):
+    """Classes over the padded order from pair-by-pair loops: padding pairs are never
+    kept, so a tile holding padding is never FULL."""
+    g = W.grid(3, 5, 7, (2, 2, 4))
+    pos = _padded_order_brute(g)
+    S = len(pos)
+    assert S == oracle.seq_len(g, "padded") == 4 * 6 * 8
+    real = [t < 3 and y < 5 and x < 7 for t, y, x in pos]
+    Bq, Bk = 16, 12
+    nQ, nK = -(-S // Bq), -(-S // Bk)
+
+    def kept(i, j):
+        if not (real[i] and real[j]):
+            return False
+        (tq, yq, xq), (tk, yk, xk) = pos[i], pos[j]
+        return bool(keep_matrix(desc, g, ([tq], [yq], [xq]), ([tk], [yk], [xk]))[0, 0])
+
+    got = oracle.classify(g, "padded", desc, Bq, Bk)["cls"]
+    for qt in range(nQ):
+        for kt in range(nK):
+            n = sum(kept(i, j) for i in range(qt * Bq, min(S, qt * Bq + Bq))
+                    for j in range(kt * Bk, min(S, kt * Bk + Bk)))
+            ref = oracle.EMPTY if n == 0 else (oracle.FULL if n == Bq * Bk else oracle.BOUNDARY)
+            assert got[qt, kt] == ref, (qt, kt, n)
+
+
+def test_padded_sliding_tiles_are_full_or_empty_away_from_padding():
+    """Sliding tiles with kernel tiles equal to the 3D tiles: a tile pair of real tokens
+    only is full or empty, and a pair holding padding is never full."""
+    g = W.grid(5, 6, 10, (2, 4, 4))  # padded to 6 x 8 x 12: 3 x 2 x 3 tiles of 32
+    desc = W.mask_sta(3, 1, 3)
+    cls = oracle.classify(g, "padded", desc, 32, 32)["cls"]
+    perm = oracle.layout_permutation(g, "padded")
+    tile_real = (perm.reshape(-1, 32) >= 0).all(axis=1)
+    both = tile_real[:, None] & tile_real[None, :]
+    assert not np.any(cls[both] == oracle.BOUNDARY)
+    assert not np.any(cls[~both] == oracle.FULL)
+
+
+def test_padded_attention_matches_frame_major():
+    """Attention in the padded order with zero padding rows equals frame-major
+    attention on the real rows: padding keys carry no weight."""
+    g = W.grid(3, 5, 7, (2, 2, 4))
+    S = 105
+    q, k, v = (_rand((1, S, 2, 8), 95 + s) for s in range(3))
+    masks = [W.mask_box(1, 2, 2, sink_frames=1), W.mask_sta(1, 1, 1)]
+    ref, ref_l = oracle.attention(q, k, v, g, "frame", masks)
+    qp, kp, vp = (oracle.reorder_tokens(x, g, layout="padded") for x in (q, k, v))
+    o, l = oracle.attention(qp, kp, vp, g, "padded", masks)
+    perm = oracle.layout_permutation(g, "padded")
+    real = perm >= 0
+    assert np.abs(oracle.reorder_tokens(o, g, inverse=True, layout="padded") - ref).max() < 1e-13
+    assert np.abs(l[:, :, real] - ref_l[:, :, perm[real]]).max() < 1e-13
+
+
+def test_padded_rounding_counts_real_pairs_only():
+    """B3 rounding on the padded order: a tile keeps its real pairs iff at least half of
+    its real pairs are kept (padding inside the tile is not counted)."""
+    g = W.grid(3, 5, 7, (2, 2, 4))
+    desc = W.mask_box(0, 1, 1)
+    Bq, Bk = 16, 16
+    pos = _padded_order_brute(g)
+    S = len(pos)
+    real = np.array([t < 3 and y < 5 and x < 7 for t, y, x in pos])
+    t, y, x = (np.array(c) for c in zip(*pos))
+    keep = keep_matrix(desc, g, (t, y, x), (t, y, x)) & real[:, None] & real[None, :]
+    ex = oracle.classify(g, "padded", desc, Bq, Bk)["cls"]
+    rd = oracle.classify(g, "padded", desc, Bq, Bk, round_tiles=True)["cls"]
+    for qt in range(S // Bq):
+        for kt in range(S // Bk):
+            blk = keep[qt * Bq:(qt + 1) * Bq, kt * Bk:(kt + 1) * Bk]
+            n_real = real[qt * Bq:(qt + 1) * Bq].sum() * real[kt * Bk:(kt + 1) * Bk].sum()
+            has_pad = n_real < Bq * Bk
+            if ex[qt, kt] != oracle.BOUNDARY:
+                assert rd[qt, kt] == ex[qt, kt]
+            elif 2 * blk.sum() >= n_real:
+                assert rd[qt, kt] == (oracle.BOUNDARY if has_pad else oracle.FULL)
+            else:
+                assert rd[qt, kt] == oracle.EMPTY
+    rows = np.arange(S)
+    rk = oracle.rounded_keep_rows(g, "padded", desc, Bq, Bk, rows)
+    assert not rk[~real].any() and not rk[:, ~real].any()
+
+
+def test_padded_sta_window_of_one_tile_is_block_diagonal():
+    """A 1 x 1 x 1 sliding window keeps exactly the pairs inside one 3D tile, also for
+    the partial tiles at the padded edges (the window counts the padded tiles)."""
+    g = W.grid(5, 3, 7, (2, 2, 4))  # partial tiles on every axis
+    S = W.seq_len(g)
+    t, y, x = token_coords(g, "frame", np.arange(S))
+    keep = keep_matrix(W.mask_sta(1, 1, 1), g, (t, y, x), (t, y, x))
+    tile = (t // 2) * 100 + (y // 2) * 10 + (x // 4)
+    assert np.array_equal(keep, tile[:, None] == tile[None, :])
