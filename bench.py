@@ -106,12 +106,14 @@ def kept_pairs(g, masks, B):
                     elif (abs(tk - tq - m["To"]) % m["Ts"]) <= m["Tw"] - 1:
                         c += n_intra
         elif m["kind"] == "sta":
-            bt, bh, bw = g["tile_t"], g["tile_h"], g["tile_w"]
-            vol = bt * bh * bw
-            per_axis = []
-            for n, w in ((T // bt, m["win_t"]), (Hg // bh, m["win_h"]), (Wg // bw, m["win_w"])):
-                per_axis.append(n * min(w, n))
-            c = per_axis[0] * per_axis[1] * per_axis[2] * vol * vol
+            # the window is a product over axes: count (query, key) coordinate pairs per
+            # axis (tiles counted over the axis padded up to whole tiles)
+            c = 1
+            for N, b, w in ((T, g["tile_t"], m["win_t"]), (Hg, g["tile_h"], m["win_h"]), (Wg, g["tile_w"], m["win_w"])):
+                n = -(-N // b)
+                a = np.arange(N) // b
+                start = np.minimum(np.maximum(a - w // 2, 0), max(n - w, 0))
+                c *= int(((a[None, :] >= start[:, None]) & (a[None, :] < start[:, None] + w)).sum())
         else:
             raise ValueError(m["kind"])
         cache[key] = c
@@ -239,8 +241,9 @@ def main():
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     o = torch.empty_like(qd)
     head_map, U = vsa.vsa_unique_masks(masks)
-    tiles = vsa.alloc_tile_lists(g, masks, Bq, Bk, dev, with_cls=False)
-    ws_bytes = vsa.vsa_fwd_workspace_bytes(B, S, H, D, vsa.VSA_BF16 if cfg["dtype"] == "bf16" else vsa.VSA_F32,
+    tiles = vsa.alloc_tile_lists(g, masks, Bq, Bk, dev, with_cls=False, layout=layout)
+    S_exec = vsa.vsa_seq_len(g, layout)  # executed length (padded grids are longer)
+    ws_bytes = vsa.vsa_fwd_workspace_bytes(B, S_exec, H, D, vsa.VSA_BF16 if cfg["dtype"] == "bf16" else vsa.VSA_F32,
                                            flags)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream(dev)
@@ -285,7 +288,7 @@ def main():
     fwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
     attn_ms = float(np.mean(fwd_ms))
 
-    f_exec = 4.0 * D * executed_pairs(tiles, head_map, B, S)
+    f_exec = 4.0 * D * executed_pairs(tiles, head_map, B, S_exec)
     n_full_tiles = int(tiles["n_full"][torch.as_tensor(head_map, device=dev).long()].sum())
     n_bnd_tiles = int(tiles["n_bnd"][torch.as_tensor(head_map, device=dev).long()].sum())
     f_kept = 4.0 * D * kept_pairs(g, masks, B)
@@ -318,8 +321,9 @@ def main():
         extra["profile_ms"] = round(float(np.mean(prof_ms)), 4)
         extra["profile_kv_gbs"] = round(2.0 * B * S * H * D * 2 / (np.mean(prof_ms) * 1e-3) / 1e9, 1)
     if reorder:
-        # the per-head token reorder alone, on one tensor: HBM GB/s (read + write)
-        y = torch.empty_like(qd)
+        # the per-head token reorder alone, on one tensor: HBM GB/s (read + write); the
+        # destination holds the executed order (the padded length for a padded grid)
+        y = torch.empty((B, S_exec, H, D), dtype=qd.dtype, device=dev)
         vsa.vsa_reorder_heads(qd, g, head_lays, dst=y, stream=stream)
         r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         r0.record(stream)
@@ -329,14 +333,14 @@ def main():
         torch.cuda.synchronize()
         r_ms = r0.elapsed_time(r1) / 5
         extra["reorder_ms_per_tensor"] = round(r_ms, 4)
-        extra["reorder_gbs"] = round(2.0 * qd.numel() * qd.element_size() / (r_ms * 1e-3) / 1e9, 1)
+        extra["reorder_gbs"] = round((qd.numel() + y.numel()) * qd.element_size() / (r_ms * 1e-3) / 1e9, 1)
         del y
 
     if "position_masks" in cfg and args.temporal_layout == "frame" and not args.round_tiles and not args.no_dense:
         # the same layer with its temporal heads attended position-major (reorder of
         # q, k, v and o inside the call): classify + forward per step, and the forward alone
         pm = cfg["position_masks"]
-        pm_tiles = vsa.alloc_tile_lists(g, pm, Bq, Bk, dev, with_cls=False)
+        pm_tiles = vsa.alloc_tile_lists(g, pm, Bq, Bk, dev, with_cls=False, layout=layout)
         pm_flags = flags | vsa.VSA_FWD_REORDER_IO
         pm_ws = torch.empty(vsa.vsa_fwd_workspace_bytes(B, S, H, D, vsa.VSA_BF16, pm_flags), dtype=torch.uint8,
                             device=dev)

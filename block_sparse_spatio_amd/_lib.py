@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libvsa.so")
 
 VSA_OK, VSA_ERR_INVALID_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_WORKSPACE, VSA_ERR_HIP = 0, -1, -2, -3, -4
 VSA_BF16, VSA_F32 = 0, 1
-VSA_LAYOUT_FRAME_MAJOR, VSA_LAYOUT_TILE_MAJOR, VSA_LAYOUT_POSITION_MAJOR = 0, 1, 2
+VSA_LAYOUT_FRAME_MAJOR, VSA_LAYOUT_TILE_MAJOR, VSA_LAYOUT_POSITION_MAJOR, VSA_LAYOUT_TILE_PADDED = 0, 1, 2, 3
 VSA_HEAD_LAYOUT_CALL, VSA_HEAD_LAYOUT_FRAME, VSA_HEAD_LAYOUT_TILE, VSA_HEAD_LAYOUT_POSITION = 0, 1, 2, 3
 VSA_MASK_ALL, VSA_MASK_BOX, VSA_MASK_STRIPE, VSA_MASK_STA = 0, 1, 2, 3
 VSA_TILE_EMPTY, VSA_TILE_FULL, VSA_TILE_BOUNDARY = 0, 1, 2
@@ -26,7 +26,8 @@ VSA_FWD_FORCE_MASK, VSA_FWD_REORDER_IO, VSA_FWD_WRITE_LSE, VSA_FWD_TILE_ALIGNED 
 VSA_CLASSIFY_ROUND_TILES = 1
 
 _KINDS = {"all": VSA_MASK_ALL, "box": VSA_MASK_BOX, "stripe": VSA_MASK_STRIPE, "sta": VSA_MASK_STA}
-_LAYOUTS = {"frame": VSA_LAYOUT_FRAME_MAJOR, "tile": VSA_LAYOUT_TILE_MAJOR, "position": VSA_LAYOUT_POSITION_MAJOR}
+_LAYOUTS = {"frame": VSA_LAYOUT_FRAME_MAJOR, "tile": VSA_LAYOUT_TILE_MAJOR, "position": VSA_LAYOUT_POSITION_MAJOR,
+            "padded": VSA_LAYOUT_TILE_PADDED}
 _HEAD_LAYOUTS = {"call": VSA_HEAD_LAYOUT_CALL, "frame": VSA_HEAD_LAYOUT_FRAME, "tile": VSA_HEAD_LAYOUT_TILE,
                  "position": VSA_HEAD_LAYOUT_POSITION}
 _MASK_FIELDS = ("kind", "sink_frames", "rt", "rh", "rw", "Tw", "To", "Ts", "Sw", "So", "Ss",
@@ -60,6 +61,7 @@ _SIGNATURES = {
     "vsa_last_error": (ctypes.c_char_p, []),
     "vsa_unique_masks": (_I, [ctypes.POINTER(vsa_mask_desc), _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "vsa_tile_counts": (_I, [ctypes.POINTER(vsa_grid), _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "vsa_seq_len": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(_I)]),
     "vsa_classify_tiles": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(vsa_mask_desc), _I, _I, _I,
                                 ctypes.POINTER(vsa_tile_lists), _P]),
     "vsa_classify_tiles_ex": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(vsa_mask_desc), _I, _I, _I, _I,
@@ -168,8 +170,16 @@ def vsa_tile_counts(grid, Bq, Bk):
     return nq.value, nk.value
 
 
-def alloc_tile_lists(grid, masks, Bq, Bk, device, with_cls=True):
-    nQ, nK = vsa_tile_counts(grid, Bq, Bk)
+def vsa_seq_len(grid, layout):
+    """Executed sequence length of a layout (T*Hg*Wg, or the padded grid's size)."""
+    s = _I()
+    _check(load().vsa_seq_len(ctypes.byref(make_grid(grid)), _layout(layout), ctypes.byref(s)))
+    return s.value
+
+
+def alloc_tile_lists(grid, masks, Bq, Bk, device, with_cls=True, layout="frame"):
+    S = vsa_seq_len(grid, layout)
+    nQ, nK = -(-S // Bq), -(-S // Bk)
     head_map, U = vsa_unique_masks(masks)
     kw = dict(device=device)
     return {
@@ -192,7 +202,7 @@ def vsa_classify_tiles(grid, layout, masks, Bq, Bk, out=None, device="cuda", str
     """Classify tiles; returns the dict of device tensors (allocated when out is None).
     round_tiles: tile-aligned rounding (vsa_classify_tiles_ex, VSA_CLASSIFY_ROUND_TILES)."""
     if out is None:
-        out = alloc_tile_lists(grid, masks, Bq, Bk, device, with_cls)
+        out = alloc_tile_lists(grid, masks, Bq, Bk, device, with_cls, layout)
     dev = out["n_full"].device
     arr = make_masks(masks)
     st = _lists_struct(out)
@@ -210,18 +220,26 @@ def vsa_fwd_workspace_bytes(B, S, H, D, dtype, flags):
 
 def vsa_sparse_attn_fwd(q, k, v, grid, layout, masks, tiles, scale=0.0, flags=0, o=None, lse=None,
                         workspace=None, stream=None):
-    """Block-sparse attention forward; q, k, v contiguous [B, S, H, D] on one device.
+    """Block-sparse attention forward; q, k, v contiguous [B, S, H, D] on one device (S the
+    executed length, or T*Hg*Wg with VSA_FWD_REORDER_IO).
     Returns (o, lse) with lse None unless VSA_FWD_WRITE_LSE is in flags."""
     for t in (q, k, v):
         if not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous [B, S, H, D]")
     B, S, H, D = q.shape
     dt = _dtype(q)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must have one shape and dtype")
     if o is None:
         o = torch.empty_like(q)
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("o must be a contiguous tensor shaped like q")
     if (flags & VSA_FWD_WRITE_LSE) and lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    need = vsa_fwd_workspace_bytes(B, S, H, D, dt, flags)
+    if lse is not None and (tuple(lse.shape) != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, H, S)}")
+    need = vsa_fwd_workspace_bytes(B, vsa_seq_len(grid, layout), H, D, dt, flags)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -243,10 +261,20 @@ def vsa_merge_partials(o_parts, lse_parts, o=None, lse=None, stream=None):
     for t in list(o_parts) + list(lse_parts):
         if not t.is_contiguous():
             raise ValueError("parts must be contiguous")
+    for t in o_parts:
+        if t.shape != o_parts[0].shape or t.dtype != o_parts[0].dtype:
+            raise ValueError("o_parts must share one shape and dtype")
+    for t in lse_parts:
+        if tuple(t.shape) != (B, H, S) or t.dtype != torch.float32:
+            raise ValueError(f"lse_parts must be float32 tensors of shape {(B, H, S)}")
     if o is None:
         o = torch.empty_like(o_parts[0])
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=o_parts[0].device)
+    if o.shape != o_parts[0].shape or o.dtype != o_parts[0].dtype or not o.is_contiguous():
+        raise ValueError("o must be a contiguous tensor shaped like the parts")
+    if tuple(lse.shape) != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, H, S)}")
     op = (_P * n)(*[_ptr(t) for t in o_parts])
     lp = (_P * n)(*[_ptr(t) for t in lse_parts])
     _check(load().vsa_merge_partials(op, lp, n, _ptr(o), _ptr(lse), _dtype(o_parts[0]), B, S, H, D,
@@ -258,22 +286,37 @@ def vsa_reorder_tokens(src, grid, inverse=False, dst=None, stream=None):
     if not src.is_contiguous():
         raise ValueError("src must be contiguous [B, S, H, D]")
     B, S, H, D = src.shape
+    if S != grid["T"] * grid["Hg"] * grid["Wg"]:
+        raise ValueError(f"src holds {S} positions, the grid {grid['T'] * grid['Hg'] * grid['Wg']}")
     if dst is None:
         dst = torch.empty_like(src)
+    if dst.shape != src.shape or dst.dtype != src.dtype or not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous tensor shaped like src")
     _check(load().vsa_reorder_tokens(_ptr(src), _ptr(dst), _dtype(src), B, H, D, ctypes.byref(make_grid(grid)),
                                      1 if inverse else 0, _stream(stream, src.device)))
     return dst
 
 
 def vsa_reorder_heads(src, grid, layouts, inverse=False, dst=None, stream=None):
-    """Per-head reorder of src [B, S, H, D]; layouts: H layout names or VSA_LAYOUT_* values."""
+    """Per-head reorder of src [B, S, H, D]; layouts: H layout names or VSA_LAYOUT_* values.
+    With the padded layout (all heads) dst has the padded length, or T*Hg*Wg when inverse."""
     if not src.is_contiguous():
         raise ValueError("src must be contiguous [B, S, H, D]")
     B, S, H, D = src.shape
     if len(layouts) != H:
         raise ValueError(f"{len(layouts)} layouts for {H} heads")
+    if _layout(layouts[0]) != VSA_LAYOUT_TILE_PADDED and S != grid["T"] * grid["Hg"] * grid["Wg"]:
+        raise ValueError(f"src holds {S} positions, the grid {grid['T'] * grid['Hg'] * grid['Wg']}")
+    S_dst = S
+    if _layout(layouts[0]) == VSA_LAYOUT_TILE_PADDED:
+        S_src = vsa_seq_len(grid, "padded") if inverse else grid["T"] * grid["Hg"] * grid["Wg"]
+        if S != S_src:
+            raise ValueError(f"src holds {S} positions, the padded reorder reads {S_src}")
+        S_dst = grid["T"] * grid["Hg"] * grid["Wg"] if inverse else vsa_seq_len(grid, "padded")
     if dst is None:
-        dst = torch.empty_like(src)
+        dst = torch.empty((B, S_dst, H, D), dtype=src.dtype, device=src.device)
+    if tuple(dst.shape) != (B, S_dst, H, D) or dst.dtype != src.dtype or not dst.is_contiguous():
+        raise ValueError(f"dst must be a contiguous {src.dtype} tensor of shape {(B, S_dst, H, D)}")
     lay = (_I * H)(*[_layout(x) for x in layouts])
     _check(load().vsa_reorder_heads(_ptr(src), _ptr(dst), _dtype(src), B, H, D, ctypes.byref(make_grid(grid)),
                                     lay, 1 if inverse else 0, _stream(stream, src.device)))

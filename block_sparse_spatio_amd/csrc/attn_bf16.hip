@@ -80,6 +80,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   if constexpr (KIND >= 0) m.kind = KIND;
   Geom g = head_geom(a.g, m);
   if constexpr (ORDER >= 0) g.layout = ORDER;
+  if constexpr (ORDER == VSA_LAYOUT_FRAME_MAJOR || ORDER == VSA_LAYOUT_POSITION_MAJOR) g.padded = 0;
   const size_t lrow = (size_t)slot * a.nQ + qt;
   // List lengths and entries are clamped to the list row, so malformed lists cannot
   // send a load outside the tensors.  The lists come in as read-only, non-aliased
@@ -441,8 +442,9 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
         *(u32x2*)(op + d) = u32x2{w0, w1};
       }
     if (a.write_lse && g2 == 0) {
-      const int lpos = a.lse_frame_major ? frame_index(g, qrow) : qrow;
-      a.lse[((size_t)b * H + h) * S + lpos] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+      const int lpos = a.lse_frame_major ? frame_index(g, qrow) : qrow;  // -1: padding row
+      if (lpos >= 0)
+        a.lse[((size_t)b * H + h) * a.lse_S + lpos] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
     }
   }
   };

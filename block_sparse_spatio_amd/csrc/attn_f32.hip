@@ -97,8 +97,8 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(FwdArgs a, MaskTable 
 #pragma unroll
     for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
     if (a.write_lse) {
-      const int lpos = a.lse_frame_major ? frame_index(g, qrow) : qrow;
-      a.lse[((size_t)b * H + h) * S + lpos] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+      const int lpos = a.lse_frame_major ? frame_index(g, qrow) : qrow;  // -1: padding row
+      if (lpos >= 0) a.lse[((size_t)b * H + h) * a.lse_S + lpos] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
     }
   }
 }

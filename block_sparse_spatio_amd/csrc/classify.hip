@@ -33,10 +33,14 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
   const Geom g = head_geom(g_call, m);
   const int r0 = qt * Bq;
   const int r1 = imin(r0 + Bq, g.S);
-  const bool q_padded = (r0 + Bq) > g.S;
+  bool q_padded = (r0 + Bq) > g.S;
 
+  // boxes of the query tile's real tokens (padding of a padded grid is never kept)
   Box R[11];
-  const int nr = decompose(g, r0, r1, R);
+  int nr = decompose(g, r0, r1, R);
+  if (g.padded) nr = clip_real(g, R, nr, q_padded);
+  long long q_real = 0;
+  for (int i = 0; i < nr; ++i) q_real += box_volume(R[i]);
 
   __shared__ int s_cnt[2][kWaves];
   const int lane = threadIdx.x & 63;
@@ -54,15 +58,24 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
       const int c0 = kt * Bk;
       const int c1 = imin(c0 + Bk, g.S);
       Box C[11];
-      const int nc = decompose(g, c0, c1, C);
-      const bool padded = q_padded || (c0 + Bk) > g.S;
+      int nc = decompose(g, c0, c1, C);
+      bool padded = q_padded || (c0 + Bk) > g.S;
+      if (g.padded) nc = clip_real(g, C, nc, padded);
       c = tile_class(g, m, R, nr, C, nc, padded);
       if (round_tiles && c == VSA_TILE_BOUNDARY) {
         // tile-aligned rounding: keep the tile's real pairs iff at least half are kept
         // (per-row popcounts of the exact row masks; Bk <= 64)
-        long long kept = 0;
-        for (int r = r0; r < r1; ++r) kept += __popcll(tile_row_mask(g, m, make_query(g, m, r), c0, c1 - c0));
-        const long long real = (long long)(r1 - r0) * (c1 - c0);
+        long long kept = 0, k_real = 0;
+        for (int r = r0; r < r1; ++r) {
+          if (g.padded) {  // padding query rows hold no pair
+            int t, y, x;
+            pos_coords(g, r, t, y, x);
+            if (t >= g.T || y >= g.Hg || x >= g.Wg) continue;
+          }
+          kept += __popcll(tile_row_mask(g, m, make_query(g, m, r), c0, c1 - c0));
+        }
+        for (int j = 0; j < nc; ++j) k_real += box_volume(C[j]);
+        const long long real = q_real * k_real;
         c = 2 * kept >= real ? (padded ? VSA_TILE_BOUNDARY : VSA_TILE_FULL) : VSA_TILE_EMPTY;
       }
       if (cls_row) cls_row[kt] = (uint8_t)c;

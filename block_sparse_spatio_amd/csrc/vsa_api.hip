@@ -35,6 +35,9 @@ vsa_status hip_fail(hipError_t e, const char* what) {
 
 constexpr long long kMaxS = 1LL << 30;
 
+long long ceil_to(long long a, long long b) { return (a + b - 1) / b * b; }
+
+// Validate the grid for a call layout; *S = T*Hg*Wg (the frame-major sequence length).
 vsa_status check_grid(const vsa_grid* g, vsa_layout layout, bool need_tile, long long* S) {
   if (!g) return fail(VSA_ERR_INVALID_ARG, "grid is NULL");
   if (g->T <= 0 || g->Hg <= 0 || g->Wg <= 0)
@@ -44,20 +47,33 @@ vsa_status check_grid(const vsa_grid* g, vsa_layout layout, bool need_tile, long
     return fail(VSA_ERR_UNSUPPORTED, "grid dimensions above 32767 are not supported");
   const long long s = (long long)g->T * g->Hg * g->Wg;
   if (s > kMaxS) return fail(VSA_ERR_UNSUPPORTED, "sequence length %lld above 2^30", s);
-  if (layout != VSA_LAYOUT_FRAME_MAJOR && layout != VSA_LAYOUT_TILE_MAJOR && layout != VSA_LAYOUT_POSITION_MAJOR)
+  if (layout != VSA_LAYOUT_FRAME_MAJOR && layout != VSA_LAYOUT_TILE_MAJOR && layout != VSA_LAYOUT_POSITION_MAJOR &&
+      layout != VSA_LAYOUT_TILE_PADDED)
     return fail(VSA_ERR_INVALID_ARG, "unknown layout %d", (int)layout);
-  const bool tile_set = g->tile_t > 0 || g->tile_h > 0 || g->tile_w > 0;
-  if (layout == VSA_LAYOUT_TILE_MAJOR || need_tile || tile_set) {
-    if (g->tile_t <= 0 || g->tile_h <= 0 || g->tile_w <= 0)
-      return fail(VSA_ERR_INVALID_ARG, "tile-major layout and sliding-tile masks need tile_t/h/w > 0");
-    if (g->T % g->tile_t || g->Hg % g->tile_h || g->Wg % g->tile_w)
-      return fail(VSA_ERR_INVALID_ARG, "tile %dx%dx%d does not divide grid %dx%dx%d", g->tile_t,
-                  g->tile_h, g->tile_w, g->T, g->Hg, g->Wg);
-  }
   if (g->tile_t < 0 || g->tile_h < 0 || g->tile_w < 0)
     return fail(VSA_ERR_INVALID_ARG, "negative tile size");
+  const bool tile_set = g->tile_t > 0 || g->tile_h > 0 || g->tile_w > 0;
+  if (layout == VSA_LAYOUT_TILE_MAJOR || layout == VSA_LAYOUT_TILE_PADDED || need_tile || tile_set) {
+    if (g->tile_t <= 0 || g->tile_h <= 0 || g->tile_w <= 0)
+      return fail(VSA_ERR_INVALID_ARG, "tile-major layouts and sliding-tile masks need tile_t/h/w > 0");
+    if (layout == VSA_LAYOUT_TILE_PADDED) {  // each axis is padded up to whole tiles
+      const long long tp = ceil_to(g->T, g->tile_t), hp = ceil_to(g->Hg, g->tile_h), wp = ceil_to(g->Wg, g->tile_w);
+      if (tp > 32767 || hp > 32767 || wp > 32767 || tp * hp * wp > kMaxS)
+        return fail(VSA_ERR_UNSUPPORTED, "padded grid %lldx%lldx%lld too large", tp, hp, wp);
+    } else if (g->T % g->tile_t || g->Hg % g->tile_h || g->Wg % g->tile_w) {
+      return fail(VSA_ERR_INVALID_ARG, "tile %dx%dx%d does not divide grid %dx%dx%d (the padded layout pads it)",
+                  g->tile_t, g->tile_h, g->tile_w, g->T, g->Hg, g->Wg);
+    }
+  }
   *S = s;
   return VSA_OK;
+}
+
+// Executed sequence length of the call layout: the padded grid's size for the padded
+// layout, else T*Hg*Wg.  The grid must have passed check_grid.
+long long exec_len(const vsa_grid* g, vsa_layout layout) {
+  if (layout != VSA_LAYOUT_TILE_PADDED) return (long long)g->T * g->Hg * g->Wg;
+  return ceil_to(g->T, g->tile_t) * ceil_to(g->Hg, g->tile_h) * ceil_to(g->Wg, g->tile_w);
 }
 
 vsa::Geom make_geom(const vsa_grid* g, vsa_layout layout) {
@@ -66,10 +82,13 @@ vsa::Geom make_geom(const vsa_grid* g, vsa_layout layout) {
   G.bt = g->tile_t > 0 ? g->tile_t : 1;
   G.bh = g->tile_h > 0 ? g->tile_h : 1;
   G.bw = g->tile_w > 0 ? g->tile_w : 1;
-  G.nT = G.T / G.bt; G.nH = G.Hg / G.bh; G.nW = G.Wg / G.bw;
+  // tile counts of the grid padded up to whole tiles (equal to the exact counts when
+  // the tile divides the grid, which every layout but the padded one requires)
+  G.nT = (G.T + G.bt - 1) / G.bt; G.nH = (G.Hg + G.bh - 1) / G.bh; G.nW = (G.Wg + G.bw - 1) / G.bw;
   G.HW = G.Hg * G.Wg;
-  G.S = G.T * G.HW;
-  G.layout = (int32_t)layout;
+  G.padded = layout == VSA_LAYOUT_TILE_PADDED ? 1 : 0;
+  G.S = (int32_t)exec_len(g, layout);
+  G.layout = (int32_t)(layout == VSA_LAYOUT_TILE_PADDED ? VSA_LAYOUT_TILE_MAJOR : layout);
   return G;
 }
 
@@ -83,7 +102,13 @@ vsa_status normalise(const vsa_mask_desc& d, const vsa_grid* g, vsa_layout layou
   if (d.sink_frames < 0) return fail(VSA_ERR_INVALID_ARG, "mask %d: sink_frames < 0", index);
   if (d.head_layout < VSA_HEAD_LAYOUT_CALL || d.head_layout > VSA_HEAD_LAYOUT_POSITION)
     return fail(VSA_ERR_INVALID_ARG, "mask %d: unknown head_layout %d", index, d.head_layout);
-  out->layout = (int16_t)(d.head_layout == VSA_HEAD_LAYOUT_CALL ? (int)layout : d.head_layout - 1);
+  if (layout == VSA_LAYOUT_TILE_PADDED && d.head_layout != VSA_HEAD_LAYOUT_CALL)
+    return fail(VSA_ERR_INVALID_ARG, "mask %d: the padded layout applies to every head (head_layout must be 0)",
+                index);
+  if (layout == VSA_LAYOUT_TILE_PADDED)
+    out->layout = VSA_LAYOUT_TILE_MAJOR;  // over the padded grid
+  else
+    out->layout = (int16_t)(d.head_layout == VSA_HEAD_LAYOUT_CALL ? (int)layout : d.head_layout - 1);
   out->kind = (int16_t)d.kind;
   out->sink = (int16_t)(d.sink_frames < g->T ? d.sink_frames : g->T);
   const bool box_unused = d.rt == 0 && d.rh == 0 && d.rw == 0;
@@ -126,7 +151,9 @@ vsa_status normalise(const vsa_mask_desc& d, const vsa_grid* g, vsa_layout layou
         return fail(VSA_ERR_INVALID_ARG, "mask %d: STA with box/stripe fields set", index);
       if (d.win_t < 1 || d.win_h < 1 || d.win_w < 1)
         return fail(VSA_ERR_INVALID_ARG, "mask %d: STA window must be >= 1 tile per axis", index);
-      const int nT = g->T / g->tile_t, nH = g->Hg / g->tile_h, nW = g->Wg / g->tile_w;
+      // tiles per axis of the grid padded up to whole tiles
+      const int nT = (g->T + g->tile_t - 1) / g->tile_t, nH = (g->Hg + g->tile_h - 1) / g->tile_h,
+                nW = (g->Wg + g->tile_w - 1) / g->tile_w;
       out->wt = (int16_t)(d.win_t < nT ? d.win_t : nT);
       out->wh = (int16_t)(d.win_h < nH ? d.win_h : nH);
       out->ww = (int16_t)(d.win_w < nW ? d.win_w : nW);
@@ -210,6 +237,15 @@ vsa_status vsa_tile_counts(const vsa_grid* grid, int32_t Bq, int32_t Bk, int32_t
   return ok();
 }
 
+vsa_status vsa_seq_len(const vsa_grid* grid, vsa_layout layout, int32_t* S) {
+  long long s;
+  vsa_status st = check_grid(grid, layout, false, &s);
+  if (st != VSA_OK) return st;
+  if (!S) return fail(VSA_ERR_INVALID_ARG, "S is NULL");
+  *S = (int32_t)exec_len(grid, layout);
+  return ok();
+}
+
 vsa_status vsa_classify_tiles(const vsa_grid* grid, vsa_layout layout, const vsa_mask_desc* masks, int32_t H,
                               int32_t Bq, int32_t Bk, const vsa_tile_lists* out, void* stream) {
   return vsa_classify_tiles_ex(grid, layout, masks, H, Bq, Bk, 0, out, stream);
@@ -231,6 +267,7 @@ vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout, const 
   int32_t U = 0;
   st = build_table(masks, H, grid, layout, &table, &hm, &U);
   if (st != VSA_OK) return st;
+  S = exec_len(grid, layout);
   const int32_t nQ = (int32_t)((S + Bq - 1) / Bq), nK = (int32_t)((S + Bk - 1) / Bk);
   hipError_t e = vsa::launch_classify(make_geom(grid, layout), table, U, Bq, Bk, round_tiles, nQ, nK, *out,
                                       (hipStream_t)stream);
@@ -267,7 +304,13 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   if (!q || !k || !v || !o) return fail(VSA_ERR_INVALID_ARG, "q, k, v, o must be non-NULL");
   if (o == q || o == k || o == v) return fail(VSA_ERR_INVALID_ARG, "o must not alias q, k or v");
   if (B <= 0 || H <= 0) return fail(VSA_ERR_INVALID_ARG, "B and H must be positive");
-  if (S != S_grid) return fail(VSA_ERR_INVALID_ARG, "S=%d but grid gives T*Hg*Wg=%lld", S, S_grid);
+  // q/k/v/o hold the executed order (the padded grid's length for the padded layout), or
+  // the frame-major sequence when the call reorders them
+  const long long S_exec = exec_len(grid, layout);
+  const long long S_io = (flags & VSA_FWD_REORDER_IO) ? S_grid : S_exec;
+  if (S != S_io)
+    return fail(VSA_ERR_INVALID_ARG, "S=%d but the grid and layout give %lld positions%s", S, S_io,
+                (flags & VSA_FWD_REORDER_IO) ? " (frame-major I/O)" : "");
   if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (D != 64 && D != 128) return fail(VSA_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", D);
   if (flags & ~(VSA_FWD_FORCE_MASK | VSA_FWD_REORDER_IO | VSA_FWD_WRITE_LSE | VSA_FWD_TILE_ALIGNED))
@@ -285,7 +328,7 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   if (!isfinite(scale)) return fail(VSA_ERR_INVALID_ARG, "scale is not finite");
   const bool reorder = (flags & VSA_FWD_REORDER_IO) != 0;
   const size_t eb = elem_size(dtype);
-  const size_t nelem = (size_t)B * S * H * D;
+  const size_t nelem = (size_t)B * S_exec * H * D;  // one reordered tensor
   vsa::MaskTable table;
   vsa::HeadMap hm;
   int32_t U = 0;
@@ -300,7 +343,8 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   }
   if (reorder && !any_permuted)
     return fail(VSA_ERR_INVALID_ARG, "VSA_FWD_REORDER_IO needs a head whose layout is not frame-major");
-  const size_t need = fwd_ws_bytes(B, S, H, D, dtype, flags);
+  if (reorder && B > 65535) return fail(VSA_ERR_UNSUPPORTED, "VSA_FWD_REORDER_IO with B=%d above 65535", B);
+  const size_t need = fwd_ws_bytes(B, (int32_t)S_exec, H, D, dtype, flags);
   if (need && (!workspace || ws_bytes < need))
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
   if (need && ((uintptr_t)workspace & 15))
@@ -309,10 +353,11 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   vsa::FwdArgs a;
   memset(&a, 0, sizeof a);
   a.g = make_geom(grid, layout);
-  a.B = B; a.S = S; a.H = H; a.D = D;
+  a.B = B; a.S = (int32_t)S_exec; a.H = H; a.D = D;
   a.Bq = Bq; a.Bk = Bk;
-  a.nQ = (S + Bq - 1) / Bq;
-  a.nK = (S + Bk - 1) / Bk;
+  a.nQ = (a.S + Bq - 1) / Bq;
+  a.nK = (a.S + Bk - 1) / Bk;
+  a.lse_S = S;
   a.scale = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
   a.force_mask = (flags & VSA_FWD_FORCE_MASK) ? 1 : 0;
   a.pad_only = (flags & VSA_FWD_TILE_ALIGNED) ? 1 : 0;
@@ -340,9 +385,9 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   }
   hipError_t e;
   if (dtype == VSA_BF16) {
-    a.s_pad = (int32_t)vt_pad(S);
+    a.s_pad = (int32_t)vt_pad(a.S);
     void* vt = ws + (reorder ? 3 * nelem * eb : 0);
-    if ((e = vsa::launch_transpose_v(a.v, vt, B, S, H, D, a.s_pad, hs)) != hipSuccess)
+    if ((e = vsa::launch_transpose_v(a.v, vt, B, a.S, H, D, a.s_pad, hs)) != hipSuccess)
       return hip_fail(e, "transpose v");
     a.vt = vt;
     e = vsa::launch_attn_bf16(a, table, hm, hs);
@@ -396,28 +441,33 @@ vsa_status vsa_reorder_heads(const void* src, void* dst, vsa_dtype dtype, int32_
   if (H <= 0 || H > VSA_MAX_HEADS) return fail(VSA_ERR_INVALID_ARG, "H must be in 1..%d", VSA_MAX_HEADS);
   vsa::HeadLayouts hl;
   memset(&hl, 0, sizeof hl);
-  bool any_tile = false, uniform = true;
+  bool any_tile = false, any_padded = false, uniform = true;
   for (int h = 0; h < H; ++h) {
     if (layouts[h] != VSA_LAYOUT_FRAME_MAJOR && layouts[h] != VSA_LAYOUT_TILE_MAJOR &&
-        layouts[h] != VSA_LAYOUT_POSITION_MAJOR)
+        layouts[h] != VSA_LAYOUT_POSITION_MAJOR && layouts[h] != VSA_LAYOUT_TILE_PADDED)
       return fail(VSA_ERR_INVALID_ARG, "head %d: unknown layout %d", h, layouts[h]);
-    hl.lay[h] = (uint8_t)layouts[h];
+    hl.lay[h] = (uint8_t)(layouts[h] == VSA_LAYOUT_TILE_PADDED ? VSA_LAYOUT_TILE_MAJOR : layouts[h]);
     any_tile = any_tile || layouts[h] == VSA_LAYOUT_TILE_MAJOR;
+    any_padded = any_padded || layouts[h] == VSA_LAYOUT_TILE_PADDED;
     uniform = uniform && layouts[h] == layouts[0];
   }
+  if (any_padded && !uniform)
+    return fail(VSA_ERR_INVALID_ARG, "the padded layout applies to every head or none");
+  const vsa_layout call = any_padded ? VSA_LAYOUT_TILE_PADDED : any_tile ? VSA_LAYOUT_TILE_MAJOR : VSA_LAYOUT_FRAME_MAJOR;
   long long S;
-  vsa_status st = check_grid(grid, any_tile ? VSA_LAYOUT_TILE_MAJOR : VSA_LAYOUT_FRAME_MAJOR, any_tile, &S);
+  vsa_status st = check_grid(grid, call, any_tile || any_padded, &S);
   if (st != VSA_OK) return st;
   if (!src || !dst) return fail(VSA_ERR_INVALID_ARG, "src and dst must be non-NULL");
   if (src == dst) return fail(VSA_ERR_INVALID_ARG, "src and dst must not alias");
   if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (B <= 0 || D <= 0) return fail(VSA_ERR_INVALID_ARG, "B, H, D must be positive");
+  if (B > 65535) return fail(VSA_ERR_UNSUPPORTED, "B=%d above 65535", B);
   if (((long long)H * D * elem_size(dtype)) % 16)
     return fail(VSA_ERR_UNSUPPORTED, "token row of H*D elements must be a multiple of 16 bytes");
   if (!uniform && ((long long)D * elem_size(dtype)) % 16)
     return fail(VSA_ERR_UNSUPPORTED, "heads with different layouts need D*element size a multiple of 16 bytes");
-  hipError_t e = vsa::launch_reorder(src, dst, elem_size(dtype), B, H, D, make_geom(grid, VSA_LAYOUT_FRAME_MAJOR),
-                                     hl, inverse ? 1 : 0, (hipStream_t)stream);
+  hipError_t e = vsa::launch_reorder(src, dst, elem_size(dtype), B, H, D, make_geom(grid, call), hl,
+                                     inverse ? 1 : 0, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "reorder launch");
   return ok();
 }
@@ -450,6 +500,8 @@ vsa_status vsa_profile_heads(const void* q, const void* k, const void* v, vsa_dt
   if (!q || !k || !v || !sample_idx || !err || !route)
     return fail(VSA_ERR_INVALID_ARG, "q, k, v, sample_idx, err, route must be non-NULL");
   if (B <= 0 || H <= 0) return fail(VSA_ERR_INVALID_ARG, "B and H must be positive");
+  if (layout == VSA_LAYOUT_TILE_PADDED)
+    return fail(VSA_ERR_UNSUPPORTED, "the profiler samples real tokens; the padded layout is not supported");
   if (S != S_grid) return fail(VSA_ERR_INVALID_ARG, "S=%d but grid gives T*Hg*Wg=%lld", S, S_grid);
   if (dtype != VSA_BF16 && dtype != VSA_F32) return fail(VSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (dtype != VSA_BF16) return fail(VSA_ERR_UNSUPPORTED, "the profiler takes bf16 inputs");

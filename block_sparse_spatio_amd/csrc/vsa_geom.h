@@ -73,10 +73,11 @@ VSA_HD void pos_coords(const Geom& g, int p, int& t, int& y, int& x) {
   }
 }
 
-// Frame-major index of the token at executed position p.
+// Frame-major index of the token at executed position p, or -1 where p is padding.
 VSA_HD int frame_index(const Geom& g, int p) {
   int t, y, x;
   pos_coords(g, p, t, y, x);
+  if (t >= g.T || y >= g.Hg || x >= g.Wg) return -1;
   return (t * g.Hg + y) * g.Wg + x;
 }
 
@@ -207,6 +208,25 @@ VSA_HD int decompose(const Geom& g, int lo, int end, Box* out) {
   }
   if (end > g.HW) nb += decompose_pm_rest(g, imax(lo, g.HW) - g.HW, end - g.HW, out + nb);
   return nb;
+}
+
+// Padded grid: cut boxes of padded coordinates down to the real tokens, dropping
+// boxes with none; `clipped` is set when some position was padding.
+VSA_HD int clip_real(const Geom& g, Box* b, int n, bool& clipped) {
+  int k = 0;
+  for (int i = 0; i < n; ++i) {
+    Box c = b[i];
+    const int t1 = imin(c.t1, g.T - 1), y1 = imin(c.y1, g.Hg - 1), x1 = imin(c.x1, g.Wg - 1);
+    if (t1 != c.t1 || y1 != c.y1 || x1 != c.x1) clipped = true;
+    if (c.t0 > t1 || c.y0 > y1 || c.x0 > x1) continue;
+    c.t1 = t1; c.y1 = y1; c.x1 = x1;
+    b[k++] = c;
+  }
+  return k;
+}
+
+VSA_HD long long box_volume(const Box& b) {
+  return (long long)(b.t1 - b.t0 + 1) * (b.y1 - b.y0 + 1) * (b.x1 - b.x0 + 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -385,6 +405,10 @@ VSA_HD uint64_t periodic_bits(int ua, int ub, int P, int w, int off) {
 // kept keys of a run (fixed t, y; x in [x0, x1]; bit of x0 is off) for query q
 VSA_HD uint64_t run_mask(const Geom& g, const DevMask& m, const QueryPos& q, int t, int y, int x0,
                          int x1, int off) {
+  if (g.padded) {  // padding keys are never kept
+    if (t >= g.T || y >= g.Hg || x0 >= g.Wg) return 0;
+    x1 = imin(x1, g.Wg - 1);
+  }
   if (t < m.sink || m.kind == VSA_MASK_ALL) return bit_range(off, off + x1 - x0);
   switch (m.kind) {
     case VSA_MASK_BOX: {
@@ -543,10 +567,23 @@ VSA_HD void run_advance_pm(const Geom& g, RunCursor& c, int len) {
   c.p += len;
 }
 
-// keys [c0, c0 + nbits) that lie before S (the only element mask of a tile-aligned list)
+// keys [c0, c0 + nbits) that are real tokens: before S, and not padding of a padded
+// grid (the only element mask of a tile-aligned list)
 VSA_HD uint64_t real_key_mask(const Geom& g, int c0, int nbits) {
-  const int n = imin(c0 + nbits, g.S) - c0;
-  return n <= 0 ? 0ull : bit_range(0, n - 1);
+  const int end = imin(c0 + nbits, g.S);
+  if (end <= c0) return 0ull;
+  if (!g.padded) return bit_range(0, end - c0 - 1);
+  uint64_t bits = 0;
+  RunCursor c = run_begin(g, c0);
+  while (c.p < end) {
+    const int len = run_len_ft(g, c, end);
+    if (c.t < g.T && c.y < g.Hg && c.x < g.Wg) {
+      const int x1 = imin(c.x + len - 1, g.Wg - 1);
+      bits |= bit_range(c.p - c0, c.p - c0 + x1 - c.x);
+    }
+    run_advance_ft(g, c, len);
+  }
+  return bits;
 }
 
 // Keep bits of keys [c0, min(c0 + nbits, S)) for query q (nbits <= 64): one loop for

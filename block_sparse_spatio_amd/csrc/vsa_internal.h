@@ -23,13 +23,39 @@ struct DevMask {
 };
 static_assert(sizeof(DevMask) == 32, "DevMask layout");
 
+// Division of 0 <= n < 2^31 by a divisor d >= 1 fixed for a call, as a multiply-high, an
+// add and a shift (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (mulhi(m, n) + n) >> l; mulhi(m, n) < n keeps the sum below 2^32.  Used where
+// every element of a memory-bound kernel divides by a few call constants.
+struct FastDiv {
+  uint32_t m, l;
+};
+
+__host__ __device__ inline FastDiv fastdiv_make(int32_t d) {
+  const uint32_t dd = d < 1 ? 1u : (uint32_t)d;
+  uint32_t l = 0;
+  while ((1ull << l) < dd) ++l;
+  FastDiv f;
+  f.m = (uint32_t)((((1ull << l) - dd) << 32) / dd + 1);
+  f.l = l;
+  return f;
+}
+
+__host__ __device__ inline int32_t fastdiv_q(int32_t n, FastDiv f) {
+  const uint32_t hi = (uint32_t)(((uint64_t)f.m * (uint32_t)n) >> 32);
+  return (int32_t)((hi + (uint32_t)n) >> f.l);
+}
+
 // Geometry of the token grid and the executed order.
 struct Geom {
-  int32_t T, Hg, Wg;
+  int32_t T, Hg, Wg;     // the token grid
   int32_t bt, bh, bw;    // 3D tile (tile-major layout and STA masks), else 1
-  int32_t nT, nH, nW;    // tile grid
-  int32_t S, HW;
-  int32_t layout;        // VSA_LAYOUT_* (kernels take it per head from DevMask::layout)
+  int32_t nT, nH, nW;    // tile grid (of the padded grid: each axis rounded up to tiles)
+  int32_t S, HW;         // executed length (T*Hg*Wg, or the padded grid's size), Hg*Wg
+  int32_t layout;        // VSA_LAYOUT_FRAME/TILE/POSITION_MAJOR (kernels take it per head
+                         // from DevMask::layout; the padded layout is TILE_MAJOR + padded)
+  int32_t padded;        // tile-major over the padded grid: positions may be padding
 };
 
 // The geometry of one head: the grid with that head's executed order.
@@ -76,7 +102,8 @@ struct FwdArgs {
   int32_t force_mask;
   int32_t pad_only;     // boundary tiles mask only keys past S (tile-aligned lists)
   int32_t write_lse;
-  int32_t lse_frame_major;  // executed order is tile-major; write lse in frame-major order
+  int32_t lse_frame_major;  // q/k/v/o were reordered: write lse in frame-major order
+  int32_t lse_S;            // length of an lse row (the caller's sequence length)
   Geom g;
 };
 

@@ -51,27 +51,29 @@ typedef enum {
 
 typedef enum { VSA_BF16 = 0, VSA_F32 = 1 } vsa_dtype;
 
-/* Order of the S positions along the sequence axis of Q/K/V/O.
- *   FRAME_MAJOR: position p = (t*Hg + y)*Wg + x (tokens of one frame contiguous).
- *   TILE_MAJOR:  the grid is cut into tiles of tile_t x tile_h x tile_w tokens; the
- *     tiles are ordered row-major over the tile grid and the tokens row-major inside
- *     a tile, so every tile is contiguous (Sliding Tile Attention explainer, method
- *     section 3; PSA notes, key design 2).  T, Hg, Wg must be multiples of the tile. */
-/* Executed token order of a head.
- *   FRAME_MAJOR:    (t, y, x) row-major, the natural order.
+/* Executed token order of a head: the order of the positions along the sequence axis
+ * of Q/K/V/O (unless the call reorders them, VSA_FWD_REORDER_IO).
+ *   FRAME_MAJOR:    position p = (t*Hg + y)*Wg + x, the natural order.
  *   TILE_MAJOR:     3D tiles of tile_t x tile_h x tile_w tokens contiguous, tiles and
  *                   in-tile tokens row-major (Sliding Tile Attention explainer, method
- *                   section 3).
+ *                   section 3; PSA notes, key design 2).  The tile must divide the grid.
  *   POSITION_MAJOR: frame 0 first in frame-major order, then for every spatial
  *                   position s = y*Wg + x (ascending) its frames 1 .. T-1: position
  *                   Hg*Wg + s*(T-1) + (t-1).  The temporal order of Sparse VideoGen on
  *                   TPU ("arranging tokens for temporal access": (F,H,W) -> (H,W,F)),
  *                   with the first frame kept as a leading block so that the
- *                   first-frame sink stays contiguous. */
+ *                   first-frame sink stays contiguous.
+ *   TILE_PADDED:    TILE_MAJOR over the grid padded up to whole tiles on every axis
+ *                   (PSA notes, key design 2, 3D padding: T' = ceil(T/tile_t)*tile_t,
+ *                   likewise H', W').  The executed length is T'*H'*W' (vsa_seq_len);
+ *                   positions outside the real grid are padding: never kept as keys,
+ *                   and their query outputs are unspecified.  A call-level layout only:
+ *                   it applies to every head (head_layout must be 0). */
 typedef enum {
   VSA_LAYOUT_FRAME_MAJOR = 0,
   VSA_LAYOUT_TILE_MAJOR = 1,
-  VSA_LAYOUT_POSITION_MAJOR = 2
+  VSA_LAYOUT_POSITION_MAJOR = 2,
+  VSA_LAYOUT_TILE_PADDED = 3
 } vsa_layout;
 
 /* Latent grid.  S = T*Hg*Wg.  tile_* is the 3D token tile used by TILE_MAJOR and by
@@ -123,7 +125,8 @@ typedef struct {
 enum { VSA_TILE_EMPTY = 0, VSA_TILE_FULL = 1, VSA_TILE_BOUNDARY = 2 };
 
 /* Output of the classifier, all caller-allocated device arrays.  With
- * nQ = ceil(S/Bq), nK = ceil(S/Bk) and U = number of distinct descriptors:
+ * nQ = ceil(S/Bq), nK = ceil(S/Bk) for the executed length S of the layout
+ * (vsa_seq_len) and U = number of distinct descriptors:
  *   cls       uint8 [U][nQ][nK]  tile class (may be NULL: not written)
  *   n_full    int32 [U][nQ]      number of FULL key tiles of each query tile
  *   n_bnd     int32 [U][nQ]      number of BOUNDARY key tiles
@@ -152,9 +155,13 @@ typedef struct {
 vsa_status vsa_unique_masks(const vsa_mask_desc* masks, int32_t H, int32_t* head_map,
                             int32_t* n_unique);
 
-/* nQ = ceil(S/Bq), nK = ceil(S/Bk) for the grid. */
+/* nQ = ceil(S/Bq), nK = ceil(S/Bk) for S = T*Hg*Wg (every layout but TILE_PADDED). */
 vsa_status vsa_tile_counts(const vsa_grid* grid, int32_t Bq, int32_t Bk, int32_t* nQ,
                            int32_t* nK);
+
+/* Executed sequence length of a layout: T*Hg*Wg, or T'*H'*W' for VSA_LAYOUT_TILE_PADDED.
+ * Tile lists of that layout have nQ = ceil(S/Bq), nK = ceil(S/Bk). */
+vsa_status vsa_seq_len(const vsa_grid* grid, vsa_layout layout, int32_t* S);
 
 /* Tile classification -------------------------------------------------------- */
 
@@ -200,19 +207,24 @@ vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout,
 #define VSA_FWD_TILE_ALIGNED 8  /* listed BOUNDARY tiles mask only keys past S: the
                                    forward of lists from VSA_CLASSIFY_ROUND_TILES */
 
-/* Workspace bytes vsa_sparse_attn_fwd needs for these arguments: for bf16,
+/* Workspace bytes vsa_sparse_attn_fwd needs for these arguments, with S the executed
+ * length (vsa_seq_len; T*Hg*Wg except for VSA_LAYOUT_TILE_PADDED): for bf16,
  * B*H*D*S64 elements (S64 = S rounded up to a multiple of 64) that hold V
  * transposed per 64-key block to [B][H][S64/64][D][64]; with VSA_FWD_REORDER_IO,
- * 3*B*S*H*D elements of dtype more (q, k, v in each head's executed order).  f32 without VSA_FWD_REORDER_IO needs none. */
+ * 3*B*S*H*D elements of dtype more (q, k, v in each head's executed order).  f32
+ * without VSA_FWD_REORDER_IO needs none. */
 vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D,
                                    vsa_dtype dtype, int32_t flags, size_t* bytes);
 
 /* Block-sparse masked attention forward.
  *   q, k, v:  device [B][S][H][D], dtype, contiguous; position p of head h is that
- *             head's executed position (its layout) unless VSA_FWD_REORDER_IO
- *   o:        device [B][S][H][D], dtype (output; must not alias q/k/v)
+ *             head's executed position (its layout) and S the executed length
+ *             (vsa_seq_len), unless VSA_FWD_REORDER_IO: then they are frame-major and
+ *             S = T*Hg*Wg
+ *   o:        device [B][S][H][D], dtype (output; must not alias q/k/v); padding rows
+ *             of the padded layout (without the reorder) are unspecified
  *   lse:      device float [B][H][S] = m + ln(l), natural log (written only with
- *             VSA_FWD_WRITE_LSE; -inf for a row with no kept key)
+ *             VSA_FWD_WRITE_LSE; -inf for a row with no kept key; padding rows as o)
  *   grid, layout, masks[H]: as given to vsa_classify_tiles for `tiles`
  *   tiles:    lists from vsa_classify_tiles with the same grid, layout, masks, Bq, Bk
  *   Bq, Bk:   bf16: Bq in {64, 128, 256}, Bk = 64; f32: Bq in {32, 64, 128}, Bk in {32, 64}
@@ -239,7 +251,10 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
  * into its own order layouts[h] (VSA_LAYOUT_*, host array [H]):
  * inverse = 0: frame-major -> layouts[h]; inverse != 0: layouts[h] -> frame-major.
  * Tile-major heads need grid tile_* dividing T, Hg, Wg (Sliding Tile Attention
- * explainer, method section 3: tokens of a tile are contiguous); position-major heads
+ * explainer, method section 3: tokens of a tile are contiguous); TILE_PADDED (all heads
+ * or none) reads src [B][T*Hg*Wg][H][D] and writes dst [B][T'*H'*W'][H][D] with zero
+ * padding rows, and inverse reads the padded sequence and drops its padding (PSA notes,
+ * key design 2); position-major heads
  * gather each spatial position's frames (Sparse VideoGen on TPU, "arranging tokens for
  * temporal access").  H*D*element size must be a multiple of 16 bytes, and D*element
  * size too when the layouts differ.  Asynchronous on stream; the caller owns both

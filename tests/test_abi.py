@@ -46,6 +46,10 @@ def test_unique_masks_and_counts():
     assert u == 2 and hm == [0, 0, 0, 1, 1, 0]
     assert vsa.vsa_tile_counts(W.grid(21, 45, 80), 128, 64) == (591, 1182)
     assert vsa.vsa_tile_counts(W.grid(30, 48, 80), 128, 64) == (900, 1800)
+    # the padded layout: 21 x 45 x 80 with 3 x 8 x 16 tiles runs on 21 x 48 x 80
+    assert vsa.vsa_seq_len(W.grid(21, 45, 80, (3, 8, 16)), "padded") == 80640
+    assert vsa.vsa_seq_len(W.grid(21, 45, 80), "frame") == 75600
+    assert vsa.vsa_seq_len(W.grid(30, 48, 80, (6, 8, 8)), "padded") == 115200
 
 
 def test_workspace_sizes():
@@ -105,6 +109,13 @@ def _call_fwd(**over):
      -3, "workspace"),
     (dict(masks=[dict(W.mask_all(), head_layout=7), W.mask_all()]), -1, "head_layout"),
     (dict(masks=[dict(W.mask_all(), head_layout="tile"), W.mask_all()]), -1, "tile"),
+    (dict(grid=W.grid(3, 5, 7, (2, 2, 4)), layout=3, S=105), -1, "positions"),  # padded: S = 192
+    (dict(grid=W.grid(3, 5, 7, (2, 2, 4)), layout=3, S=192, ws_bytes=10), -3, "workspace"),
+    (dict(grid=W.grid(3, 5, 7, (2, 2, 4)), layout=3, S=105, flags=2, ws_bytes=10), -3, "workspace"),
+    (dict(grid=W.grid(3, 5, 7, (2, 2, 4)), layout=3, S=192, flags=2), -1, "frame-major I/O"),
+    (dict(grid=W.grid(3, 5, 7, (2, 2, 4)), layout=3, S=192,
+          masks=[W.mask_all(), W.with_head_layout(W.mask_all(), "frame")]), -1, "every head"),
+    (dict(grid=W.grid(3, 5, 7), layout=3, S=105), -1, "tile"),
     (dict(flags=2, layout=1, grid=W.grid(4, 8, 8, (2, 4, 4)), ws_bytes=1000), -3, "workspace"),
     (dict(ws=None, ws_bytes=0), -3, "workspace"),
     (dict(ws=0xA008), -1, "aligned"),
@@ -159,6 +170,10 @@ def test_profile_validation():
     st = lib.vsa_profile_heads(0x1, 0x2, 0x3, vsa.VSA_BF16, 1, 256, 2, 64, ctypes.byref(g), 0, 0x4, 8,
                                moved, 3, err, 0x5, 0.0, 0x6, 1 << 30, None)
     assert st == -2 and "call's layout" in vsa.vsa_last_error()
+    gp = _lib.make_grid(W.grid(4, 8, 8, (2, 4, 4)))
+    st = lib.vsa_profile_heads(0x1, 0x2, 0x3, vsa.VSA_BF16, 1, 256, 2, 64, ctypes.byref(gp), 3, 0x4, 8,
+                               cands, 3, err, 0x5, 0.0, 0x6, 1 << 30, None)
+    assert st == -2 and "padded" in vsa.vsa_last_error()
 
 
 def test_reorder_validation():
@@ -180,6 +195,9 @@ def test_reorder_validation():
     assert st == -2 and "D*element" in vsa.vsa_last_error()
     st = lib.vsa_reorder_heads(0x1, 0x2, vsa.VSA_BF16, 1, 4, 64, ctypes.byref(g), None, 0, None)
     assert st == -1 and "layouts" in vsa.vsa_last_error()
+    gp = _lib.make_grid(W.grid(3, 5, 7, (2, 2, 4)))
+    st = lib.vsa_reorder_heads(0x1, 0x2, vsa.VSA_BF16, 1, 4, 64, ctypes.byref(gp), I4(3, 3, 0, 3), 0, None)
+    assert st == -1 and "every head" in vsa.vsa_last_error()
 
 
 def _call_merge(n=2, o_ok=True, lse_ok=True, D=128, dtype=0, S=10, out=0x9000, misalign=False):
@@ -217,3 +235,24 @@ def test_classify_ex_validation():
     assert st == -1 and "flag" in vsa.vsa_last_error()
     st = lib.vsa_classify_tiles_ex(g, 0, arr, 1, 64, 128, vsa.VSA_CLASSIFY_ROUND_TILES, ctypes.byref(lists), None)
     assert st == -2 and "Bk <= 64" in vsa.vsa_last_error()
+
+
+def test_binding_rejects_mis_sized_outputs():
+    """The binding checks tensor shapes before any pointer reaches the library (the C
+    ABI cannot see allocation sizes): a destination shorter than the padded order is an
+    error, not a write past its end."""
+    import torch
+    g = W.grid(3, 5, 7, (2, 2, 4))  # 105 tokens, 192 positions padded
+    x = torch.zeros((1, 105, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dst must be"):
+        vsa.vsa_reorder_heads(x, g, ["padded", "padded"], dst=torch.zeros_like(x))
+    with pytest.raises(ValueError, match="padded reorder reads"):
+        vsa.vsa_reorder_heads(x, g, ["padded", "padded"], inverse=True)
+    with pytest.raises(ValueError, match="src holds"):
+        vsa.vsa_reorder_tokens(torch.zeros((1, 99, 2, 64)), W.grid(4, 5, 5, (2, 5, 5)))
+    q = torch.zeros((1, 105, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="o must be"):
+        vsa.vsa_sparse_attn_fwd(q, q, q, g, "frame", [W.mask_all()] * 2, {"Bq": 64, "Bk": 64},
+                                o=torch.zeros((1, 104, 2, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse_parts"):
+        vsa.vsa_merge_partials([q, q], [torch.zeros((1, 2, 104)), torch.zeros((1, 2, 105))])

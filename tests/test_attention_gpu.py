@@ -264,3 +264,78 @@ def test_full_config_position_major_sampled_rows(gpu_lib):
     ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
     assert_close(o[:, rows][:, :, heads], ref_o, "bf16", f"{name} position-major sampled rows")
     assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3
+
+
+def _padded_case(dtype):
+    g = W.grid(5, 6, 10, (2, 4, 4))  # padded to 6 x 8 x 12
+    masks = [W.mask_sta(3, 1, 3), W.mask_box(1, 2, 3, sink_frames=1), W.mask_stripe(1, 0, 2, 2, 1, 7)]
+    q, k, v = W.qkv(2, W.seq_len(g), len(masks), 64 if dtype == "f32" else 128, dtype, seed=31)
+    return g, masks, q, k, v
+
+
+@pytest.mark.parametrize("dtype,Bq,Bk", [("bf16", 64, 64), ("bf16", 128, 64), ("bf16", 256, 64),
+                                         ("f32", 32, 32), ("f32", 64, 64)])
+def test_padded_reorder_io(gpu_lib, dtype, Bq, Bk):
+    """Frame-major I/O attended tile-major over the padded grid (reorder inside the
+    call) equals frame-major attention: o and lse."""
+    g, masks, q, k, v = _padded_case(dtype)
+    say(f"padded reorder io {dtype} Bq={Bq} Bk={Bk}")
+    o, lse, tiles = run_attention(q, k, v, g, "padded", masks, Bq, Bk, reorder_io=True, flags=vsa.VSA_FWD_WRITE_LSE)
+    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks)
+    assert_close(o, ref_o, dtype, "padded, reorder inside")
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= (5e-3 if dtype == "bf16" else 1e-5)
+
+
+def test_padded_in_place(gpu_lib):
+    """Without the reorder flag q, k, v are already in the padded order (zero padding
+    rows from the oracle's permutation): the real rows equal the frame-major result."""
+    g, masks, q, k, v = _padded_case("bf16")
+    qp, kp, vp = (torch.from_numpy(oracle.reorder_tokens(x.float().numpy(), g, layout="padded")).to(x.dtype)
+                  for x in (q, k, v))
+    say("padded in place")
+    o, lse, _ = run_attention(qp, kp, vp, g, "padded", masks, 128, 64, flags=vsa.VSA_FWD_WRITE_LSE)
+    perm = oracle.layout_permutation(g, "padded")
+    real = perm >= 0
+    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks)
+    o = o.cpu()[:, torch.from_numpy(np.flatnonzero(real))]
+    assert_close(o, ref_o[:, perm[real]], "bf16", "padded in place")
+    assert np.abs(lse.cpu().numpy()[:, :, real] - ref_lse[:, :, perm[real]]).max() <= 5e-3
+
+
+def test_padded_tile_aligned_forward(gpu_lib):
+    """B3 rounding on the padded order, forward with VSA_FWD_TILE_ALIGNED: equals the
+    oracle's attention under the rounded mask (padding keys masked, interior too)."""
+    g, masks, q, k, v = _padded_case("bf16")
+    Bq, Bk = 128, 64
+    d = dev()
+    qp, kp, vp = (torch.from_numpy(oracle.reorder_tokens(x.float().numpy(), g, layout="padded")).to(x.dtype)
+                  for x in (q, k, v))
+    say("padded tile-aligned forward")
+    tiles = vsa.vsa_classify_tiles(g, "padded", masks, Bq, Bk, device=d, round_tiles=True)
+    o, _ = vsa.vsa_sparse_attn_fwd(qp.to(d), kp.to(d), vp.to(d), g, "padded", masks, tiles,
+                                   flags=vsa.VSA_FWD_TILE_ALIGNED)
+    torch.cuda.synchronize()
+    real = np.flatnonzero(oracle.layout_permutation(g, "padded") >= 0)
+    ref_o, _ = oracle.attention(qp, kp, vp, g, "padded", masks, rows=real, round_tiles=(Bq, Bk))
+    assert_close(o.cpu()[:, torch.from_numpy(real)], ref_o, "bf16", "padded B3")
+
+
+def test_full_config_padded_sampled_rows(gpu_lib):
+    """Sliding tiles on the padded Wan 2.1 720p latent, reorder in and out inside the
+    call (the launch configuration the benchmark times): sampled rows against the oracle."""
+    cfg = W.config("wan_sta_padded")
+    g, masks, Bq = cfg["grid"], cfg["masks"], cfg["Bq"]
+    S = W.seq_len(g)
+    say("full config wan_sta_padded")
+    q, k, v = W.qkv(cfg["B"], S, cfg["H"], cfg["D"], cfg["dtype"], seed=cfg["seed"])
+    d = dev()
+    tiles = vsa.vsa_classify_tiles(g, "padded", masks, Bq, cfg["Bk"], device=d, with_cls=False)
+    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "padded", masks, tiles,
+                                     flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    rows = sample_rows_per_tile(S, Bq, seed=5, per_tile=0, max_tiles=24)
+    heads = [0, 13, 39]
+    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
+    assert_close(o[:, rows][:, :, heads], ref_o, "bf16", "wan_sta_padded sampled rows")
+    assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3

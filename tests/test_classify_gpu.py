@@ -212,3 +212,39 @@ def test_classify_position_major_full_config(gpu_lib):
     n_frame = int(frame["n_full"][hmf[-1]].sum() + frame["n_bnd"][hmf[-1]].sum())
     say(f"temporal head executed tiles: position-major {n_pos}, frame-major {n_frame}")
     assert n_pos < n_frame / 2
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_classify_random_padded(gpu_lib, seed):
+    """Tile-major order over a grid padded up to whole tiles: classes bit-exact against
+    the oracle (padding pairs are never kept), exact and rounded."""
+    rng = np.random.default_rng(3000 + seed)
+    tile = tuple(int(x) for x in rng.integers(1, 5, 3))
+    g = W.grid(int(rng.integers(1, 8)), int(rng.integers(1, 9)), int(rng.integers(1, 12)), tile)
+    H = int(rng.integers(1, 5))
+    masks = [_random_desc(rng, "tile") for _ in range(H)]
+    Bq = int(rng.choice([1, 3, 8, 16, 32, 64, 128]))
+    Bk = int(rng.choice([1, 5, 16, 32, 64]))
+    round_tiles = seed % 3 == 1
+    say(f"classify padded seed={seed} grid={g} Bq={Bq} Bk={Bk} round={round_tiles} masks={masks}")
+    tiles = gpu_lib.vsa_classify_tiles(g, "padded", masks, Bq, Bk, device=dev(), round_tiles=round_tiles)
+    torch.cuda.synchronize()
+    hm, U = gpu_lib.vsa_unique_masks(masks)
+    for h, desc in enumerate(masks):
+        ref = oracle.classify(g, "padded", desc, Bq, Bk, round_tiles=round_tiles)
+        check_lists_against(tiles, hm[h], ref["q_tiles"], ref["cls"])
+
+
+def test_classify_padded_full_config(gpu_lib):
+    """Sliding tiles on the padded Wan 2.1 720p latent (21 x 48 x 80 for 3 x 8 x 16
+    tiles): sampled query tiles bit-exact."""
+    cfg = W.config("wan_sta_padded")
+    g, Bq, Bk = cfg["grid"], cfg["Bq"], cfg["Bk"]
+    say("classify padded full config wan_sta_padded")
+    tiles = gpu_lib.vsa_classify_tiles(g, "padded", cfg["masks"], Bq, Bk, device=dev())
+    torch.cuda.synchronize()
+    assert tiles["nQ"] == -(-80640 // Bq)
+    rng = np.random.default_rng(11)
+    qts = _sampled_q_tiles(tiles["nQ"], rng, 6)
+    ref = oracle.classify(g, "padded", cfg["masks"][0], Bq, Bk, q_tiles=qts)
+    check_lists_against(tiles, 0, qts, ref["cls"])

@@ -47,3 +47,23 @@ def test_reorder_heads_matches_permutation(gpu_lib, g, dtype, layouts, D):
         perm = torch.from_numpy(oracle.layout_permutation(g, lay))
         assert torch.equal(y[:, :, h], x[:, perm, h]), (h, lay)
     assert torch.equal(z.cpu(), x)
+
+
+@pytest.mark.parametrize("g,dtype,H,D", [
+    (W.grid(3, 5, 7, (2, 2, 4)), "bf16", 2, 64),
+    (W.grid(5, 6, 10, (2, 4, 4)), "f32", 3, 128),
+    (W.grid(21, 45, 80, (3, 8, 16)), "bf16", 4, 128),
+])
+def test_reorder_padded_matches_permutation(gpu_lib, g, dtype, H, D):
+    """Frame-major -> tile-major over the padded grid (zero padding rows) and back."""
+    S = W.seq_len(g)
+    say(f"reorder padded grid={g} {dtype} H={H} D={D}")
+    x = W.qkv(1, S, H, D, dtype, seed=6)[0]
+    y = gpu_lib.vsa_reorder_heads(x.to(dev()), g, ["padded"] * H)
+    z = gpu_lib.vsa_reorder_heads(y, g, ["padded"] * H, inverse=True)
+    torch.cuda.synchronize()
+    perm = oracle.layout_permutation(g, "padded")
+    assert y.shape[1] == len(perm) == oracle.seq_len(g, "padded")
+    ref = torch.from_numpy(oracle.reorder_tokens(x.float().numpy(), g, layout="padded")).to(x.dtype)
+    assert torch.equal(y.cpu(), ref)
+    assert torch.equal(z.cpu(), x)

@@ -129,6 +129,13 @@ def config(name):
         return dict(name="sta_hunyuan", seed=1003, B=1, grid=grid(30, 48, 80, (6, 8, 8)),
                     layout="tile", H=H, D=128, dtype="bf16", Bq=128, Bk=64,
                     masks=[mask_sta(3, 3, 3)] * H)
+    if name == "wan_sta_padded":
+        # sliding tiles on the Wan 2.1 720p latent: the 3 x 8 x 16 block of the PSA notes'
+        # worked example does not divide H = 45, so the grid is padded to 21 x 48 x 80
+        H = 40
+        return dict(name="wan_sta_padded", seed=1005, B=1, grid=grid(21, 45, 80, (3, 8, 16)),
+                    layout="padded", H=H, D=128, dtype="bf16", Bq=128, Bk=64,
+                    masks=[mask_sta(3, 3, 3)] * H)
     if name == "stripe_route":
         H = 40
         return dict(name="stripe_route", seed=1004, B=2, grid=grid(21, 45, 80), layout="frame",
