@@ -121,6 +121,29 @@ def kept_pairs(g, masks, B):
     return total * B
 
 
+def choose_head_layouts(vsa, g, masks, Bq, Bk, dev, orders=("frame", "position")):
+    """Per-head token order with the lowest tile cost (full tiles 1, boundary tiles 2),
+    from the GPU classifier's lists in each candidate order (a per-shape decision made
+    once, outside the timed step; the per-head flags of Sparse VideoGen on TPU, chosen
+    by cost)."""
+    cost = []
+    for order in orders:
+        om = [dict(m, head_layout=order) for m in masks]
+        t = vsa.vsa_classify_tiles(g, "frame", om, Bq, Bk, device=dev, with_cls=False)
+        hm, _ = vsa.vsa_unique_masks(om)
+        per_head = [0] * len(masks)
+        # a boundary tile costs about twice a full one (element mask, run arithmetic)
+        nt = (t["n_full"] + 2 * t["n_bnd"]).sum(dim=1).cpu().tolist()
+        for h in range(len(masks)):
+            per_head[h] = nt[hm[h]]
+        cost.append(per_head)
+    out = []
+    for h, m in enumerate(masks):
+        best = min(range(len(orders)), key=lambda i: cost[i][h])
+        out.append(dict(m, head_layout=orders[best]) if orders[best] != "frame" else m)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
@@ -188,6 +211,9 @@ def main():
     ap.add_argument("--temporal-layout", choices=("frame", "position"), default="frame",
                     help="executed order of the temporal heads of wan_mixed: position = each spatial "
                          "position's frames contiguous, reordered inside the call (frame-major I/O)")
+    ap.add_argument("--head-layouts", choices=("workload", "auto"), default="workload",
+                    help="auto: give every head the order (frame- or position-major) in which the "
+                         "classifier lists the fewest executed tiles; q/k/v/o stay frame-major")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the comparison runs (all-keep dense; position-major temporal heads)")
@@ -232,6 +258,11 @@ def main():
     S = W.seq_len(g)
     Bq = args.Bq or cfg["Bq"]
     Bk = cfg["Bk"]
+    if args.head_layouts == "auto":
+        if layout != "frame":
+            print(f"--head-layouts auto needs a frame-major workload, not {args.config}", file=sys.stderr)
+            return 2
+        masks = choose_head_layouts(vsa, g, masks, Bq, Bk, dev)
     head_lays = W.head_layouts(masks, layout)
     reorder = any(x != "frame" for x in head_lays)
     flags = args.flags | (vsa.VSA_FWD_REORDER_IO if reorder else 0) | (vsa.VSA_FWD_TILE_ALIGNED if args.round_tiles else 0)

@@ -460,6 +460,8 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     run(Frame{}, Stripe{});
   else if (m_head.layout == VSA_LAYOUT_POSITION_MAJOR && m_head.kind == VSA_MASK_BOX)
     run(Position{}, Box{});
+  else if (m_head.layout == VSA_LAYOUT_POSITION_MAJOR && m_head.kind == VSA_MASK_STRIPE)
+    run(Position{}, Stripe{});
   else
     run(AnyOrder{}, Any{});
 }

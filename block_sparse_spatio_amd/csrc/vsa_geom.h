@@ -361,13 +361,23 @@ VSA_HD int tile_class(const Geom& g, const DevMask& m, const Box* R, int nr, con
 struct QueryPos {
   int t, y, x, s;     // coordinates, s = y*Wg + x
   int st, sh, sw;     // STA window starts (tile coordinates)
+  uint64_t tkeep;     // stripe masks with T <= 64: bit t set iff key frame t passes the
+                      // temporal stripe test for this query
 };
+
+// The temporal stripe test of key frame t for query frame tq.
+VSA_HD bool stripe_frame_kept(const DevMask& m, int t, int tq) { return (iabs(t - tq - m.To) % m.Ts) < m.Tw; }
 
 VSA_HD QueryPos make_query(const Geom& g, const DevMask& m, int p) {
   QueryPos q;
   pos_coords(g, p, q.t, q.y, q.x);
   q.s = q.y * g.Wg + q.x;
   q.st = q.sh = q.sw = 0;
+  q.tkeep = 0;
+  if (m.kind == VSA_MASK_STRIPE && g.T <= 64) {
+    for (int t = 0; t < g.T; ++t)
+      if (stripe_frame_kept(m, t, q.t)) q.tkeep |= 1ull << t;
+  }
   if (m.kind == VSA_MASK_STA) {
     q.st = sta_start(q.t / g.bt, m.wt, g.nT);
     q.sh = sta_start(q.y / g.bh, m.wh, g.nH);
@@ -419,7 +429,7 @@ VSA_HD uint64_t run_mask(const Geom& g, const DevMask& m, const QueryPos& q, int
       return lo <= hi ? bit_range(off + lo - x0, off + hi - x0) : 0;
     }
     case VSA_MASK_STRIPE: {
-      if ((iabs(t - q.t - m.To) % m.Ts) >= m.Tw) return 0;
+      if (g.T <= 64 ? !((q.tkeep >> t) & 1) : !stripe_frame_kept(m, t, q.t)) return 0;
       // u = s_k - s_q - So over the run; kept where (|u| mod Ss) < Sw
       const int ubase = y * g.Wg - q.s - m.So;  // u = x + ubase
       return periodic_bits(x0 + ubase, x1 + ubase, m.Ss, m.Sw, off);
@@ -459,7 +469,10 @@ VSA_HD uint64_t run_mask_t(const Geom& g, const DevMask& m, const QueryPos& q, i
       return lo <= hi ? bits | bit_range(off + lo - t0, off + hi - t0) : bits;
     }
     case VSA_MASK_STRIPE: {
-      if ((iabs(y * g.Wg + x - q.s - m.So) % m.Ss) >= m.Sw) return bits;
+      const int ds = iabs(y * g.Wg + x - q.s - m.So);
+      if ((ds < m.Ss ? ds : ds % m.Ss) >= m.Sw) return bits;
+      if (g.T <= 64)  // frames t0 .. t1 of the precomputed temporal test
+        return bits | (((q.tkeep >> t0) & (~0ull >> (63 - (t1 - t0)))) << off);
       // v = t_k - t_q - To over the run; kept where (|v| mod Ts) < Tw
       const int vbase = -q.t - m.To;
       return bits | periodic_bits(t0 + vbase, t1 + vbase, m.Ts, m.Tw, off);
