@@ -119,14 +119,12 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   // K tile: row R of LDS holds key swap_bits23(R), 16-byte chunks swizzled by ksw(R).
   // V^T tile (one contiguous D x 64 block in global memory): row d of LDS holds channel d
   // (64 keys, 128 bytes), chunks swizzled by vtsw(d).
-  int dma_k[C::NI], dma_v[C::NI], krow[C::NI], kcol[C::NI];
+  int dma_k[C::NI], dma_v[C::NI];
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
     const int R = (wave * C::NI + i) * C::ROWS_PER_DMA + lane / C::CH;
     const int p = lane % C::CH;
-    krow[i] = swap_bits23(R);
-    kcol[i] = (p ^ ksw<D, NW>(R)) * 8;
-    dma_k[i] = 2 * (krow[i] * tok_stride + kcol[i]);  // bytes
+    dma_k[i] = 2 * (swap_bits23(R) * tok_stride + (p ^ ksw<D, NW>(R)) * 8);  // bytes
     const int d = (wave * C::NI + i) * 8 + lane / 8;                // 8 V^T rows per DMA
     dma_v[i] = 2 * (d * BK + (((lane % 8) ^ vtsw(d)) * 8));
   }
@@ -261,11 +259,18 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     const uint32_t kl0 = lds_addr(k_fill + wave * C::NI * 1024);
     const uint32_t vl0 = lds_addr(v_fill + wave * C::NI * 1024);
     int koff[C::NI];  // tail tile: rows past S read row S-1 (masked keys, finite data)
-    {
-      const bool tail = ktf * BK + BK > S;
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) koff[i] = dma_k[i];
+    if (__builtin_expect(ktf * BK + BK > S, 0)) {
+      // a real branch (the empty asm cannot be executed speculatively), so that the
+      // other steps do not pay for the clamped offsets of the one tail tile
+      asm volatile("");
       const int lim = S - 1 - ktf * BK;
 #pragma unroll
-      for (int i = 0; i < C::NI; ++i) koff[i] = tail ? 2 * (imin(krow[i], lim) * tok_stride + kcol[i]) : dma_k[i];
+      for (int i = 0; i < C::NI; ++i) {
+        const int R = (wave * C::NI + i) * C::ROWS_PER_DMA + lane / C::CH;
+        koff[i] = 2 * (imin(swap_bits23(R), lim) * tok_stride + ((lane % C::CH) ^ ksw<D, NW>(R)) * 8);
+      }
     }
     uint32_t w_next = ~0u;
     if constexpr (NEXT_BND) w_next = mask_word(kt1);
