@@ -52,8 +52,9 @@ vsa_status check_grid(const vsa_grid* g, vsa_layout layout, bool need_tile, long
     return fail(VSA_ERR_INVALID_ARG, "unknown layout %d", (int)layout);
   if (g->tile_t < 0 || g->tile_h < 0 || g->tile_w < 0)
     return fail(VSA_ERR_INVALID_ARG, "negative tile size");
-  const bool tile_set = g->tile_t > 0 || g->tile_h > 0 || g->tile_w > 0;
-  if (layout == VSA_LAYOUT_TILE_MAJOR || layout == VSA_LAYOUT_TILE_PADDED || need_tile || tile_set) {
+  // the tile matters only to tile-major orders and sliding-tile masks; elsewhere it is
+  // ignored
+  if (layout == VSA_LAYOUT_TILE_MAJOR || layout == VSA_LAYOUT_TILE_PADDED || need_tile) {
     if (g->tile_t <= 0 || g->tile_h <= 0 || g->tile_w <= 0)
       return fail(VSA_ERR_INVALID_ARG, "tile-major layouts and sliding-tile masks need tile_t/h/w > 0");
     if (layout == VSA_LAYOUT_TILE_PADDED) {  // each axis is padded up to whole tiles

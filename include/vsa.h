@@ -76,8 +76,9 @@ typedef enum {
   VSA_LAYOUT_TILE_PADDED = 3
 } vsa_layout;
 
-/* Latent grid.  S = T*Hg*Wg.  tile_* is the 3D token tile used by TILE_MAJOR and by
- * STA masks (0 when unused). */
+/* Latent grid.  S = T*Hg*Wg.  tile_* is the 3D token tile used by the tile-major orders
+ * and by STA masks (0 when unused; ignored by calls that use neither).  TILE_MAJOR and
+ * STA masks in the other orders need it to divide T, Hg, Wg; TILE_PADDED does not. */
 typedef struct {
   int32_t T, Hg, Wg;
   int32_t tile_t, tile_h, tile_w;
