@@ -64,15 +64,21 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
       c = tile_class(g, m, R, nr, C, nc, padded);
       if (round_tiles && c == VSA_TILE_BOUNDARY) {
         // tile-aligned rounding: keep the tile's real pairs iff at least half are kept
-        // (per-row popcounts of the exact row masks; Bk <= 64)
+        // kept pairs: summed over box pairs where the predicate is a product over the
+        // axes, else per-row popcounts of the exact row masks (Bk <= 64)
         long long kept = 0, k_real = 0;
-        for (int r = r0; r < r1; ++r) {
-          if (g.padded) {  // padding query rows hold no pair
-            int t, y, x;
-            pos_coords(g, r, t, y, x);
-            if (t >= g.T || y >= g.Hg || x >= g.Wg) continue;
+        bool by_boxes = m.kind != VSA_MASK_STRIPE;
+        for (int i = 0; by_boxes && i < nr; ++i)
+          for (int j = 0; j < nc; ++j) kept += box_pair_kept(g, m, R[i], C[j]);
+        if (!by_boxes) {
+          for (int r = r0; r < r1; ++r) {
+            if (g.padded) {  // padding query rows hold no pair
+              int t, y, x;
+              pos_coords(g, r, t, y, x);
+              if (t >= g.T || y >= g.Hg || x >= g.Wg) continue;
+            }
+            kept += __popcll(tile_row_mask(g, m, make_query(g, m, r), c0, c1 - c0));
           }
-          kept += __popcll(tile_row_mask(g, m, make_query(g, m, r), c0, c1 - c0));
         }
         for (int j = 0; j < nc; ++j) k_real += box_volume(C[j]);
         const long long real = q_real * k_real;

@@ -332,6 +332,51 @@ VSA_HD void box_pair_test(const Geom& g, const DevMask& m, const Box& r, const B
   }
 }
 
+// #{(a, b) : a in [a0, a1], b in [b0, b1], |b - a| <= r}; r < 0 = unbounded
+VSA_HD long long radius_pairs(int a0, int a1, int b0, int b1, int r) {
+  if (r < 0) return (long long)(a1 - a0 + 1) * (b1 - b0 + 1);
+  long long n = 0;
+  for (int a = a0; a <= a1; ++a) n += imax(0, imin(b1, a + r) - imax(b0, a - r) + 1);
+  return n;
+}
+
+// #{(a, b) : a in [a0, a1], b in [b0, b1], b's tile inside the sliding window of a's}
+VSA_HD long long window_pairs(int a0, int a1, int b0, int b1, int bsz, int w, int n) {
+  long long cnt = 0;
+  for (int a = a0; a <= a1; ++a) {
+    const int s = sta_start(a / bsz, w, n);
+    cnt += imax(0, imin(b1, (s + w) * bsz - 1) - imax(b0, s * bsz) + 1);
+  }
+  return cnt;
+}
+
+// Kept pairs of query box r x key box c (sink included) for the kinds whose predicate
+// is a product over the three axes (ALL, BOX, STA); -1 for the others.
+VSA_HD long long box_pair_kept(const Geom& g, const DevMask& m, const Box& r, Box c) {
+  if (m.kind == VSA_MASK_STRIPE) return -1;
+  const long long nq = box_volume(r);
+  long long kept = 0;
+  if (c.t0 < m.sink) {  // key frames below the sink: every pair kept
+    const int t1 = imin(c.t1, m.sink - 1);
+    kept += nq * (long long)(t1 - c.t0 + 1) * (c.y1 - c.y0 + 1) * (c.x1 - c.x0 + 1);
+    if (t1 == c.t1) return kept;
+    c.t0 = t1 + 1;
+  }
+  switch (m.kind) {
+    case VSA_MASK_ALL:
+      return kept + nq * box_volume(c);
+    case VSA_MASK_BOX:
+      return kept + radius_pairs(r.t0, r.t1, c.t0, c.t1, m.rt) * radius_pairs(r.y0, r.y1, c.y0, c.y1, m.rh) *
+                        radius_pairs(r.x0, r.x1, c.x0, c.x1, m.rw);
+    case VSA_MASK_STA:
+      return kept + window_pairs(r.t0, r.t1, c.t0, c.t1, g.bt, m.wt, g.nT) *
+                        window_pairs(r.y0, r.y1, c.y0, c.y1, g.bh, m.wh, g.nH) *
+                        window_pairs(r.x0, r.x1, c.x0, c.x1, g.bw, m.ww, g.nW);
+    default:
+      return -1;
+  }
+}
+
 // Tile class of query boxes R[nr] x key boxes C[nc] (padded: the tile reaches past S).
 VSA_HD int tile_class(const Geom& g, const DevMask& m, const Box* R, int nr, const Box* C, int nc,
                       bool padded) {
