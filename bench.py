@@ -1,8 +1,9 @@
 """Benchmark of the block-sparse video attention hot path on one MI355X.
 
 One step = one pass of the path over one batch of synthetic input: tile
-classification of the layer's masks (vsa_classify_tiles) followed by the sparse
-attention forward (vsa_sparse_attn_fwd).  The default workload is the Wan-2.1-14B
+classification of the layer's masks (vsa_classify_tiles), the element masks of the
+listed boundary tiles (vsa_boundary_words, bf16 unless --no-mask-words), and the
+sparse attention forward that reads them (vsa_sparse_attn_fwd_ex).  The default workload is the Wan-2.1-14B
 720p-shaped mixed-head layer (21 x 45 x 80 = 75,600 tokens, 40 heads, d = 128,
 bf16, heads 0-19 spatial and 20-39 temporal with a frame-0 sink, tiles 128 x 64).
 
@@ -214,6 +215,9 @@ def main():
     ap.add_argument("--head-layouts", choices=("workload", "auto"), default="workload",
                     help="auto: give every head the order (frame- or position-major) in which the "
                          "classifier lists the fewest executed tiles; q/k/v/o stay frame-major")
+    ap.add_argument("--no-mask-words", action="store_true",
+                    help="let the forward derive the boundary tiles' element masks itself instead of "
+                         "precomputing them in the step (vsa_boundary_words)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the comparison runs (all-keep dense; position-major temporal heads)")
@@ -278,6 +282,13 @@ def main():
                                            flags)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream(dev)
+    # the boundary tiles' element masks, computed in every step; the table holds every
+    # key tile per list row (cap = nK), so the step needs no host read of the lists
+    use_words = cfg["dtype"] == "bf16" and not args.round_tiles and not args.no_mask_words
+    words = None
+    if use_words:
+        words = {"words": torch.empty((tiles["n_unique"], tiles["nQ"], tiles["nK"], Bq // 32, 64), dtype=torch.int32,
+                                      device=dev), "cap": tiles["nK"]}
 
     # the sampled-query profiler is part of the step when the workload routes heads
     profile = "candidates" in cfg
@@ -296,14 +307,19 @@ def main():
         vsa.vsa_classify_tiles(g, layout, masks, Bq, Bk, out=tiles, stream=stream, round_tiles=args.round_tiles)
         if ev is not None:
             ev[1].record(stream)
-        vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles, flags=flags, o=o, workspace=ws, stream=stream)
+        if use_words:
+            vsa.vsa_boundary_words(g, layout, masks, tiles, cap=words["cap"], out=words["words"], stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+        vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles, flags=flags, o=o, workspace=ws, stream=stream,
+                                words=words)
         if ev is not None:
             ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -316,7 +332,8 @@ def main():
     ms_step = total_ms / args.steps
     prof_ms = [e[0].elapsed_time(e[3]) for e in evs]
     cls_ms = [e[3].elapsed_time(e[1]) for e in evs]
-    fwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    words_ms = [e[1].elapsed_time(e[4]) for e in evs]
+    fwd_ms = [e[4].elapsed_time(e[2]) for e in evs]
     attn_ms = float(np.mean(fwd_ms))
 
     f_exec = 4.0 * D * executed_pairs(tiles, head_map, B, S_exec)
@@ -375,11 +392,18 @@ def main():
         pm_flags = flags | vsa.VSA_FWD_REORDER_IO
         pm_ws = torch.empty(vsa.vsa_fwd_workspace_bytes(B, S, H, D, vsa.VSA_BF16, pm_flags), dtype=torch.uint8,
                             device=dev)
+        pm_words = None
+        if use_words:
+            pm_words = {"words": torch.empty((pm_tiles["n_unique"], pm_tiles["nQ"], pm_tiles["nK"], Bq // 32, 64),
+                                             dtype=torch.int32, device=dev), "cap": pm_tiles["nK"]}
 
         def pm_step():
             vsa.vsa_classify_tiles(g, layout, pm, Bq, Bk, out=pm_tiles, stream=stream)
+            if use_words:
+                vsa.vsa_boundary_words(g, layout, pm, pm_tiles, cap=pm_words["cap"], out=pm_words["words"],
+                                       stream=stream)
             vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, pm, pm_tiles, flags=pm_flags, o=o, workspace=pm_ws,
-                                    stream=stream)
+                                    stream=stream, words=pm_words)
 
         for _ in range(2):
             pm_step()
@@ -397,7 +421,7 @@ def main():
             "ms_per_step": round(pm_ms, 4), "speedup_vs_frame_major": round(ms_step / pm_ms, 3),
             "executed_tflop": round(pm_exec / 1e12, 3),
             "note": "heads 20-39 attended in position-major order, q/k/v/o reordered inside the call"}
-        del pm_tiles, pm_ws
+        del pm_tiles, pm_ws, pm_words
 
     # merging two partial results of this shape (LSE merge): HBM GB/s of the
     # algorithmic traffic (2 parts read + 1 output written, with their LSE rows)
@@ -441,6 +465,9 @@ def main():
         "attn_ms_per_call": round(attn_ms, 4),
         "attn_ms_p10_p90": [round(float(np.percentile(fwd_ms, 10)), 4), round(float(np.percentile(fwd_ms, 90)), 4)],
         "classify_ms": round(float(np.mean(cls_ms)), 4),
+        "mask_words": use_words,
+        "mask_words_ms": round(float(np.mean(words_ms)), 4) if use_words else None,
+        "mask_words_table_mib": round(words["words"].numel() * 4 / 2**20, 1) if use_words else None,
         "boundary_tile_frac": round(n_bnd_tiles / max(1, n_full_tiles + n_bnd_tiles), 5),
         **extra,
         "tflops_executed_attn": round(achieved, 2),

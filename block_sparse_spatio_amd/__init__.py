@@ -10,6 +10,6 @@ from ._lib import (  # noqa: F401
     VSA_HEAD_LAYOUT_FRAME, VSA_HEAD_LAYOUT_TILE, VSA_HEAD_LAYOUT_POSITION, VSA_TILE_BOUNDARY, VSA_TILE_EMPTY, VSA_TILE_FULL,
     LIB_PATH, VsaError, alloc_tile_lists, default_scale, load, make_grid, make_masks,
     vsa_classify_tiles, vsa_fwd_workspace_bytes, vsa_last_error, vsa_profile_heads,
-    vsa_profile_workspace_bytes, vsa_reorder_tokens, vsa_sparse_attn_fwd, vsa_tile_counts,
+    vsa_profile_workspace_bytes, vsa_reorder_tokens, vsa_sparse_attn_fwd, vsa_tile_counts, vsa_boundary_words,
     vsa_merge_partials, vsa_reorder_heads, vsa_seq_len, vsa_unique_masks,
 )

@@ -70,6 +70,11 @@ _SIGNATURES = {
     "vsa_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I,
                                  ctypes.POINTER(vsa_mask_desc), ctypes.POINTER(vsa_tile_lists), _I, _I,
                                  ctypes.c_float, _I, _P, ctypes.c_size_t, _P]),
+    "vsa_sparse_attn_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I,
+                                    ctypes.POINTER(vsa_mask_desc), ctypes.POINTER(vsa_tile_lists), _I, _I,
+                                    ctypes.c_float, _I, _P, _I, _P, ctypes.c_size_t, _P]),
+    "vsa_boundary_words": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(vsa_mask_desc), _I, _I, _I,
+                                ctypes.POINTER(vsa_tile_lists), _P, _I, _P]),
     "vsa_reorder_tokens": (_I, [_P, _P, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I, _P]),
     "vsa_reorder_heads": (_I, [_P, _P, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), ctypes.POINTER(_I), _I, _P]),
     "vsa_merge_partials": (_I, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -218,10 +223,29 @@ def vsa_fwd_workspace_bytes(B, S, H, D, dtype, flags):
     return n.value
 
 
+def vsa_boundary_words(grid, layout, masks, tiles, cap=None, out=None, stream=None):
+    """Element masks of the listed boundary tiles for the bf16 forward.  cap: entries per
+    list row (default: every key tile, so no list row is cut short).  Returns
+    {"words": int32 [U, nQ, cap, Bq/32, 64] device tensor (uint32 bit patterns), "cap": cap}."""
+    U, nQ, nK, Bq = tiles["n_unique"], tiles["nQ"], tiles["nK"], tiles["Bq"]
+    cap = nK if cap is None else int(cap)
+    shape = (U, nQ, cap, Bq // 32, 64)
+    dev = tiles["n_bnd"].device
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=dev)
+    if tuple(out.shape) != shape or out.dtype != torch.int32 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous int32 tensor of shape {shape}")
+    st = _lists_struct(tiles)
+    _check(load().vsa_boundary_words(ctypes.byref(make_grid(grid)), _layout(layout), make_masks(masks), len(masks),
+                                     Bq, tiles["Bk"], ctypes.byref(st), _ptr(out), cap, _stream(stream, dev)))
+    return {"words": out, "cap": cap}
+
+
 def vsa_sparse_attn_fwd(q, k, v, grid, layout, masks, tiles, scale=0.0, flags=0, o=None, lse=None,
-                        workspace=None, stream=None):
+                        workspace=None, stream=None, words=None):
     """Block-sparse attention forward; q, k, v contiguous [B, S, H, D] on one device (S the
-    executed length, or T*Hg*Wg with VSA_FWD_REORDER_IO).
+    executed length, or T*Hg*Wg with VSA_FWD_REORDER_IO).  words: the result of
+    vsa_boundary_words for these lists (bf16 only; vsa_sparse_attn_fwd_ex).
     Returns (o, lse) with lse None unless VSA_FWD_WRITE_LSE is in flags."""
     for t in (q, k, v):
         if not t.is_contiguous():
@@ -244,10 +268,19 @@ def vsa_sparse_attn_fwd(q, k, v, grid, layout, masks, tiles, scale=0.0, flags=0,
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lists_struct(tiles)
-    _check(load().vsa_sparse_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dt, B, S, H, D, ctypes.byref(make_grid(grid)),
-        _layout(layout), make_masks(masks), ctypes.byref(st), tiles["Bq"], tiles["Bk"], float(scale),
-        flags, _ptr(workspace), ws_bytes, _stream(stream, q.device)))
+    if words is None:
+        _check(load().vsa_sparse_attn_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dt, B, S, H, D, ctypes.byref(make_grid(grid)),
+            _layout(layout), make_masks(masks), ctypes.byref(st), tiles["Bq"], tiles["Bk"], float(scale),
+            flags, _ptr(workspace), ws_bytes, _stream(stream, q.device)))
+    else:
+        w = words["words"]
+        if tuple(w.shape) != (tiles["n_unique"], tiles["nQ"], words["cap"], tiles["Bq"] // 32, 64):
+            raise ValueError("words do not match the tile lists")
+        _check(load().vsa_sparse_attn_fwd_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dt, B, S, H, D, ctypes.byref(make_grid(grid)),
+            _layout(layout), make_masks(masks), ctypes.byref(st), tiles["Bq"], tiles["Bk"], float(scale),
+            flags, _ptr(w), words["cap"], _ptr(workspace), ws_bytes, _stream(stream, q.device)))
     return o, (lse if flags & VSA_FWD_WRITE_LSE else None)
 
 

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libvsa.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["vsa_api.hip", "classify.hip", "attn_bf16.hip", "attn_f32.hip", "reorder.hip", "profile.hip",
+SOURCES = ["vsa_api.hip", "classify.hip", "attn_bf16.hip", "attn_f32.hip", "reorder.hip", "profile.hip", "words.hip",
            "transpose.hip", "merge.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -52,6 +52,10 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   __shared__ __attribute__((aligned(1024))) char kbuf1[C::TILE_B];
   __shared__ __attribute__((aligned(1024))) char vbuf0[C::TILE_B];
   __shared__ __attribute__((aligned(1024))) char vbuf1[C::TILE_B];
+  // precomputed mask words of the boundary tile whose K is in kbuf0 / kbuf1 (one
+  // 32-bit word per lane and wave), moved by the same DMA path as K
+  __shared__ __attribute__((aligned(256))) char mbuf0[NW * 256];
+  __shared__ __attribute__((aligned(256))) char mbuf1[NW * 256];
 
   const int S = a.S, H = a.H;
   const int Bq = 32 * NW;
@@ -135,6 +139,14 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 #pragma unroll
   for (int j = 0; j < 4; ++j) vofs[j] = l32 * (BK * 2) + (((2 * j + g2) ^ vtsw(l32)) * 16);
 
+  // list entry it of a boundary tile with precomputed words (uniform); its words
+  const uint32_t* words_row = a.words ? a.words + (lrow * a.words_cap) * (NW * 64) : nullptr;
+  auto has_words = [&](int it) -> bool {
+    return words_row != nullptr && !a.pad_only && it >= nf && it < n_tiles && it - nf < a.words_cap;
+  };
+  auto issue_words = [&](int it, char* mb) __attribute__((always_inline)) {
+    dma4(words_row + (size_t)(it - nf) * (NW * 64) + wave * 64, 4u * (uint32_t)lane, lds_addr(mb + wave * 256));
+  };
   auto tile_of = [&](int it) -> int {
     return imin(imax(it < nf ? full_list[it] : bnd_list[it - nf], 0), a.nK - 1);
   };
@@ -273,7 +285,12 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
       }
     }
     uint32_t w_next = ~0u;
-    if constexpr (NEXT_BND) w_next = mask_word(kt1);
+    if constexpr (NEXT_BND) {
+      if (has_words(it + 1))  // landed with K(it+1) before this step's barrier
+        w_next = *(const uint32_t*)((P == 0 ? mbuf1 : mbuf0) + wave * 256 + 4 * lane);
+      else
+        w_next = mask_word(kt1);
+    }
 
     // running max with lazy rescaling
     const bool grow = mt_cur > m_run + lazy;
@@ -312,6 +329,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
         if (i % (NQK / C::NI) == 0) {
           const int d = i / (NQK / C::NI);
           dma16(ksrc, koff[d], kl0 + d * 1024);
+          if (d == 0 && has_words(it + 2)) issue_words(it + 2, P == 0 ? mbuf0 : mbuf1);
         }
 #pragma unroll
         for (int e = 0; e < EA; e += 2) {
@@ -390,12 +408,15 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     kt1 = n_tiles > 1 ? tile_of(1) : 0;
     kt2 = n_tiles > 2 ? tile_of(2) : 0;
     issue(kt0, kbuf0, false);
+    if (has_words(0)) issue_words(0, mbuf0);
     wait_vmcnt<0>();
     barrier_lds();
     if (n_tiles > 1) issue(kt1, kbuf1, false);
+    if (has_words(1)) issue_words(1, mbuf1);
     issue(kt0, vbuf0, true);
     qk(kbuf0, s_cur);
-    if (n_full_path == 0) apply_mask(s_cur, mask_word(kt0));
+    if (n_full_path == 0)
+      apply_mask(s_cur, has_words(0) ? *(const uint32_t*)(mbuf0 + wave * 256 + 4 * lane) : mask_word(kt0));
     mt_cur = row_max(s_cur);
   }
   // steps [0, n_full_path - 1) are followed by a full tile, steps up to n_tiles - 2 by

@@ -73,6 +73,11 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
 
+// The same for 4 bytes per lane (global_load_lds_dword): LDS at m0 + 4*lane.
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (whose release fence
 // would also wait for every DMA in flight).  LDS reads issued before it are complete
 // (lgkmcnt(0)); DMA completion is waited for explicitly with wait_vmcnt.

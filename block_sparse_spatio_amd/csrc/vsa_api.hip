@@ -276,6 +276,33 @@ vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout, const 
   return ok();
 }
 
+vsa_status vsa_boundary_words(const vsa_grid* grid, vsa_layout layout, const vsa_mask_desc* masks, int32_t H,
+                              int32_t Bq, int32_t Bk, const vsa_tile_lists* tiles, uint32_t* words, int32_t cap,
+                              void* stream) {
+  long long S;
+  vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && needs_tile(masks, H), &S);
+  if (st != VSA_OK) return st;
+  if ((Bq != 64 && Bq != 128 && Bq != 256) || Bk != 64)
+    return fail(VSA_ERR_UNSUPPORTED, "mask words for tiles Bq=%d Bk=%d (supported: Bq 64/128/256, Bk 64)", Bq, Bk);
+  if (!tiles || !tiles->n_bnd || !tiles->bnd_idx)
+    return fail(VSA_ERR_INVALID_ARG, "tile lists (n_bnd, bnd_idx) must be non-NULL");
+  if (cap < 0) return fail(VSA_ERR_INVALID_ARG, "cap=%d is negative", cap);
+  if (cap > 0 && !words) return fail(VSA_ERR_INVALID_ARG, "words is NULL");
+  if (((uintptr_t)words & 15)) return fail(VSA_ERR_INVALID_ARG, "words must be 16-byte aligned");
+  vsa::MaskTable table;
+  vsa::HeadMap hm;
+  int32_t U = 0;
+  st = build_table(masks, H, grid, layout, &table, &hm, &U);
+  if (st != VSA_OK) return st;
+  S = exec_len(grid, layout);
+  const int32_t nQ = (int32_t)((S + Bq - 1) / Bq), nK = (int32_t)((S + Bk - 1) / Bk);
+  if (cap > nK) return fail(VSA_ERR_INVALID_ARG, "cap=%d above the %d key tiles", cap, nK);
+  hipError_t e = vsa::launch_boundary_words(make_geom(grid, layout), table, U, Bq, nQ, nK, tiles->n_bnd,
+                                            tiles->bnd_idx, words, cap, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mask words launch");
+  return ok();
+}
+
 // bf16: V^T [B][H][D][S rounded up to 64] (the PV operand, transposed once per call);
 // with VSA_FWD_REORDER_IO, tile-major copies of q, k and v before it.
 static size_t vt_pad(int32_t S) { return ((size_t)S + 63) / 64 * 64; }
@@ -299,6 +326,15 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
                                int32_t B, int32_t S, int32_t H, int32_t D, const vsa_grid* grid, vsa_layout layout,
                                const vsa_mask_desc* masks, const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk,
                                float scale, int32_t flags, void* workspace, size_t ws_bytes, void* stream) {
+  return vsa_sparse_attn_fwd_ex(q, k, v, o, lse, dtype, B, S, H, D, grid, layout, masks, tiles, Bq, Bk, scale, flags,
+                                nullptr, 0, workspace, ws_bytes, stream);
+}
+
+vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, vsa_dtype dtype,
+                                  int32_t B, int32_t S, int32_t H, int32_t D, const vsa_grid* grid, vsa_layout layout,
+                                  const vsa_mask_desc* masks, const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk,
+                                  float scale, int32_t flags, const uint32_t* words, int32_t words_cap,
+                                  void* workspace, size_t ws_bytes, void* stream) {
   long long S_grid;
   vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && needs_tile(masks, H), &S_grid);
   if (st != VSA_OK) return st;
@@ -327,6 +363,12 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   if (!tiles || !tiles->n_full || !tiles->n_bnd || !tiles->full_idx || !tiles->bnd_idx)
     return fail(VSA_ERR_INVALID_ARG, "tile lists must be non-NULL");
   if (!isfinite(scale)) return fail(VSA_ERR_INVALID_ARG, "scale is not finite");
+  if (words_cap < 0 || (words_cap > 0 && !words) || (words && words_cap == 0))
+    return fail(VSA_ERR_INVALID_ARG, "words and words_cap must be both set or both unset (words_cap=%d)", words_cap);
+  if (words && dtype != VSA_BF16) return fail(VSA_ERR_UNSUPPORTED, "precomputed mask words are for bf16 only");
+  if (words && (flags & VSA_FWD_TILE_ALIGNED))
+    return fail(VSA_ERR_INVALID_ARG, "precomputed mask words do not apply to VSA_FWD_TILE_ALIGNED lists");
+  if (((uintptr_t)words & 15)) return fail(VSA_ERR_INVALID_ARG, "words must be 16-byte aligned");
   const bool reorder = (flags & VSA_FWD_REORDER_IO) != 0;
   const size_t eb = elem_size(dtype);
   const size_t nelem = (size_t)B * S_exec * H * D;  // one reordered tensor
@@ -367,6 +409,9 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
   a.lse = lse;
   a.n_full = tiles->n_full; a.n_bnd = tiles->n_bnd;
   a.full_idx = tiles->full_idx; a.bnd_idx = tiles->bnd_idx;
+  a.words = words;
+  a.words_cap = words ? words_cap : 0;
+  if (words_cap > a.nK) return fail(VSA_ERR_INVALID_ARG, "words_cap=%d above the %d key tiles", words_cap, a.nK);
   hipStream_t hs = (hipStream_t)stream;
   const vsa::Geom& G = a.g;
   char* ws = (char*)workspace;

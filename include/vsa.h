@@ -246,6 +246,42 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
                                float scale, int32_t flags, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* Precomputed element masks of boundary tiles (bf16 forward) ------------------- */
+
+/* The forward masks each listed BOUNDARY tile element by element (Sparse VideoGen on
+ * TPU, "avoid in-tile masking ...": only partially kept tiles pay for it).  It can
+ * derive those masks itself, or read them from a table that this call fills
+ * beforehand, which frees the forward's vector unit for the softmax.  Like the tile
+ * lists, the table depends only on the grid, the masks and the tile sizes, so one
+ * table serves every forward with the same lists.
+ *   grid, layout, masks[H], Bq, Bk, tiles: as given to vsa_classify_tiles (exact
+ *          lists, not rounded ones); Bq in {64, 128, 256}, Bk = 64
+ *   words: device uint32 [U][nQ][cap][Bq/32][64] (U unique masks, nQ = ceil(S/Bq) with
+ *          S the executed length); entry j < min(n_bnd, cap) of a list row holds the
+ *          masks of that row's j-th boundary tile; other entries are not written
+ *   cap:   entries per list row, 0..nK (a forward masks entries past cap itself)
+ * Word (w, l) of an entry belongs to query row w*32 + (l mod 32) of the query tile
+ * (rows past S use row S-1) and holds, from bit 0, whether keys 8*(l div 32) + {0..7},
+ * {16..23}, {32..39}, {48..55} of the key tile are kept.  16-byte aligned.  Asynchronous
+ * on stream; integer-exact. */
+vsa_status vsa_boundary_words(const vsa_grid* grid, vsa_layout layout,
+                              const vsa_mask_desc* masks, int32_t H, int32_t Bq,
+                              int32_t Bk, const vsa_tile_lists* tiles, uint32_t* words,
+                              int32_t cap, void* stream);
+
+/* vsa_sparse_attn_fwd reading the boundary masks of list entries j < words_cap from
+ * words (vsa_boundary_words with the same arguments and cap = words_cap); the output is
+ * identical.  words = NULL with words_cap = 0 is vsa_sparse_attn_fwd.  bf16 only, not
+ * with VSA_FWD_TILE_ALIGNED. */
+vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, vsa_dtype dtype, int32_t B, int32_t S,
+                                  int32_t H, int32_t D, const vsa_grid* grid,
+                                  vsa_layout layout, const vsa_mask_desc* masks,
+                                  const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk,
+                                  float scale, int32_t flags, const uint32_t* words,
+                                  int32_t words_cap, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
 /* Token reorder ---------------------------------------------------------------- */
 
 /* Permute the sequence axis of src [B][S][H][D] into dst (no aliasing), each head h

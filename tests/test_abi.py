@@ -237,6 +237,58 @@ def test_classify_ex_validation():
     assert st == -2 and "Bk <= 64" in vsa.vsa_last_error()
 
 
+def _call_fwd_ex(words, cap, **over):
+    lib = vsa.load()
+    g = W.grid(4, 8, 8)
+    arr = _lib.make_masks([W.mask_spatial(1), W.mask_temporal(1)])
+    args = dict(dtype=vsa.VSA_BF16, flags=0, Bq=64)
+    args.update(over)
+    lists = _lib.vsa_tile_lists(0x5000, 0x6000, 0x7000, 0x8000, 0x9000)
+    st = lib.vsa_sparse_attn_fwd_ex(0x1000, 0x2000, 0x3000, 0x4000, None, args["dtype"], 1, 256, 2, 64,
+                                    ctypes.byref(_lib.make_grid(g)), 0, arr, ctypes.byref(lists), args["Bq"], 64,
+                                    0.0, args["flags"], words, cap, 0xA000, 1 << 40, None)
+    return st, vsa.vsa_last_error()
+
+
+@pytest.mark.parametrize("words,cap,over,status,needle", [
+    (None, 3, {}, -1, "both set"),
+    (0xB000, 0, {}, -1, "both set"),
+    (0xB000, -1, {}, -1, "both set"),
+    (0xB000, 5, {}, -1, "above the 4 key tiles"),
+    (0xB004, 2, {}, -1, "aligned"),
+    (0xB000, 2, dict(dtype=vsa.VSA_F32), -2, "bf16 only"),
+    (0xB000, 2, dict(flags=vsa.VSA_FWD_TILE_ALIGNED), -1, "TILE_ALIGNED"),
+])
+def test_fwd_ex_validation(words, cap, over, status, needle):
+    st, msg = _call_fwd_ex(words, cap, **over)
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_boundary_words_validation():
+    lib = vsa.load()
+    arr = _lib.make_masks([W.mask_spatial(1), W.mask_stripe(1, 0, 2, 1, 0, 5)])
+    g = ctypes.byref(_lib.make_grid(W.grid(4, 8, 8)))
+    lists = _lib.vsa_tile_lists(0x10, 0x20, 0x30, 0x40, 0x50)
+    cases = [
+        (dict(Bk=32), -2, "Bk 64"),
+        (dict(Bq=32), -2, "Bq 64/128/256"),
+        (dict(cap=5), -1, "above the 4 key tiles"),
+        (dict(cap=-1), -1, "negative"),
+        (dict(words=None), -1, "words is NULL"),
+        (dict(words=0x1008), -1, "aligned"),
+        (dict(lists=_lib.vsa_tile_lists(0x10, 0x20, None, 0x40, 0x50)), -1, "non-NULL"),
+        (dict(grid=ctypes.byref(_lib.make_grid(W.grid(0, 8, 8)))), -1, "positive"),
+    ]
+    for over, status, needle in cases:
+        a = dict(grid=g, Bq=64, Bk=64, lists=lists, words=0x1000, cap=2)
+        a.update(over)
+        st = lib.vsa_boundary_words(a["grid"], 0, arr, 2, a["Bq"], a["Bk"], ctypes.byref(a["lists"]), a["words"],
+                                    a["cap"], None)
+        msg = vsa.vsa_last_error()
+        assert st == status and needle in msg, (over, st, msg)
+
+
 def test_binding_rejects_mis_sized_outputs():
     """The binding checks tensor shapes before any pointer reaches the library (the C
     ABI cannot see allocation sizes): a destination shorter than the padded order is an
@@ -256,3 +308,13 @@ def test_binding_rejects_mis_sized_outputs():
                                 o=torch.zeros((1, 104, 2, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="lse_parts"):
         vsa.vsa_merge_partials([q, q], [torch.zeros((1, 2, 104)), torch.zeros((1, 2, 105))])
+    tiles = {"cls": None, "n_full": torch.zeros((1, 2), dtype=torch.int32), "n_bnd": torch.zeros((1, 2), dtype=torch.int32),
+             "full_idx": torch.zeros((1, 2, 2), dtype=torch.int32), "bnd_idx": torch.zeros((1, 2, 2), dtype=torch.int32),
+             "n_unique": 1, "nQ": 2, "nK": 2, "Bq": 64, "Bk": 64}
+    with pytest.raises(ValueError, match="out must be"):
+        vsa.vsa_boundary_words(W.grid(2, 8, 8), "frame", [W.mask_all()], tiles, cap=2,
+                               out=torch.zeros((1, 2, 1, 2, 64), dtype=torch.int32))
+    q2 = torch.zeros((1, 128, 1, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="words do not match"):
+        vsa.vsa_sparse_attn_fwd(q2, q2, q2, W.grid(2, 8, 8), "frame", [W.mask_all()], tiles,
+                                words={"words": torch.zeros((1, 2, 2, 4, 64), dtype=torch.int32), "cap": 2})
