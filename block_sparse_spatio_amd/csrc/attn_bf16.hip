@@ -38,6 +38,8 @@ namespace {
 
 using namespace pipe;
 
+constexpr int kAllWords = -2;  // kind tag: every boundary mask of the workgroup comes from the word table
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const int32_t* __restrict__ n_bnd_p,
@@ -80,6 +82,8 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   auto run = [&](auto order_tag, auto kind_tag) __attribute__((always_inline)) {
   constexpr int ORDER = decltype(order_tag)::value;  // token order fixed at compile time, or -1
   constexpr int KIND = decltype(kind_tag)::value;    // mask kind fixed at compile time, or -1
+  // every boundary tile's mask comes from the word table (no mask arithmetic at all)
+  constexpr bool ALL_WORDS = KIND == kAllWords;
   DevMask m = m_head;
   if constexpr (KIND >= 0) m.kind = KIND;
   Geom g = head_geom(a.g, m);
@@ -142,6 +146,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   // list entry it of a boundary tile with precomputed words (uniform); its words
   const uint32_t* words_row = a.words ? a.words + (lrow * a.words_cap) * (NW * 64) : nullptr;
   auto has_words = [&](int it) -> bool {
+    if constexpr (ALL_WORDS) return it >= nf && it < n_tiles;
     return words_row != nullptr && !a.pad_only && it >= nf && it < n_tiles && it - nf < a.words_cap;
   };
   auto issue_words = [&](int it, char* mb) __attribute__((always_inline)) {
@@ -286,8 +291,11 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     }
     uint32_t w_next = ~0u;
     if constexpr (NEXT_BND) {
-      if (has_words(it + 1))  // landed with K(it+1) before this step's barrier
-        w_next = *(const uint32_t*)((P == 0 ? mbuf1 : mbuf0) + wave * 256 + 4 * lane);
+      // the words landed with K(it+1) before this step's barrier; when the table holds the
+      // whole boundary list, a boundary successor always has them
+      const uint32_t* w_lds = (const uint32_t*)((P == 0 ? mbuf1 : mbuf0) + wave * 256 + 4 * lane);
+      if (ALL_WORDS || has_words(it + 1))
+        w_next = *w_lds;
       else
         w_next = mask_word(kt1);
     }
@@ -415,8 +423,9 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     if (has_words(1)) issue_words(1, mbuf1);
     issue(kt0, vbuf0, true);
     qk(kbuf0, s_cur);
-    if (n_full_path == 0)
-      apply_mask(s_cur, has_words(0) ? *(const uint32_t*)(mbuf0 + wave * 256 + 4 * lane) : mask_word(kt0));
+    if (n_full_path == 0)  // tile 0 is a boundary tile (with words when the table holds the list)
+      apply_mask(s_cur, (ALL_WORDS || has_words(0)) ? *(const uint32_t*)(mbuf0 + wave * 256 + 4 * lane)
+                                                    : mask_word(kt0));
     mt_cur = row_max(s_cur);
   }
   // steps [0, n_full_path - 1) are followed by a full tile, steps up to n_tiles - 2 by
@@ -480,7 +489,13 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   using Frame = std::integral_constant<int, VSA_LAYOUT_FRAME_MAJOR>;
   using Position = std::integral_constant<int, VSA_LAYOUT_POSITION_MAJOR>;
   using AnyOrder = std::integral_constant<int, -1>;
-  if (m_head.layout == VSA_LAYOUT_FRAME_MAJOR && m_head.kind == VSA_MASK_BOX)
+  using AllWords = std::integral_constant<int, kAllWords>;
+  // a word table that holds this query tile's whole boundary list serves every order and
+  // kind (the per-workgroup choice is uniform)
+  const int nb_row = imin(imax(n_bnd_p[(size_t)slot * a.nQ + qt], 0), a.nK);
+  if (a.words && nb_row <= a.words_cap && !a.pad_only && !a.force_mask)
+    run(AnyOrder{}, AllWords{});
+  else if (m_head.layout == VSA_LAYOUT_FRAME_MAJOR && m_head.kind == VSA_MASK_BOX)
     run(Frame{}, Box{});
   else if (m_head.layout == VSA_LAYOUT_FRAME_MAJOR && m_head.kind == VSA_MASK_STRIPE)
     run(Frame{}, Stripe{});

@@ -271,8 +271,10 @@ vsa_status vsa_boundary_words(const vsa_grid* grid, vsa_layout layout,
 
 /* vsa_sparse_attn_fwd reading the boundary masks of list entries j < words_cap from
  * words (vsa_boundary_words with the same arguments and cap = words_cap); the output is
- * identical.  words = NULL with words_cap = 0 is vsa_sparse_attn_fwd.  bf16 only, not
- * with VSA_FWD_TILE_ALIGNED. */
+ * identical.  Query tiles whose boundary list fits in the table (n_bnd <= words_cap, so
+ * every list with cap = nK or cap = the longest list) run with no mask arithmetic at
+ * all; the others derive the masks of the entries past the cap.  words = NULL with
+ * words_cap = 0 is vsa_sparse_attn_fwd.  bf16 only, not with VSA_FWD_TILE_ALIGNED. */
 vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
                                   float* lse, vsa_dtype dtype, int32_t B, int32_t S,
                                   int32_t H, int32_t D, const vsa_grid* grid,

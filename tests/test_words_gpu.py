@@ -1,7 +1,7 @@
 """Precomputed element masks of boundary tiles on the GPU: the words are bit-exact
 against the oracle's keep predicate, entries past the lists are left alone, and the
 bf16 forward that reads them gives exactly the output of the forward that derives the
-masks itself (whole table, a table cut short, and the forced-mask ablation)."""
+masks itself (tables holding every list, tables cut short, and the forced-mask ablation)."""
 import numpy as np
 import pytest
 import torch
@@ -136,7 +136,9 @@ def test_forward_with_words_is_identical(gpu_lib, seed):
     tiles = vsa.vsa_classify_tiles(g, layout, masks, Bq, 64, device=dev(), with_cls=False)
     o0, l0 = vsa.vsa_sparse_attn_fwd(q, k, v, g, layout, masks, tiles, flags=flags)
     cap = max(1, int(tiles["n_bnd"].max()))
-    for c in sorted({cap, max(1, cap // 2), 1}):
+    # nK and the longest list: every workgroup's list fits (the instance without any mask
+    # arithmetic); shorter tables mix it with workgroups that derive the masks past the cap
+    for c in sorted({tiles["nK"], cap, max(1, cap // 2), 1}):
         words = _words(g, layout, masks, tiles, c)
         o1, l1 = vsa.vsa_sparse_attn_fwd(q, k, v, g, layout, masks, tiles, flags=flags, words=words)
         torch.cuda.synchronize()
@@ -165,8 +167,12 @@ def test_forward_with_words_full_config(gpu_lib, name):
     cap = max(1, int(tiles["n_bnd"].max()))
     words = vsa.vsa_boundary_words(g, layout, masks, tiles, cap=cap)
     o1, _ = vsa.vsa_sparse_attn_fwd(q, k, v, g, layout, masks, tiles, words=words)
+    del words
+    full = vsa.vsa_boundary_words(g, layout, masks, tiles)  # cap = nK
+    o2, _ = vsa.vsa_sparse_attn_fwd(q, k, v, g, layout, masks, tiles, words=full)
     torch.cuda.synchronize()
     if layout == "padded":
         real = torch.from_numpy(oracle.is_real(g, *oracle.token_coords(g, "padded", np.arange(S)))).to(dev())
-        o0, o1 = o0[:, real], o1[:, real]
+        o0, o1, o2 = o0[:, real], o1[:, real], o2[:, real]
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(o0.view(torch.int16), o2.view(torch.int16))
