@@ -122,27 +122,36 @@ def kept_pairs(g, masks, B):
     return total * B
 
 
-def choose_head_layouts(vsa, g, masks, Bq, Bk, dev, orders=("frame", "position")):
-    """Per-head token order with the lowest tile cost (full tiles 1, boundary tiles 2),
-    from the GPU classifier's lists in each candidate order (a per-shape decision made
-    once, outside the timed step; the per-head flags of Sparse VideoGen on TPU, chosen
-    by cost)."""
-    cost = []
-    for order in orders:
+def choose_head_layouts(vsa, g, masks, Bq, Bk, dev, bnd_cost=1.2):
+    """Per-head token order with the lowest tile cost, from the GPU classifier's lists in
+    each candidate order: frame-major, position-major, and tile-major over one grid tile
+    of the form (1, Hg, w) for w dividing Wg (w <= 16: a frame read w columns at a time,
+    which makes column-band stripes contiguous).  The tile that gives the lowest total
+    is kept.  A full tile costs 1 and a boundary tile bnd_cost (its masks come from the
+    word table).  A per-shape decision made once, outside the timed step (the per-head
+    flags of Sparse VideoGen on TPU, chosen by cost).  Returns (grid, masks)."""
+    def per_head(grid, order):
         om = [dict(m, head_layout=order) for m in masks]
-        t = vsa.vsa_classify_tiles(g, "frame", om, Bq, Bk, device=dev, with_cls=False)
+        t = vsa.vsa_classify_tiles(grid, "frame", om, Bq, Bk, device=dev, with_cls=False)
         hm, _ = vsa.vsa_unique_masks(om)
-        per_head = [0] * len(masks)
-        # a boundary tile costs about twice a full one (element mask, run arithmetic)
-        nt = (t["n_full"] + 2 * t["n_bnd"]).sum(dim=1).cpu().tolist()
-        for h in range(len(masks)):
-            per_head[h] = nt[hm[h]]
-        cost.append(per_head)
-    out = []
-    for h, m in enumerate(masks):
-        best = min(range(len(orders)), key=lambda i: cost[i][h])
-        out.append(dict(m, head_layout=orders[best]) if orders[best] != "frame" else m)
-    return out
+        nt = (t["n_full"].double() + bnd_cost * t["n_bnd"].double()).sum(dim=1).cpu().tolist()
+        return [nt[hm[h]] for h in range(len(masks))]
+
+    base = {"frame": per_head(g, "frame"), "position": per_head(g, "position")}
+    best_total, best = None, None
+    tiles = [None] + [(1, g["Hg"], w) for w in (1, 2, 4, 8, 16) if g["Wg"] % w == 0]
+    for tile in tiles:
+        cand = dict(base)
+        grid = g
+        if tile is not None:
+            grid = dict(g, tile_t=tile[0], tile_h=tile[1], tile_w=tile[2])
+            cand["tile"] = per_head(grid, "tile")
+        picks = [min(cand, key=lambda o: cand[o][h]) for h in range(len(masks))]
+        total = sum(cand[o][h] for h, o in enumerate(picks))
+        if best_total is None or total < best_total:
+            best_total, best = total, (grid if "tile" in picks else g, picks)
+    grid, picks = best
+    return grid, [dict(m, head_layout=o) if o != "frame" else m for m, o in zip(masks, picks)]
 
 
 # ---------------------------------------------------------------------------
@@ -213,8 +222,9 @@ def main():
                     help="executed order of the temporal heads of wan_mixed: position = each spatial "
                          "position's frames contiguous, reordered inside the call (frame-major I/O)")
     ap.add_argument("--head-layouts", choices=("workload", "auto"), default="workload",
-                    help="auto: give every head the order (frame- or position-major) in which the "
-                         "classifier lists the fewest executed tiles; q/k/v/o stay frame-major")
+                    help="auto: give every head the order (frame-, position- or tile-major over a "
+                         "(1, Hg, w) grid tile) in which the classifier's lists cost least; q/k/v/o stay "
+                         "frame-major")
     ap.add_argument("--no-mask-words", action="store_true",
                     help="let the forward derive the boundary tiles' element masks itself instead of "
                          "precomputing them in the step (vsa_boundary_words)")
@@ -266,7 +276,7 @@ def main():
         if layout != "frame":
             print(f"--head-layouts auto needs a frame-major workload, not {args.config}", file=sys.stderr)
             return 2
-        masks = choose_head_layouts(vsa, g, masks, Bq, Bk, dev)
+        g, masks = choose_head_layouts(vsa, g, masks, Bq, Bk, dev)
     head_lays = W.head_layouts(masks, layout)
     reorder = any(x != "frame" for x in head_lays)
     flags = args.flags | (vsa.VSA_FWD_REORDER_IO if reorder else 0) | (vsa.VSA_FWD_TILE_ALIGNED if args.round_tiles else 0)
@@ -461,7 +471,8 @@ def main():
         "config": {"workload": args.config, "B": B, "S": S, "H": H, "D": D, "grid": [g["T"], g["Hg"], g["Wg"]],
                    "layout": layout, "Bq": Bq, "Bk": Bk, "masks": sorted({m["kind"] for m in masks}),
                    "unique_masks": U, "flags": flags, "tile_rounding": bool(args.round_tiles),
-                   "head_layouts": {x: head_lays.count(x) for x in sorted(set(head_lays))}},
+                   "head_layouts": {x: head_lays.count(x) for x in sorted(set(head_lays))},
+                   "grid_tile": [g.get("tile_t", 0), g.get("tile_h", 0), g.get("tile_w", 0)]},
         "attn_ms_per_call": round(attn_ms, 4),
         "attn_ms_p10_p90": [round(float(np.percentile(fwd_ms, 10)), 4), round(float(np.percentile(fwd_ms, 90)), 4)],
         "classify_ms": round(float(np.mean(cls_ms)), 4),

@@ -280,6 +280,41 @@ VSA_HD bool s_contiguous(const Geom& g, const Box& b) {
   return b.y0 == b.y1 || (b.x0 == 0 && b.x1 == g.Wg - 1);
 }
 
+VSA_HD int igcd(int a, int b) {
+  while (b) { const int r = a % b; a = b; b = r; }
+  return a;
+}
+
+VSA_HD int floor_div(int a, int b) {  // b > 0
+  return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+
+// Stripe test over the spatial differences of two boxes that are not runs of s: the
+// rows dy in [dy0, dy1] each contribute the interval d = dy*Wg + [dx0, dx1] - So, kept
+// where (|d| mod Ss) < Sw.  While a row's interval lies wholly below 0, or wholly at or
+// above 0, moving dy by Ss / gcd(Wg, Ss) moves d by a multiple of Ss and repeats the
+// row's result, so each of those two ranges needs at most one period of rows; only the
+// rows whose interval contains 0 are tested one by one.
+VSA_HD void stripe_rows_test(const Geom& g, const DevMask& m, int dy0, int dy1, int dx0, int dx1, bool& all,
+                             bool& any) {
+  all = true;
+  any = false;
+  const int per = m.Ss / igcd(g.Wg, m.Ss);
+  // rows with d < 0 throughout: dy*Wg + dx1 - So < 0; rows with d >= 0 throughout:
+  // dy*Wg + dx0 - So >= 0
+  const int neg_end = imin(dy1, floor_div(m.So - dx1 - 1, g.Wg));
+  const int pos_begin = imax(dy0, -floor_div(dx0 - m.So, g.Wg));
+  auto row = [&](int dy) {
+    bool a, n;
+    periodic_test(dy * g.Wg + dx0, dy * g.Wg + dx1, m.So, m.Ss, m.Sw, a, n);
+    all = all && a;
+    any = any || n;
+  };
+  for (int dy = dy0; dy <= imin(neg_end, dy0 + per - 1); ++dy) row(dy);
+  for (int dy = imax(dy0, neg_end + 1); dy <= imin(dy1, pos_begin - 1); ++dy) row(dy);
+  for (int dy = pos_begin; dy <= imin(dy1, pos_begin + per - 1); ++dy) row(dy);
+}
+
 // all / any kept over query box r x key box c for the mask without its sink.
 VSA_HD void box_pair_test(const Geom& g, const DevMask& m, const Box& r, const Box& c, bool& all,
                           bool& any) {
@@ -305,13 +340,7 @@ VSA_HD void box_pair_test(const Geom& g, const DevMask& m, const Box& r, const B
         int sk0 = c.y0 * g.Wg + c.x0, sk1 = c.y1 * g.Wg + c.x1;
         periodic_test(sk0 - sq1, sk1 - sq0, m.So, m.Ss, m.Sw, as, ns);
       } else {
-        int dx0 = c.x0 - r.x1, dx1 = c.x1 - r.x0;
-        for (int dy = c.y0 - r.y1; dy <= c.y1 - r.y0; ++dy) {
-          bool a, n;
-          periodic_test(dy * g.Wg + dx0, dy * g.Wg + dx1, m.So, m.Ss, m.Sw, a, n);
-          as = as && a;
-          ns = ns || n;
-        }
+        stripe_rows_test(g, m, c.y0 - r.y1, c.y1 - r.y0, c.x0 - r.x1, c.x1 - r.x0, as, ns);
       }
       all = at && as;
       any = nt && ns;
@@ -533,6 +562,61 @@ VSA_HD uint64_t run_mask_t(const Geom& g, const DevMask& m, const QueryPos& q, i
   }
 }
 
+// kept keys of a column run of tile-major order over tiles one column wide (fixed t, x;
+// y in [y0, y1]; bit of y0 is off) for query q
+VSA_HD uint64_t run_mask_y(const Geom& g, const DevMask& m, const QueryPos& q, int t, int x, int y0, int y1,
+                           int off) {
+  if (g.padded) {  // padding keys are never kept
+    if (t >= g.T || x >= g.Wg || y0 >= g.Hg) return 0;
+    y1 = imin(y1, g.Hg - 1);
+  }
+  if (t < m.sink || m.kind == VSA_MASK_ALL) return bit_range(off, off + y1 - y0);
+  switch (m.kind) {
+    case VSA_MASK_BOX: {
+      if (m.rt >= 0 && iabs(t - q.t) > m.rt) return 0;
+      if (m.rw >= 0 && iabs(x - q.x) > m.rw) return 0;
+      int lo = y0, hi = y1;
+      if (m.rh >= 0) { lo = imax(lo, q.y - m.rh); hi = imin(hi, q.y + m.rh); }
+      return lo <= hi ? bit_range(off + lo - y0, off + hi - y0) : 0;
+    }
+    case VSA_MASK_STRIPE: {
+      if (g.T <= 64 ? !((q.tkeep >> t) & 1) : !stripe_frame_kept(m, t, q.t)) return 0;
+      if (m.Sw <= 0) return 0;
+      // u = s_k - s_q - So steps by Wg along the run; kept where (|u| mod Ss) < Sw.  The
+      // residue is carried from row to row (one division per sign of u).
+      uint64_t bits = 0;
+      int u = y0 * g.Wg + x - q.s - m.So;
+      const int step = g.Wg % m.Ss;
+      int y = y0;
+      if (u < 0) {
+        int r = (-u) % m.Ss;  // |u| mod Ss, |u| falling by Wg per row
+        for (; y <= y1 && u < 0; ++y, u += g.Wg) {
+          if (r < m.Sw) bits |= 1ull << (off + y - y0);
+          r -= step;
+          if (r < 0) r += m.Ss;
+        }
+      }
+      if (y <= y1) {
+        int r = u % m.Ss;  // u >= 0 from here on
+        for (; y <= y1; ++y) {
+          if (r < m.Sw) bits |= 1ull << (off + y - y0);
+          r += step;
+          if (r >= m.Ss) r -= m.Ss;
+        }
+      }
+      return bits;
+    }
+    case VSA_MASK_STA: {
+      const int at = t / g.bt, ax = x / g.bw;
+      if (at < q.st || at >= q.st + m.wt || ax < q.sw || ax >= q.sw + m.ww) return 0;
+      const int lo = imax(y0, q.sh * g.bh), hi = imin(y1, (q.sh + m.wh) * g.bh - 1);
+      return lo <= hi ? bit_range(off + lo - y0, off + hi - y0) : 0;
+    }
+    default:
+      return 0;
+  }
+}
+
 // Run cursor over executed positions: advances through maximal runs of constant
 // (t, y) with contiguous x.
 struct RunCursor {
@@ -651,6 +735,29 @@ VSA_HD uint64_t tile_row_mask_ft(const Geom& g, const DevMask& m, const QueryPos
   const int end = imin(c0 + nbits, g.S);
   uint64_t bits = 0;
   RunCursor c = run_begin(g, c0);
+  if (g.layout == VSA_LAYOUT_TILE_MAJOR && g.bw == 1 && g.bh > 1) {
+    // tiles one column wide: x is fixed inside a tile, so the runs go along y
+    while (c.p < end) {
+      const int len = imin(g.bh - c.ih, end - c.p);
+      bits |= run_mask_y(g, m, q, c.t, c.x, c.y, c.y + len - 1, c.p - c0);
+      c.p += len;
+      c.ih += len;
+      if (c.ih >= g.bh) {
+        c.ih = 0;
+        if (++c.it >= g.bt) {
+          c.it = 0;
+          if (++c.tw >= g.nW) {
+            c.tw = 0;
+            if (++c.th >= g.nH) { c.th = 0; ++c.tt; }
+          }
+        }
+      }
+      c.t = c.tt * g.bt + c.it;
+      c.y = c.th * g.bh + c.ih;
+      c.x = c.tw;  // bw = 1
+    }
+    return bits;
+  }
   while (c.p < end) {
     const int len = run_len_ft(g, c, end);
     bits |= run_mask(g, m, q, c.t, c.y, c.x, c.x + len - 1, c.p - c0);

@@ -339,3 +339,55 @@ def test_full_config_padded_sampled_rows(gpu_lib):
     ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
     assert_close(o[:, rows][:, :, heads], ref_o, "bf16", "wan_sta_padded sampled rows")
     assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3
+
+
+@pytest.mark.parametrize("tile", [(1, 9, 1), (1, 9, 2), (2, 3, 4)])
+def test_column_strip_tiles_reorder_io(gpu_lib, tile):
+    """Stripe heads attended tile-major over narrow grid tiles (a frame read a few
+    columns at a time, which makes column-band stripes contiguous), beside position- and
+    frame-major heads, with the reorder inside the call: o and lse against the oracle in
+    frame-major coordinates, with and without the mask-word table."""
+    g = W.grid(4, 9, 16, tile)
+    masks = [W.with_head_layout(W.mask_stripe(1, 0, 3, 2, 0, 16), "tile"),
+             W.with_head_layout(W.mask_stripe(2, 1, 7, 3, 0, 16), "tile"),
+             W.with_head_layout(W.mask_stripe(1, 1, 3, 2, 0, 144), "position"),
+             W.mask_stripe(1, 0, 2, 4, 0, 16)]
+    q, k, v = W.qkv(2, W.seq_len(g), len(masks), 128, "bf16", seed=33)
+    say(f"column strip tiles {tile}")
+    d = dev()
+    tiles = vsa.vsa_classify_tiles(g, "frame", masks, 128, 64, device=d, with_cls=False)
+    flags = vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO
+    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks)
+    for words in (None, vsa.vsa_boundary_words(g, "frame", masks, tiles)):
+        o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "frame", masks, tiles, flags=flags,
+                                         words=words)
+        torch.cuda.synchronize()
+        assert_close(o, ref_o, "bf16", f"column strips {tile}, words={words is not None}")
+        assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 5e-3
+
+
+def test_full_config_stripes_chosen_orders_sampled_rows(gpu_lib):
+    """The stripe layer with every head in the order the benchmark's cost-based chooser
+    picks (frame-, position- or tile-major over a column-strip grid tile), reorder inside
+    the call and mask words, as the benchmark times it: sampled frame-major rows of heads
+    in every chosen order against the oracle."""
+    import bench
+    name = "stripe_route"
+    cfg, (q, k, v) = _full_inputs(name)
+    d = dev()
+    g, masks = bench.choose_head_layouts(vsa, cfg["grid"], cfg["masks"], cfg["Bq"], cfg["Bk"], d)
+    lays = W.head_layouts(masks, "frame")
+    say(f"full config {name} chosen orders {sorted(set(lays))} grid tile {g['tile_t'], g['tile_h'], g['tile_w']}")
+    tiles = vsa.vsa_classify_tiles(g, "frame", masks, cfg["Bq"], cfg["Bk"], device=d, with_cls=False)
+    words = vsa.vsa_boundary_words(g, "frame", masks, tiles)
+    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "frame", masks, tiles, words=words,
+                                     flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
+    torch.cuda.synchronize()
+    del words
+    assert torch.isfinite(o).all()
+    S = W.seq_len(g)
+    rows = sample_rows_per_tile(S, cfg["Bq"], seed=6, per_tile=0, max_tiles=16)
+    heads = sorted({lays.index(x) for x in set(lays)} | {0, 39})
+    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
+    assert_close(o[:, rows][:, :, heads], ref_o, "bf16", f"{name} chosen orders sampled rows")
+    assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3
