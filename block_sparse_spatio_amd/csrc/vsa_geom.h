@@ -297,6 +297,18 @@ VSA_HD int floor_div(int a, int b) {  // b > 0
 // rows whose interval contains 0 are tested one by one.
 VSA_HD void stripe_rows_test(const Geom& g, const DevMask& m, int dy0, int dy1, int dx0, int dx1, bool& all,
                              bool& any) {
+  // every |d| below Ss (no wrap): kept iff |d| <= Sw - 1, so "any" asks whether some row
+  // interval meets [-(Sw-1), Sw-1] and "all" whether the extremes stay inside it
+  const int dmin = dy0 * g.Wg + dx0 - m.So, dmax = dy1 * g.Wg + dx1 - m.So;
+  if (dmin > -m.Ss && dmax < m.Ss) {
+    const int w = m.Sw - 1;
+    if (w < 0) { all = false; any = false; return; }
+    const int A = dx0 - m.So, B = dx1 - m.So;  // row dy spans [A + dy*Wg, B + dy*Wg]
+    const int lo = imax(dy0, -floor_div(w + B, g.Wg)), hi = imin(dy1, floor_div(w - A, g.Wg));
+    any = lo <= hi;
+    all = dmin >= -w && dmax <= w;
+    return;
+  }
   all = true;
   any = false;
   const int per = m.Ss / igcd(g.Wg, m.Ss);
@@ -582,11 +594,23 @@ VSA_HD uint64_t run_mask_y(const Geom& g, const DevMask& m, const QueryPos& q, i
     case VSA_MASK_STRIPE: {
       if (g.T <= 64 ? !((q.tkeep >> t) & 1) : !stripe_frame_kept(m, t, q.t)) return 0;
       if (m.Sw <= 0) return 0;
-      // u = s_k - s_q - So steps by Wg along the run; kept where (|u| mod Ss) < Sw.  The
-      // residue is carried from row to row (one division per sign of u).
+      // u = s_k - s_q - So steps by Wg along the run; kept where (|u| mod Ss) < Sw.
       uint64_t bits = 0;
       int u = y0 * g.Wg + x - q.s - m.So;
+      const int u1 = u + (y1 - y0) * g.Wg;
+      if (u > -m.Ss && u1 < m.Ss) {  // no wrap: kept iff |u| <= Sw - 1, one range of rows
+        const int w = m.Sw - 1, c = u - y0 * g.Wg;  // u = y*Wg + c
+        const int lo = imax(y0, -floor_div(w + c, g.Wg)), hi = imin(y1, floor_div(w - c, g.Wg));
+        return lo <= hi ? bit_range(off + lo - y0, off + hi - y0) : 0;
+      }
       const int step = g.Wg % m.Ss;
+      if (step == 0) {  // the residue is fixed on each side of u = 0
+        const int yb = imin(imax(y0, -floor_div(x - q.s - m.So, g.Wg)), y1 + 1);  // first row with u >= 0
+        if (yb > y0 && (iabs(u) % m.Ss) < m.Sw) bits |= bit_range(off, off + yb - 1 - y0);
+        if (yb <= y1 && ((yb * g.Wg + x - q.s - m.So) % m.Ss) < m.Sw) bits |= bit_range(off + yb - y0, off + y1 - y0);
+        return bits;
+      }
+      // otherwise the residue is carried from row to row (one division per sign of u)
       int y = y0;
       if (u < 0) {
         int r = (-u) % m.Ss;  // |u| mod Ss, |u| falling by Wg per row
