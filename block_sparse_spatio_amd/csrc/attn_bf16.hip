@@ -111,13 +111,17 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   const uint16_t* vp = (const uint16_t*)a.v;
   const int tok_stride = H * D;  // elements between consecutive tokens
   const size_t base_bh = ((size_t)b * S) * tok_stride + (size_t)h * D;
+  // q and o: the executed order, or the caller's frame-major rows (gathered / scattered)
+  const size_t base_io = a.gather_io ? ((size_t)b * a.lse_S) * tok_stride + (size_t)h * D : base_bh;
 
   // ---- this lane's query row: B operand of S^T = K Q^T ----
   const int qrow = qt * Bq + wave * 32 + l32;
   const int qrow_c = qrow < S ? qrow : S - 1;
   bf16x8 qf[KSTEPS];
   {
-    const uint16_t* src = qp + base_bh + (size_t)qrow_c * tok_stride + g2 * 8;
+    // a padding row of a padded grid reads row 0 (finite data; its output is dropped)
+    const int qsrc = a.gather_io ? imax(frame_index(g, qrow_c), 0) : qrow_c;
+    const uint16_t* src = qp + base_io + (size_t)qsrc * tok_stride + g2 * 8;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + s * 16));
   }
@@ -465,8 +469,9 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   // ---- epilogue: O = acc / l, lse = scale*m + ln(l) ----
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < S) {
-    uint16_t* op = (uint16_t*)a.o + base_bh + (size_t)qrow * tok_stride;
+  const int orow = qrow >= S ? -1 : a.gather_io ? frame_index(g, qrow) : qrow;  // -1: no output row
+  if (orow >= 0) {
+    uint16_t* op = (uint16_t*)a.o + base_io + (size_t)orow * tok_stride;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -477,7 +482,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
         *(u32x2*)(op + d) = u32x2{w0, w1};
       }
     if (a.write_lse && g2 == 0) {
-      const int lpos = a.lse_frame_major ? frame_index(g, qrow) : qrow;  // -1: padding row
+      const int lpos = a.lse_frame_major ? (a.gather_io ? orow : frame_index(g, qrow)) : qrow;  // -1: padding
       if (lpos >= 0)
         a.lse[((size_t)b * H + h) * a.lse_S + lpos] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
     }

@@ -10,8 +10,11 @@
 //
 // One workgroup per (b, h, 64-key block): the 64 x D block is read with 16-byte
 // coalesced loads (one 2*D-byte row per key), staged in LDS, and written as D rows of
-// 64 keys (128 contiguous bytes each).
-#include "vsa_internal.h"
+// 64 keys (128 contiguous bytes each).  With a gather geometry, V is the caller's
+// frame-major tensor and key p of head h (in that head's executed order) is read from
+// its frame-major row, so the V^T of a reordering call needs no reordered copy of V
+// (padding keys of a padded grid read as zeros).
+#include "vsa_geom.h"
 
 namespace vsa {
 
@@ -25,16 +28,29 @@ constexpr int kThreads = 256;
 template <int D>
 __global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* __restrict__ v,
                                                                uint16_t* __restrict__ vt, int S, int H,
-                                                               int s_pad) {
+                                                               int s_pad, Geom g, HeadLayouts hl, int gather,
+                                                               int S_src) {
   __shared__ uint16_t tile[kKeys][D + 2];  // +2: odd word stride keeps the column reads spread
+  __shared__ int src_row[kKeys];
   const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int k0 = kb * kKeys;
   constexpr int CH = D / 8;  // 16-byte chunks per key row
+  if (threadIdx.x < kKeys) {
+    const int key = k0 + threadIdx.x;
+    int sr = key < S ? key : -1;
+    if (gather && sr >= 0) {
+      Geom gh = g;
+      gh.layout = hl.lay[h];
+      sr = frame_index(gh, key);
+    }
+    src_row[threadIdx.x] = sr;
+  }
+  __syncthreads();
   for (int e = threadIdx.x; e < kKeys * CH; e += kThreads) {
     const int r = e / CH, c = e % CH;
-    const int key = k0 + r;
+    const int sr = src_row[r];
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < S) x = *(const u32x4*)(v + (((size_t)b * S + key) * H + h) * D + c * 8);
+    if (sr >= 0) x = *(const u32x4*)(v + (((size_t)b * S_src + sr) * H + h) * D + c * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       tile[r][c * 8 + 2 * j] = (uint16_t)(x[j] & 0xffffu);
@@ -56,14 +72,22 @@ __global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* _
 }  // namespace
 
 hipError_t launch_transpose_v(const void* v, void* vt, int32_t B, int32_t S, int32_t H, int32_t D,
-                              int32_t s_pad, hipStream_t stream) {
+                              int32_t s_pad, const Geom* gather, const HeadLayouts* hl, int32_t S_src,
+                              hipStream_t stream) {
   dim3 grid(s_pad / kKeys, H, B);
+  Geom g{};
+  HeadLayouts lay{};
+  if (gather) {
+    g = *gather;
+    lay = *hl;
+  }
+  const int src_len = gather ? S_src : S;
   if (D == 128)
     hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(kThreads), 0, stream, (const uint16_t*)v,
-                       (uint16_t*)vt, S, H, s_pad);
+                       (uint16_t*)vt, S, H, s_pad, g, lay, gather ? 1 : 0, src_len);
   else if (D == 64)
     hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(kThreads), 0, stream, (const uint16_t*)v,
-                       (uint16_t*)vt, S, H, s_pad);
+                       (uint16_t*)vt, S, H, s_pad, g, lay, gather ? 1 : 0, src_len);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -304,11 +304,14 @@ vsa_status vsa_boundary_words(const vsa_grid* grid, vsa_layout layout, const vsa
 }
 
 // bf16: V^T [B][H][D][S rounded up to 64] (the PV operand, transposed once per call);
-// with VSA_FWD_REORDER_IO, tile-major copies of q, k and v before it.
+// with VSA_FWD_REORDER_IO, k in each head's executed order before it (q and v are
+// gathered and o scattered by row).  f32 with VSA_FWD_REORDER_IO: reordered copies of
+// q, k and v.
 static size_t vt_pad(int32_t S) { return ((size_t)S + 63) / 64 * 64; }
 static size_t fwd_ws_bytes(int32_t B, int32_t S, int32_t H, int32_t D, vsa_dtype dtype, int32_t flags) {
   const size_t eb = elem_size(dtype);
-  size_t n = (flags & VSA_FWD_REORDER_IO) ? 3ull * B * S * H * D * eb : 0;
+  const size_t copies = dtype == VSA_BF16 ? 1 : 3;
+  size_t n = (flags & VSA_FWD_REORDER_IO) ? copies * B * S * H * D * eb : 0;
   if (dtype == VSA_BF16) n += (size_t)B * H * D * vt_pad(S) * eb;
   return n;
 }
@@ -406,6 +409,7 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   a.pad_only = (flags & VSA_FWD_TILE_ALIGNED) ? 1 : 0;
   a.write_lse = (flags & VSA_FWD_WRITE_LSE) ? 1 : 0;
   a.lse_frame_major = reorder ? 1 : 0;
+  a.gather_io = (reorder && dtype == VSA_BF16) ? 1 : 0;
   a.lse = lse;
   a.n_full = tiles->n_full; a.n_bnd = tiles->n_bnd;
   a.full_idx = tiles->full_idx; a.bnd_idx = tiles->bnd_idx;
@@ -415,11 +419,29 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   hipStream_t hs = (hipStream_t)stream;
   const vsa::Geom& G = a.g;
   char* ws = (char*)workspace;
+  hipError_t e;
+  if (dtype == VSA_BF16) {
+    // with the reorder only k is copied into each head's order: the kernel gathers its
+    // query rows and scatters its output rows, and the V^T transpose gathers v
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    if (reorder) {
+      if ((e = vsa::launch_reorder(k, ws, (int)eb, B, H, D, G, hl, 0, hs)) != hipSuccess) return hip_fail(e, "reorder k");
+      a.k = ws;
+    }
+    a.s_pad = (int32_t)vt_pad(a.S);
+    void* vt = ws + (reorder ? nelem * eb : 0);
+    if ((e = vsa::launch_transpose_v(v, vt, B, a.S, H, D, a.s_pad, reorder ? &G : nullptr, &hl, S, hs)) !=
+        hipSuccess)
+      return hip_fail(e, "transpose v");
+    a.vt = vt;
+    e = vsa::launch_attn_bf16(a, table, hm, hs);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ok();
+  }
   if (reorder) {
     void* wq = ws;
     void* wk = ws + nelem * eb;
     void* wv = ws + 2 * nelem * eb;
-    hipError_t e;
     if ((e = vsa::launch_reorder(q, wq, (int)eb, B, H, D, G, hl, 0, hs)) != hipSuccess) return hip_fail(e, "reorder q");
     if ((e = vsa::launch_reorder(k, wk, (int)eb, B, H, D, G, hl, 0, hs)) != hipSuccess) return hip_fail(e, "reorder k");
     if ((e = vsa::launch_reorder(v, wv, (int)eb, B, H, D, G, hl, 0, hs)) != hipSuccess) return hip_fail(e, "reorder v");
@@ -429,17 +451,7 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   } else {
     a.q = q; a.k = k; a.v = v; a.o = o;
   }
-  hipError_t e;
-  if (dtype == VSA_BF16) {
-    a.s_pad = (int32_t)vt_pad(a.S);
-    void* vt = ws + (reorder ? 3 * nelem * eb : 0);
-    if ((e = vsa::launch_transpose_v(a.v, vt, B, a.S, H, D, a.s_pad, hs)) != hipSuccess)
-      return hip_fail(e, "transpose v");
-    a.vt = vt;
-    e = vsa::launch_attn_bf16(a, table, hm, hs);
-  } else {
-    e = vsa::launch_attn_f32(a, table, hm, hs);
-  }
+  e = vsa::launch_attn_f32(a, table, hm, hs);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (reorder) {
     e = vsa::launch_reorder(ws, o, (int)eb, B, H, D, G, hl, 1, hs);

@@ -104,6 +104,10 @@ struct FwdArgs {
   int32_t write_lse;
   int32_t lse_frame_major;  // q/k/v/o were reordered: write lse in frame-major order
   int32_t lse_S;            // length of an lse row (the caller's sequence length)
+  // bf16 with the reorder: q and o are the caller's frame-major tensors (lse_S rows per
+  // batch item) and each query row is gathered / each output row scattered through its
+  // head's order; only k is reordered (v is gathered by the transpose)
+  int32_t gather_io;
   // bf16 path, optional: precomputed mask words of boundary list entries j < words_cap,
   // [U][nQ][words_cap][Bq/32 waves][64 lanes] (launch_boundary_words)
   const uint32_t* words;
@@ -118,8 +122,11 @@ hipError_t launch_attn_f32(const FwdArgs& a, const MaskTable& masks, const HeadM
 hipError_t launch_boundary_words(const Geom& g, const MaskTable& masks, int32_t U, int32_t Bq, int32_t nQ,
                                  int32_t nK, const int32_t* n_bnd, const int32_t* bnd_idx, uint32_t* words,
                                  int32_t cap, hipStream_t stream);
+// gather (may be NULL): v is frame-major with S_src rows per batch item and key p of
+// head h is its frame-major row under layout hl->lay[h] of *gather (zeros for padding)
 hipError_t launch_transpose_v(const void* v, void* vt, int32_t B, int32_t S, int32_t H, int32_t D,
-                              int32_t s_pad, hipStream_t stream);
+                              int32_t s_pad, const Geom* gather, const HeadLayouts* hl, int32_t S_src,
+                              hipStream_t stream);
 hipError_t launch_reorder(const void* src, void* dst, int32_t elem_bytes, int32_t B,
                           int32_t H, int32_t D, const Geom& g, const HeadLayouts& hl,
                           int32_t inverse, hipStream_t stream);

@@ -211,9 +211,10 @@ vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout,
 /* Workspace bytes vsa_sparse_attn_fwd needs for these arguments, with S the executed
  * length (vsa_seq_len; T*Hg*Wg except for VSA_LAYOUT_TILE_PADDED): for bf16,
  * B*H*D*S64 elements (S64 = S rounded up to a multiple of 64) that hold V
- * transposed per 64-key block to [B][H][S64/64][D][64]; with VSA_FWD_REORDER_IO,
- * 3*B*S*H*D elements of dtype more (q, k, v in each head's executed order).  f32
- * without VSA_FWD_REORDER_IO needs none. */
+ * transposed per 64-key block to [B][H][S64/64][D][64], and with VSA_FWD_REORDER_IO
+ * B*S*H*D elements more (k in each head's executed order; q and v are gathered and o
+ * scattered by row); f32 with VSA_FWD_REORDER_IO: 3*B*S*H*D elements (q, k, v in each
+ * head's executed order), without it none. */
 vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D,
                                    vsa_dtype dtype, int32_t flags, size_t* bytes);
 

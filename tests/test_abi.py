@@ -58,7 +58,9 @@ def test_workspace_sizes():
     assert vsa.vsa_fwd_workspace_bytes(2, 100, 3, 64, vsa.VSA_BF16, 0) == 2 * 3 * 64 * 128 * 2
     assert vsa.vsa_fwd_workspace_bytes(2, 100, 3, 64, vsa.VSA_F32, 0) == 0
     assert vsa.vsa_fwd_workspace_bytes(1, 115200, 24, 128, vsa.VSA_BF16, vsa.VSA_FWD_REORDER_IO) \
-        == 3 * 115200 * 24 * 128 * 2 + vt
+        == 115200 * 24 * 128 * 2 + vt  # k reordered; q, v gathered, o scattered
+    assert vsa.vsa_fwd_workspace_bytes(2, 100, 3, 64, vsa.VSA_F32, vsa.VSA_FWD_REORDER_IO) \
+        == 3 * 2 * 100 * 3 * 64 * 4
     assert vsa.vsa_profile_workspace_bytes(2, 75600, 40, 128, 64, 3) > 0
 
 
