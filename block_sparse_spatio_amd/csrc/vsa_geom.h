@@ -346,6 +346,11 @@ VSA_HD void box_pair_test(const Geom& g, const DevMask& m, const Box& r, const B
     case VSA_MASK_STRIPE: {
       bool at, nt;
       periodic_test(c.t0 - r.t1, c.t1 - r.t0, m.To, m.Ts, m.Tw, at, nt);
+      if (!nt) {  // no key frame passes the temporal test: nothing kept
+        all = false;
+        any = false;
+        return;
+      }
       bool as = true, ns = false;
       if (s_contiguous(g, r) && s_contiguous(g, c)) {
         int sq0 = r.y0 * g.Wg + r.x0, sq1 = r.y1 * g.Wg + r.x1;
