@@ -23,6 +23,14 @@
 //    transpose.hip once per call), so both operands are plain 16-byte LDS reads at full
 //    LDS bandwidth.  16-byte chunks are XOR-swizzled per row so that the operand reads
 //    spread over all LDS banks (the DMA writes are contiguous anyway).
+//  * A boundary tile's element mask is one 32-bit word per lane (bit i: score register i
+//    kept).  It comes from a word table computed beforehand (words.hip), DMA'd into LDS
+//    beside the tile's K rows, or, for list entries the table does not hold, is derived
+//    in the loop from the mask descriptor (vsa_geom.h).  Workgroups whose whole boundary
+//    list is in the table run an instance with no mask arithmetic at all.
+//  * With the caller's frame-major q and o (the reordering call), each lane gathers its
+//    query row and scatters its output row through the head's order; k arrives in the
+//    head's order and V^T was gathered by the transpose.
 //  * The running max is refreshed lazily: the accumulator is rescaled only when a row's
 //    tile max exceeds the reference by more than 2^8 in exp2 units (any lane of the
 //    wave), which keeps every probability <= 256 and the result exact up to rounding.
