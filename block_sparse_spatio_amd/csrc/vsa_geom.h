@@ -92,17 +92,20 @@ VSA_HD int order_digits(const Geom& g, int* radix) {
   return 6;
 }
 
-// Box of positions [cur, cur + cnt*W[j+1]) given that digits < j are those of cur,
-// digit j runs over cnt values from cur's digit j, and digits > j are full.
-VSA_HD Box level_box(const Geom& g, int n, const int* radix, const int* W, int cur, int j,
-                     int cnt) {
-  int lo[6], hi[6];
+// Digit intervals of the positions [cur, cur + cnt*W[j+1]) given cur's digits d (most
+// significant first): digits < j are those of cur, digit j runs over cnt values from
+// d[j], and digits > j are full.
+VSA_HD void digit_ranges(int n, const int* radix, const int* d, int j, int cnt, int* lo, int* hi) {
   for (int k = 0; k < n; ++k) {
-    int d = (cur / W[k + 1]) % radix[k];
-    if (k < j) { lo[k] = d; hi[k] = d; }
-    else if (k == j) { lo[k] = d; hi[k] = d + cnt - 1; }
+    if (k < j) { lo[k] = d[k]; hi[k] = d[k]; }
+    else if (k == j) { lo[k] = d[k]; hi[k] = d[k] + cnt - 1; }
     else { lo[k] = 0; hi[k] = radix[k] - 1; }
   }
+}
+
+VSA_HD Box level_box(const Geom& g, int n, const int* radix, const int* d, int j, int cnt) {
+  int lo[6], hi[6];
+  digit_ranges(n, radix, d, j, cnt, lo, hi);
   Box b;
   if (n == 3) {
     b.t0 = lo[0]; b.t1 = hi[0]; b.y0 = lo[1]; b.y1 = hi[1]; b.x0 = lo[2]; b.x1 = hi[2];
@@ -116,84 +119,79 @@ VSA_HD Box level_box(const Geom& g, int n, const int* radix, const int* W, int c
   return b;
 }
 
-// Position-major: [lo, end) inside the part after the frame-0 block, as boxes of the
-// digits (y, x, t-1) with radices (Hg, Wg, T-1), at most 5.
-VSA_HD Box pm_box(const Geom& g, const int* W, int cur, int j, int cnt) {
-  const int radix[3] = {g.Hg, g.Wg, g.T - 1};
+// Position-major: boxes of the digits (y, x, t-1) with radices (Hg, Wg, T-1) inside the
+// part after the frame-0 block.
+VSA_HD Box pm_box(const int* radix, const int* d, int j, int cnt) {
   int lo[3], hi[3];
-  for (int k = 0; k < 3; ++k) {
-    int d = (cur / W[k + 1]) % radix[k];
-    if (k < j) { lo[k] = d; hi[k] = d; }
-    else if (k == j) { lo[k] = d; hi[k] = d + cnt - 1; }
-    else { lo[k] = 0; hi[k] = radix[k] - 1; }
-  }
+  digit_ranges(3, radix, d, j, cnt, lo, hi);
   Box b;
   b.y0 = lo[0]; b.y1 = hi[0]; b.x0 = lo[1]; b.x1 = hi[1];
   b.t0 = lo[2] + 1; b.t1 = hi[2] + 1;
   return b;
 }
 
-VSA_HD int decompose_pm_rest(const Geom& g, int lo, int end, Box* out) {
-  const int radix[3] = {g.Hg, g.Wg, g.T - 1};
-  int W[4];
-  W[3] = 1;
-  for (int k = 2; k >= 0; --k) W[k] = W[k + 1] * radix[k];
+// Split positions [lo, end) of a mixed-radix order (radix[0] most significant, W[k] the
+// weight of digit k - 1) into at most 2n-1 boxes, each a run of one digit with the
+// coarser digits fixed and the finer ones full.  The digits of the running position are
+// carried along, so only the starting digits and the descending counts divide.
+template <typename BoxFn>
+VSA_HD int decompose_radix(int n, const int* radix, int lo, int end, Box* out, BoxFn box) {
+  int W[7];
+  W[n] = 1;
+  for (int k = n - 1; k >= 0; --k) W[k] = W[k + 1] * radix[k];
+  if (lo >= end) return 0;
+  int d[6];
+  for (int k = n - 1, x = lo; k >= 0; --k) {
+    const int q = x / radix[k];
+    d[k] = x - q * radix[k];
+    x = q;
+  }
   int nb = 0, cur = lo;
-  if (cur >= end) return 0;
-  int j = 2;
+  // ascending: align cur to ever coarser digit boundaries (the digits finer than j are
+  // already zero)
+  int j = n - 1;
   for (; j >= 0; --j) {
-    int blk = W[j];
-    int next = ((cur + blk - 1) / blk) * blk;
+    const int cnt = d[j] == 0 ? 0 : radix[j] - d[j];
+    const int next = cur + cnt * W[j + 1];
     if (next > end) break;
-    if (next > cur) {
-      out[nb++] = pm_box(g, W, cur, j, (next - cur) / W[j + 1]);
+    if (cnt > 0) {
+      out[nb++] = box(d, j, cnt);
       cur = next;
+      d[j] = 0;  // digit j wraps and carries into the coarser digits
+      for (int k = j - 1; k >= 0; --k) {
+        if (++d[k] < radix[k]) break;
+        d[k] = 0;
+      }
     }
     if (cur == end) return nb;
   }
   if (j < 0) j = 0;
-  for (; j < 3 && cur < end; ++j) {
-    int cnt = (end - cur) / W[j + 1];
+  // descending: whole runs of digit j, then finer digits (no carry: the run stays below
+  // the next boundary of digit j)
+  for (; j < n && cur < end; ++j) {
+    const int cnt = (end - cur) / W[j + 1];
     if (cnt > 0) {
-      out[nb++] = pm_box(g, W, cur, j, cnt);
+      out[nb++] = box(d, j, cnt);
       cur += cnt * W[j + 1];
+      d[j] += cnt;
     }
   }
   return nb;
+}
+
+VSA_HD int decompose_pm_rest(const Geom& g, int lo, int end, Box* out) {
+  const int radix[3] = {g.Hg, g.Wg, g.T - 1};
+  return decompose_radix(3, radix, lo, end, out,
+                         [&](const int* d, int j, int cnt) { return pm_box(radix, d, j, cnt); });
 }
 
 // Split positions [lo, end) of a frame- or tile-major order into at most 2n-1 boxes
 // (mixed-radix range decomposition).
 VSA_HD int decompose_mixed(const Geom& g, int lo, int end, Box* out) {
   int radix[6];
-  int n = order_digits(g, radix);
-  int W[7];
-  W[n] = 1;
-  for (int k = n - 1; k >= 0; --k) W[k] = W[k + 1] * radix[k];
-  int nb = 0, cur = lo;
-  if (cur >= end) return 0;
-  // ascending: align cur to ever coarser digit boundaries
-  int j = n - 1;
-  for (; j >= 0; --j) {
-    int blk = W[j];
-    int next = ((cur + blk - 1) / blk) * blk;
-    if (next > end) break;
-    if (next > cur) {
-      out[nb++] = level_box(g, n, radix, W, cur, j, (next - cur) / W[j + 1]);
-      cur = next;
-    }
-    if (cur == end) return nb;
-  }
-  if (j < 0) j = 0;
-  // descending: whole runs of digit j, then finer digits
-  for (; j < n && cur < end; ++j) {
-    int cnt = (end - cur) / W[j + 1];
-    if (cnt > 0) {
-      out[nb++] = level_box(g, n, radix, W, cur, j, cnt);
-      cur += cnt * W[j + 1];
-    }
-  }
-  return nb;
+  const int n = order_digits(g, radix);
+  return decompose_radix(n, radix, lo, end, out,
+                         [&](const int* d, int j, int cnt) { return level_box(g, n, radix, d, j, cnt); });
 }
 
 // Split executed positions [lo, end) into boxes: at most 2n-1 for frame- and
@@ -426,6 +424,23 @@ VSA_HD long long box_pair_kept(const Geom& g, const DevMask& m, const Box& r, Bo
 // Tile class of query boxes R[nr] x key boxes C[nc] (padded: the tile reaches past S).
 VSA_HD int tile_class(const Geom& g, const DevMask& m, const Box* R, int nr, const Box* C, int nc,
                       bool padded) {
+  // Frame pre-test: when no key frame is a sink frame and no pair of the two tiles'
+  // frame ranges passes the temporal part of the mask, nothing is kept.  (Tiles of the
+  // position-major order span all frames, where the test never decides.)
+  if (g.layout != VSA_LAYOUT_POSITION_MAJOR && nr > 0 && nc > 0 &&
+      (m.kind == VSA_MASK_STRIPE || (m.kind == VSA_MASK_BOX && m.rt >= 0))) {
+    int q0 = R[0].t0, q1 = R[0].t1, k0 = C[0].t0, k1 = C[0].t1;
+    for (int i = 1; i < nr; ++i) { q0 = imin(q0, R[i].t0); q1 = imax(q1, R[i].t1); }
+    for (int j = 1; j < nc; ++j) { k0 = imin(k0, C[j].t0); k1 = imax(k1, C[j].t1); }
+    if (k0 >= m.sink) {
+      bool a, n;
+      if (m.kind == VSA_MASK_STRIPE)
+        periodic_test(k0 - q1, k1 - q0, m.To, m.Ts, m.Tw, a, n);
+      else
+        radius_test(k0 - q1, k1 - q0, m.rt, a, n);
+      if (!n) return VSA_TILE_EMPTY;
+    }
+  }
   bool all = true, any = false;
   for (int i = 0; i < nr; ++i) {
     for (int j = 0; j < nc; ++j) {
