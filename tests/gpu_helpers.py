@@ -7,7 +7,7 @@ import block_sparse_spatio_amd as vsa
 import oracle
 import workloads as W
 
-# spec tolerances (oracle run on the same bf16-rounded / fp32 inputs)
+# parity tolerances (oracle run on the same bf16-rounded / fp32 inputs)
 BF16_MAX_ABS, BF16_MEAN_ABS = 2e-2, 1e-3
 F32_MAX_ABS = 1e-5
 

@@ -1,4 +1,4 @@
-"""Attention forward on the GPU against the CPU oracle (spec tolerances:
+"""Attention forward on the GPU against the CPU oracle (parity tolerances:
 fp32 max-abs <= 1e-5; bf16 max-abs <= 2e-2 and mean-abs <= 1e-3, the oracle run on
 the same bf16-rounded inputs)."""
 import numpy as np

@@ -1,6 +1,6 @@
 """Merging partial attention results on the GPU against the oracle's log-sum-exp merge
 (DSA study guide, section 18).  fp32 outputs within 1e-5; bf16 outputs within the
-spec bf16 tolerance (max-abs 2e-2, mean-abs 1e-3); lse within 1e-5."""
+parity bf16 tolerance (max-abs 2e-2, mean-abs 1e-3); lse within 1e-5."""
 import numpy as np
 import pytest
 import torch
