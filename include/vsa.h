@@ -199,10 +199,11 @@ vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout,
 /* Attention forward ----------------------------------------------------------- */
 
 #define VSA_FWD_FORCE_MASK 1  /* ablation: run every listed tile through the masked path */
-#define VSA_FWD_REORDER_IO 2  /* q/k/v/o are frame-major; each head's tokens are reordered
-                                 into its executed layout (the call's, or its descriptor's
-                                 head_layout) in the workspace, attention runs there and
-                                 O is reordered back (Sparse VideoGen on TPU, "layout
+#define VSA_FWD_REORDER_IO 2  /* q/k/v/o are frame-major; each head attends in its executed
+                                 layout (the call's, or its descriptor's head_layout): bf16
+                                 reorders k into the workspace and maps the rows of q, v and
+                                 o through the layout, f32 reorders q, k, v into the
+                                 workspace and o back (Sparse VideoGen on TPU, "layout
                                  transforms on local heads"); needs a head not frame-major */
 #define VSA_FWD_WRITE_LSE 4   /* write lse (must then be non-NULL) */
 #define VSA_FWD_TILE_ALIGNED 8  /* listed BOUNDARY tiles mask only keys past S: the
