@@ -182,6 +182,8 @@ def _full_inputs(name):
     ("wan_single", 256, "masks"), ("wan_single", 128, "extra_masks"), ("sta_hunyuan", 128, "masks"),
     ("stripe_route", 128, "masks")])
 def test_full_config_sampled_rows(gpu_lib, name, Bq, which):
+    """Full-size workloads in the launch configuration the benchmark times (boundary
+    masks from the word table, cap = nK): sampled rows against the oracle."""
     cfg, (q, k, v) = _full_inputs(name)
     g, layout, masks = cfg["grid"], cfg["layout"], cfg[which]
     S = W.seq_len(g)
@@ -190,9 +192,11 @@ def test_full_config_sampled_rows(gpu_lib, name, Bq, which):
     qd, kd, vd = q.to(d), k.to(d), v.to(d)
     reorder = layout == "tile"
     tiles = vsa.vsa_classify_tiles(g, layout, masks, Bq, cfg["Bk"], device=d, with_cls=False)
-    o, lse = vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles,
+    words = vsa.vsa_boundary_words(g, layout, masks, tiles)
+    o, lse = vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles, words=words,
                                      flags=vsa.VSA_FWD_WRITE_LSE | (vsa.VSA_FWD_REORDER_IO if reorder else 0))
     torch.cuda.synchronize()
+    del words
     assert torch.isfinite(o).all()
     # oracle on sampled rows (frame-major indices: the reorder is inside the call)
     rows = sample_rows_per_tile(S, Bq, seed=3, per_tile=0, max_tiles=24)
@@ -255,9 +259,11 @@ def test_full_config_position_major_sampled_rows(gpu_lib):
     say(f"full config {name} position-major temporal heads Bq={Bq}")
     d = dev()
     tiles = vsa.vsa_classify_tiles(g, "frame", masks, Bq, cfg["Bk"], device=d, with_cls=False)
-    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "frame", masks, tiles,
+    words = vsa.vsa_boundary_words(g, "frame", masks, tiles)
+    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "frame", masks, tiles, words=words,
                                      flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
     torch.cuda.synchronize()
+    del words
     assert torch.isfinite(o).all()
     rows = sample_rows_per_tile(S, Bq, seed=4, per_tile=0, max_tiles=24)
     heads = [0, 7, 19, 20, 27, 39]
@@ -330,9 +336,11 @@ def test_full_config_padded_sampled_rows(gpu_lib):
     q, k, v = W.qkv(cfg["B"], S, cfg["H"], cfg["D"], cfg["dtype"], seed=cfg["seed"])
     d = dev()
     tiles = vsa.vsa_classify_tiles(g, "padded", masks, Bq, cfg["Bk"], device=d, with_cls=False)
-    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "padded", masks, tiles,
+    words = vsa.vsa_boundary_words(g, "padded", masks, tiles)
+    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "padded", masks, tiles, words=words,
                                      flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
     torch.cuda.synchronize()
+    del words
     assert torch.isfinite(o).all()
     rows = sample_rows_per_tile(S, Bq, seed=5, per_tile=0, max_tiles=24)
     heads = [0, 13, 39]
