@@ -116,7 +116,6 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 
   const uint16_t* qp = (const uint16_t*)a.q;
   const uint16_t* kp = (const uint16_t*)a.k;
-  const uint16_t* vp = (const uint16_t*)a.v;
   const int tok_stride = H * D;  // elements between consecutive tokens
   const size_t base_bh = ((size_t)b * S) * tok_stride + (size_t)h * D;
   // q and o: the executed order, or the caller's frame-major rows (gathered / scattered)
