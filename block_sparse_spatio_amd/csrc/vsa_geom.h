@@ -500,18 +500,19 @@ VSA_HD uint64_t bit_range(int lo, int hi) {  // bits lo..hi inclusive, 0 <= lo <
 // Bits off + (u - ua) for the u in [ua, ub] with (|u| mod P) < w (the stripe predicate
 // along one run of keys).
 VSA_HD uint64_t periodic_bits(int ua, int ub, int P, int w, int off) {
+  // one division per sign of u: the periods are stepped from the first one
   uint64_t bits = 0;
   if (ub >= 0) {
     int lo = imax(ua, 0);
-    for (int j = lo / P; j <= ub / P; ++j) {
-      int a = imax(lo, j * P), b = imin(ub, j * P + w - 1);
+    for (int base = (lo / P) * P; base <= ub; base += P) {
+      int a = imax(lo, base), b = imin(ub, base + w - 1);
       if (a <= b) bits |= bit_range(off + a - ua, off + b - ua);
     }
   }
   if (ua < 0) {
     int lo = imax(-ub, 1), hi = -ua;  // |u| in [lo, hi]
-    for (int j = lo / P; j <= hi / P; ++j) {
-      int a = imax(lo, j * P), b = imin(hi, j * P + w - 1);
+    for (int base = (lo / P) * P; base <= hi; base += P) {
+      int a = imax(lo, base), b = imin(hi, base + w - 1);
       if (a <= b) bits |= bit_range(off - b - ua, off - a - ua);
     }
   }

@@ -14,8 +14,9 @@
 // as in the forward.  Entries j >= min(n_bnd, cap) are not written.
 //
 // One thread per query row computes its 64-bit row mask (vsa_geom.h) and writes both
-// lanes' words; gridDim.z strides over the entries.  Bound by the mask arithmetic;
-// integer-exact.
+// lanes' words; gridDim.z strides over the entries.  The list row is staged in LDS with
+// coalesced loads, so the entry loop does not wait on a global load per entry.
+// Integer-exact.
 #include "vsa_geom.h"
 
 namespace vsa {
@@ -23,6 +24,7 @@ namespace vsa {
 namespace {
 
 constexpr int kStride = 4;  // entries of a row split over this many workgroups
+constexpr int kStage = 1024;  // list entries staged in LDS at a time (a multiple of kStride)
 
 __global__ __launch_bounds__(256) void boundary_words_kernel(Geom g_call, MaskTable masks, int Bq, int nQ, int nK,
                                                              const int32_t* __restrict__ n_bnd,
@@ -39,15 +41,22 @@ __global__ __launch_bounds__(256) void boundary_words_kernel(Geom g_call, MaskTa
   const int nw = Bq / 32;
   const int32_t* list = bnd_idx + row * nK;
   uint32_t* out = words + row * cap * (size_t)(nw * 64) + (r >> 5) * 64 + (r & 31);
-  for (int j = blockIdx.z; j < nb; j += kStride) {
-    const int kt = imin(imax(list[j], 0), nK - 1);
-    const uint64_t bits = tile_row_mask(g, m, qpos, kt * 64, 64);
-    const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
+  __shared__ int s_kt[kStage];
+  for (int base = 0; base < nb; base += kStage) {
+    const int cnt = imin(kStage, nb - base);
+    __syncthreads();  // the previous chunk's entries are read
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) s_kt[i] = imin(imax(list[base + i], 0), nK - 1);
+    __syncthreads();
+    for (int jj = blockIdx.z; jj < cnt; jj += kStride) {  // base is a multiple of kStride
+      const int kt = s_kt[jj];
+      const uint64_t bits = tile_row_mask(g, m, qpos, kt * 64, 64);
+      const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
 #pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {
-      const uint32_t w = ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
-                         (((hi >> (8 * g2)) & 0xffu) << 16) | (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
-      out[(size_t)j * (nw * 64) + 32 * g2] = w;
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const uint32_t w = ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
+                           (((hi >> (8 * g2)) & 0xffu) << 16) | (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
+        out[(size_t)(base + jj) * (nw * 64) + 32 * g2] = w;
+      }
     }
   }
 }
