@@ -225,10 +225,14 @@ def vsa_fwd_workspace_bytes(B, S, H, D, dtype, flags):
 
 def vsa_boundary_words(grid, layout, masks, tiles, cap=None, out=None, stream=None):
     """Element masks of the listed boundary tiles for the bf16 forward.  cap: entries per
-    list row (default: every key tile, so no list row is cut short).  Returns
+    list row; None (default) sizes the table to the longest boundary list, which reads
+    the list lengths back to the host (waits for the classification); pass nK to size it
+    without that read (every list fits).  Returns
     {"words": int32 [U, nQ, cap, Bq/32, 64] device tensor (uint32 bit patterns), "cap": cap}."""
     U, nQ, nK, Bq = tiles["n_unique"], tiles["nQ"], tiles["nK"], tiles["Bq"]
-    cap = nK if cap is None else int(cap)
+    if cap is None:
+        cap = max(1, int(tiles["n_bnd"].max()))
+    cap = int(cap)
     shape = (U, nQ, cap, Bq // 32, 64)
     dev = tiles["n_bnd"].device
     if out is None:

@@ -192,7 +192,7 @@ def test_full_config_sampled_rows(gpu_lib, name, Bq, which):
     qd, kd, vd = q.to(d), k.to(d), v.to(d)
     reorder = layout == "tile"
     tiles = vsa.vsa_classify_tiles(g, layout, masks, Bq, cfg["Bk"], device=d, with_cls=False)
-    words = vsa.vsa_boundary_words(g, layout, masks, tiles)
+    words = vsa.vsa_boundary_words(g, layout, masks, tiles, cap=tiles["nK"])
     o, lse = vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles, words=words,
                                      flags=vsa.VSA_FWD_WRITE_LSE | (vsa.VSA_FWD_REORDER_IO if reorder else 0))
     torch.cuda.synchronize()
@@ -259,7 +259,7 @@ def test_full_config_position_major_sampled_rows(gpu_lib):
     say(f"full config {name} position-major temporal heads Bq={Bq}")
     d = dev()
     tiles = vsa.vsa_classify_tiles(g, "frame", masks, Bq, cfg["Bk"], device=d, with_cls=False)
-    words = vsa.vsa_boundary_words(g, "frame", masks, tiles)
+    words = vsa.vsa_boundary_words(g, "frame", masks, tiles, cap=tiles["nK"])
     o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "frame", masks, tiles, words=words,
                                      flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
     torch.cuda.synchronize()
@@ -336,7 +336,7 @@ def test_full_config_padded_sampled_rows(gpu_lib):
     q, k, v = W.qkv(cfg["B"], S, cfg["H"], cfg["D"], cfg["dtype"], seed=cfg["seed"])
     d = dev()
     tiles = vsa.vsa_classify_tiles(g, "padded", masks, Bq, cfg["Bk"], device=d, with_cls=False)
-    words = vsa.vsa_boundary_words(g, "padded", masks, tiles)
+    words = vsa.vsa_boundary_words(g, "padded", masks, tiles, cap=tiles["nK"])
     o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "padded", masks, tiles, words=words,
                                      flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
     torch.cuda.synchronize()
@@ -387,7 +387,7 @@ def test_full_config_stripes_chosen_orders_sampled_rows(gpu_lib):
     lays = W.head_layouts(masks, "frame")
     say(f"full config {name} chosen orders {sorted(set(lays))} grid tile {g['tile_t'], g['tile_h'], g['tile_w']}")
     tiles = vsa.vsa_classify_tiles(g, "frame", masks, cfg["Bq"], cfg["Bk"], device=d, with_cls=False)
-    words = vsa.vsa_boundary_words(g, "frame", masks, tiles)
+    words = vsa.vsa_boundary_words(g, "frame", masks, tiles, cap=tiles["nK"])
     o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "frame", masks, tiles, words=words,
                                      flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
     torch.cuda.synchronize()

@@ -168,7 +168,7 @@ def test_forward_with_words_full_config(gpu_lib, name):
     words = vsa.vsa_boundary_words(g, layout, masks, tiles, cap=cap)
     o1, _ = vsa.vsa_sparse_attn_fwd(q, k, v, g, layout, masks, tiles, words=words)
     del words
-    full = vsa.vsa_boundary_words(g, layout, masks, tiles)  # cap = nK
+    full = vsa.vsa_boundary_words(g, layout, masks, tiles, cap=tiles["nK"])
     o2, _ = vsa.vsa_sparse_attn_fwd(q, k, v, g, layout, masks, tiles, words=full)
     torch.cuda.synchronize()
     if layout == "padded":
