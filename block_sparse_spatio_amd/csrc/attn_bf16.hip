@@ -328,8 +328,8 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 
     // stage A.  On the last tile the product runs on the stale buffer and is discarded:
     // keeping it unconditional keeps the stage straight-line code.  Chunk i issues the
-    // operand read of MFMA i+2, MFMA i, and the exponentials of EA scores; scheduling
-    // fences between chunks keep that order, so every LDS read has two MFMAs to land.
+    // operand read of MFMA i+3, MFMA i, and the exponentials of EA scores; scheduling
+    // fences between chunks keep that order, so every LDS read has three MFMAs to land.
     f32x16 s_next[2] = {f32x16{}, f32x16{}};
     bf16x2 pk[16];  // P(it): pk[v/2] holds scores v, v+1 (v = kb*16 + register)
     // Issue priority: the other wave on this SIMD is usually in the opposite stage, and
@@ -337,13 +337,14 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     // vector unit and the matrix core fed while stage B streams MFMAs.
     __builtin_amdgcn_s_setprio(1);
     {
-      u32x4 kr[3];
+      u32x4 kr[4];
       kr[0] = kread(k_use, 0);
       kr[1] = kread(k_use, 1);
+      kr[2] = kread(k_use, 2);
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
-        if (i + 2 < NQK) kr[(i + 2) % 3] = kread(k_use, i + 2);
-        s_next[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[i % 3]),
+        if (i + 3 < NQK) kr[(i + 3) % 4] = kread(k_use, i + 3);
+        s_next[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[i % 4]),
                                                                 qf[i >> 1], s_next[i & 1], 0, 0, 0);
         if (i % (NQK / C::NI) == 0) {
           const int d = i / (NQK / C::NI);
@@ -367,19 +368,20 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     // masks (boundary successor) and max-reduces EB scores of S(it+1)
     __builtin_amdgcn_s_setprio(0);
     {
-      u32x4 vr[3];
+      u32x4 vr[4];
       vr[0] = vread(v_use, 0);
       vr[1] = vread(v_use, 1);
+      vr[2] = vread(v_use, 2);
       float mx = -INFINITY;
       const uint32_t w = w_next;
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
-        if (i + 2 < NPV) vr[(i + 2) % 3] = vread(v_use, i + 2);
+        if (i + 3 < NPV) vr[(i + 3) % 4] = vread(v_use, i + 3);
         const int j = i / DB, db = i % DB;
         const bf16x8 pf = __builtin_bit_cast(
             bf16x8, u32x4{__builtin_bit_cast(uint32_t, pk[4 * j + 0]), __builtin_bit_cast(uint32_t, pk[4 * j + 1]),
                           __builtin_bit_cast(uint32_t, pk[4 * j + 2]), __builtin_bit_cast(uint32_t, pk[4 * j + 3])});
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i % 3]), pf, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i % 4]), pf, acc[db], 0, 0, 0);
         if (i % (NPV / C::NI) == 0) {
           const int d = i / (NPV / C::NI);
           dma16(vsrc, dma_v[d], vl0 + d * 1024);
