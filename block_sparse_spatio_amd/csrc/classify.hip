@@ -8,8 +8,9 @@
 // tile masked only at the padding) when at least half of its real pairs are kept,
 // and empty otherwise.
 //
-// One workgroup per (query tile, mask).  The query range's boxes are computed once;
-// each thread classifies key tiles with interval arithmetic (vsa_geom.h), and a
+// One workgroup per (query tile, mask).  The query range's boxes are computed once, into
+// LDS; each thread classifies key tiles with interval arithmetic (vsa_geom.h), visiting
+// the key tile's boxes one at a time so that nothing is held in private memory, and a
 // workgroup-wide prefix count keeps the lists in ascending key-tile order.
 // HBM-bound on the class map and list writes; integer-exact.
 #include "vsa_geom.h"
@@ -33,13 +34,27 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
   const Geom g = head_geom(g_call, m);
   const int r0 = qt * Bq;
   const int r1 = imin(r0 + Bq, g.S);
-  bool q_padded = (r0 + Bq) > g.S;
 
-  // boxes of the query tile's real tokens (padding of a padded grid is never kept)
-  Box R[11];
-  int nr = decompose(g, r0, r1, R);
-  if (g.padded) nr = clip_real(g, R, nr, q_padded);
+  // boxes of the query tile's real tokens (padding of a padded grid is never kept), the
+  // same for every thread: built once into LDS
+  __shared__ Box s_R[11];
+  __shared__ int s_nr, s_qpad;
+  if (threadIdx.x == 0) {
+    int nr = 0;
+    bool qp = (r0 + Bq) > g.S;
+    for_each_box(g, r0, r1, [&](Box b) {
+      if (!g.padded || clip_box(g, b, qp)) s_R[nr++] = b;
+    });
+    s_nr = nr;
+    s_qpad = qp;
+  }
+  __syncthreads();
+  const int nr = s_nr;
+  const bool q_padded = s_qpad;
+  const Box* R = s_R;
+  int q0 = 0, q1 = 0;
   long long q_real = 0;
+  if (nr > 0) frame_range(R, nr, q0, q1);
   for (int i = 0; i < nr; ++i) q_real += box_volume(R[i]);
 
   __shared__ int s_cnt[2][kWaves];
@@ -57,19 +72,15 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
     if (kt < nK) {
       const int c0 = kt * Bk;
       const int c1 = imin(c0 + Bk, g.S);
-      Box C[11];
-      int nc = decompose(g, c0, c1, C);
       bool padded = q_padded || (c0 + Bk) > g.S;
-      if (g.padded) nc = clip_real(g, C, nc, padded);
-      c = tile_class(g, m, R, nr, C, nc, padded);
+      c = tile_class_range(g, m, R, nr, q0, q1, c0, c1, padded);
       if (round_tiles && c == VSA_TILE_BOUNDARY) {
         // tile-aligned rounding: keep the tile's real pairs iff at least half are kept
         // kept pairs: summed over box pairs where the predicate is a product over the
         // axes, else per-row popcounts of the exact row masks (Bk <= 64)
         long long kept = 0, k_real = 0;
-        bool by_boxes = m.kind != VSA_MASK_STRIPE;
-        for (int i = 0; by_boxes && i < nr; ++i)
-          for (int j = 0; j < nc; ++j) kept += box_pair_kept(g, m, R[i], C[j]);
+        const bool by_boxes = m.kind != VSA_MASK_STRIPE;
+        tile_counts(g, m, R, nr, c0, c1, by_boxes, kept, k_real, padded);
         if (!by_boxes) {
           for (int r = r0; r < r1; ++r) {
             if (g.padded) {  // padding query rows hold no pair
@@ -80,7 +91,6 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
             kept += __popcll(tile_row_mask(g, m, make_query(g, m, r), c0, c1 - c0));
           }
         }
-        for (int j = 0; j < nc; ++j) k_real += box_volume(C[j]);
         const long long real = q_real * k_real;
         c = 2 * kept >= real ? (padded ? VSA_TILE_BOUNDARY : VSA_TILE_FULL) : VSA_TILE_EMPTY;
       }

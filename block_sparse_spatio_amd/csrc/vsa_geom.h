@@ -81,144 +81,150 @@ VSA_HD int frame_index(const Geom& g, int p) {
   return (t * g.Hg + y) * g.Wg + x;
 }
 
-// Digits of the executed order, most significant first.
-VSA_HD int order_digits(const Geom& g, int* radix) {
-  if (g.layout == VSA_LAYOUT_FRAME_MAJOR) {
-    radix[0] = g.T; radix[1] = g.Hg; radix[2] = g.Wg;
-    return 3;
+// ---------------------------------------------------------------------------
+// boxes of a run of executed positions
+// ---------------------------------------------------------------------------
+// Each order is a mixed-radix numbering with six digits, most significant first:
+// frame-major (T, Hg, Wg, 1, 1, 1), tile-major (nT, nH, nW, bt, bh, bw), and the part of
+// the position-major order after its frame-0 block (Hg, Wg, T-1, 1, 1, 1), whose frame-0
+// block is frame-major.  Axis a is digit a times mul[a] plus digit a+3; `pm` orders
+// the axes (y, x, t-1) instead of (t, y, x).
+struct Order {
+  int radix[6];
+  int mul[3];
+  bool pm;
+};
+
+VSA_HD Order main_order(const Geom& g) {
+  Order o;
+  if (g.layout == VSA_LAYOUT_TILE_MAJOR) {
+    o.radix[0] = g.nT; o.radix[1] = g.nH; o.radix[2] = g.nW;
+    o.radix[3] = g.bt; o.radix[4] = g.bh; o.radix[5] = g.bw;
+    o.mul[0] = g.bt; o.mul[1] = g.bh; o.mul[2] = g.bw;
+  } else {  // frame-major, and the frame-0 block of the position-major order
+    o.radix[0] = g.T; o.radix[1] = g.Hg; o.radix[2] = g.Wg;
+    o.radix[3] = o.radix[4] = o.radix[5] = 1;
+    o.mul[0] = o.mul[1] = o.mul[2] = 1;
   }
-  radix[0] = g.nT; radix[1] = g.nH; radix[2] = g.nW;
-  radix[3] = g.bt; radix[4] = g.bh; radix[5] = g.bw;
-  return 6;
+  o.pm = false;
+  return o;
 }
 
-// Digit intervals of the positions [cur, cur + cnt*W[j+1]) given cur's digits d (most
-// significant first): digits < j are those of cur, digit j runs over cnt values from
-// d[j], and digits > j are full.
-VSA_HD void digit_ranges(int n, const int* radix, const int* d, int j, int cnt, int* lo, int* hi) {
-  for (int k = 0; k < n; ++k) {
-    if (k < j) { lo[k] = d[k]; hi[k] = d[k]; }
-    else if (k == j) { lo[k] = d[k]; hi[k] = d[k] + cnt - 1; }
-    else { lo[k] = 0; hi[k] = radix[k] - 1; }
-  }
+VSA_HD Order pm_rest_order(const Geom& g) {
+  Order o;
+  o.radix[0] = g.Hg; o.radix[1] = g.Wg; o.radix[2] = g.T - 1;
+  o.radix[3] = o.radix[4] = o.radix[5] = 1;
+  o.mul[0] = o.mul[1] = o.mul[2] = 1;
+  o.pm = true;
+  return o;
 }
 
-VSA_HD Box level_box(const Geom& g, int n, const int* radix, const int* d, int j, int cnt) {
-  int lo[6], hi[6];
-  digit_ranges(n, radix, d, j, cnt, lo, hi);
-  Box b;
-  if (n == 3) {
-    b.t0 = lo[0]; b.t1 = hi[0]; b.y0 = lo[1]; b.y1 = hi[1]; b.x0 = lo[2]; b.x1 = hi[2];
-  } else {
-    // axis a: tile digit a, in-tile digit a+3.  When the tile digit is an interval the
-    // in-tile digit is full, so each axis is a single coordinate interval.
-    b.t0 = lo[0] * g.bt + lo[3]; b.t1 = hi[0] * g.bt + hi[3];
-    b.y0 = lo[1] * g.bh + lo[4]; b.y1 = hi[1] * g.bh + hi[4];
-    b.x0 = lo[2] * g.bw + lo[5]; b.x1 = hi[2] * g.bw + hi[5];
-  }
-  return b;
-}
-
-// Position-major: boxes of the digits (y, x, t-1) with radices (Hg, Wg, T-1) inside the
-// part after the frame-0 block.
-VSA_HD Box pm_box(const int* radix, const int* d, int j, int cnt) {
-  int lo[3], hi[3];
-  digit_ranges(3, radix, d, j, cnt, lo, hi);
-  Box b;
-  b.y0 = lo[0]; b.y1 = hi[0]; b.x0 = lo[1]; b.x1 = hi[1];
-  b.t0 = lo[2] + 1; b.t1 = hi[2] + 1;
-  return b;
-}
-
-// Split positions [lo, end) of a mixed-radix order (radix[0] most significant, W[k] the
-// weight of digit k - 1) into at most 2n-1 boxes, each a run of one digit with the
-// coarser digits fixed and the finer ones full.  The digits of the running position are
-// carried along, so only the starting digits and the descending counts divide.
-template <typename BoxFn>
-VSA_HD int decompose_radix(int n, const int* radix, int lo, int end, Box* out, BoxFn box) {
-  int W[7];
-  W[n] = 1;
-  for (int k = n - 1; k >= 0; --k) W[k] = W[k + 1] * radix[k];
-  if (lo >= end) return 0;
+// Visit the boxes of positions [lo, end) of one order, in ascending position order.
+// Each box is a run of one digit with the coarser digits fixed and the finer ones full,
+// taken at the coarsest digit that the running position is aligned to and whose unit
+// still fits before `end` (the mixed-radix range decomposition: at most 2*6-1 boxes, at
+// most 5 for three-digit orders).  The digit arrays are indexed by unrolled loop
+// counters only, so on the GPU they stay in registers.
+template <typename Emit>
+VSA_HD void order_boxes(const Order& o, int lo, int end, Emit&& emit) {
+  if (lo >= end) return;
+  int W[7];  // W[k + 1]: weight of digit k
+  W[6] = 1;
+#pragma unroll
+  for (int k = 5; k >= 0; --k) W[k] = W[k + 1] * o.radix[k];
   int d[6];
-  for (int k = n - 1, x = lo; k >= 0; --k) {
-    const int q = x / radix[k];
-    d[k] = x - q * radix[k];
-    x = q;
-  }
-  int nb = 0, cur = lo;
-  // ascending: align cur to ever coarser digit boundaries (the digits finer than j are
-  // already zero)
-  int j = n - 1;
-  for (; j >= 0; --j) {
-    const int cnt = d[j] == 0 ? 0 : radix[j] - d[j];
-    const int next = cur + cnt * W[j + 1];
-    if (next > end) break;
-    if (cnt > 0) {
-      out[nb++] = box(d, j, cnt);
-      cur = next;
-      d[j] = 0;  // digit j wraps and carries into the coarser digits
-      for (int k = j - 1; k >= 0; --k) {
-        if (++d[k] < radix[k]) break;
+  {
+    int x = lo;
+#pragma unroll
+    for (int k = 5; k >= 0; --k) {
+      if (o.radix[k] > 1) {
+        const int q = x / o.radix[k];
+        d[k] = x - q * o.radix[k];
+        x = q;
+      } else {
         d[k] = 0;
       }
     }
-    if (cur == end) return nb;
   }
-  if (j < 0) j = 0;
-  // descending: whole runs of digit j, then finer digits (no carry: the run stays below
-  // the next boundary of digit j)
-  for (; j < n && cur < end; ++j) {
-    const int cnt = (end - cur) / W[j + 1];
-    if (cnt > 0) {
-      out[nb++] = box(d, j, cnt);
-      cur += cnt * W[j + 1];
-      d[j] += cnt;
+  int cur = lo;
+#pragma nounroll
+  while (cur < end) {
+    const int rem = end - cur;
+    int jnz = 0;  // finest nonzero digit: cur is aligned to the weight of every digit >= jnz
+#pragma unroll
+    for (int k = 0; k < 6; ++k)
+      if (d[k] != 0) jnz = k;
+    int j = 5, w = 1, r = 1, dj = 0;  // the run's digit, its weight, radix and start
+#pragma unroll
+    for (int k = 5; k >= 0; --k)
+      if (k >= jnz && W[k + 1] <= rem) { j = k; w = W[k + 1]; r = o.radix[k]; dj = d[k]; }
+    const int cnt = imin(r - dj, rem / w);
+    // digits > j are zero (aligned); the box spans d..hi per digit
+    int A0[3], A1[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const int h0 = a < j ? d[a] : (a == j ? d[a] + cnt - 1 : o.radix[a] - 1);
+      const int h1 = a + 3 < j ? d[a + 3] : (a + 3 == j ? d[a + 3] + cnt - 1 : o.radix[a + 3] - 1);
+      A0[a] = d[a] * o.mul[a] + d[a + 3];
+      A1[a] = h0 * o.mul[a] + h1;
+    }
+    Box b;
+    if (o.pm) {
+      b.t0 = A0[2] + 1; b.t1 = A1[2] + 1; b.y0 = A0[0]; b.y1 = A1[0]; b.x0 = A0[1]; b.x1 = A1[1];
+    } else {
+      b.t0 = A0[0]; b.t1 = A1[0]; b.y0 = A0[1]; b.y1 = A1[1]; b.x0 = A0[2]; b.x1 = A1[2];
+    }
+    emit(b);
+    cur += cnt * w;
+    int carry = 0;  // digit j advances by cnt, carrying into the coarser digits
+#pragma unroll
+    for (int k = 5; k >= 0; --k) {
+      const int v = d[k] + (k == j ? cnt : 0) + carry;
+      carry = v >= o.radix[k] ? 1 : 0;
+      d[k] = carry ? v - o.radix[k] : v;
     }
   }
-  return nb;
 }
 
-VSA_HD int decompose_pm_rest(const Geom& g, int lo, int end, Box* out) {
-  const int radix[3] = {g.Hg, g.Wg, g.T - 1};
-  return decompose_radix(3, radix, lo, end, out,
-                         [&](const int* d, int j, int cnt) { return pm_box(radix, d, j, cnt); });
-}
-
-// Split positions [lo, end) of a frame- or tile-major order into at most 2n-1 boxes
-// (mixed-radix range decomposition).
-VSA_HD int decompose_mixed(const Geom& g, int lo, int end, Box* out) {
-  int radix[6];
-  const int n = order_digits(g, radix);
-  return decompose_radix(n, radix, lo, end, out,
-                         [&](const int* d, int j, int cnt) { return level_box(g, n, radix, d, j, cnt); });
-}
-
-// Split executed positions [lo, end) into boxes: at most 2n-1 for frame- and
-// tile-major orders, at most 10 for position-major (frame-0 block, then the rest).
-VSA_HD int decompose(const Geom& g, int lo, int end, Box* out) {
-  if (g.layout != VSA_LAYOUT_POSITION_MAJOR) return decompose_mixed(g, lo, end, out);
-  int nb = 0;
-  if (lo < g.HW) {
-    Geom f = g;
-    f.layout = VSA_LAYOUT_FRAME_MAJOR;  // positions below HW are frame 0 in frame-major order
-    nb = decompose_mixed(f, lo, imin(end, g.HW), out);
+// Visit the boxes of executed positions [lo, end): at most 11 for frame- and tile-major
+// orders, at most 10 for position-major (frame-0 block, then the rest).  One loop over
+// the (at most two) segments, so `emit` is expanded once.
+template <typename Emit>
+VSA_HD void for_each_box(const Geom& g, int lo, int end, Emit&& emit) {
+  const bool pm = g.layout == VSA_LAYOUT_POSITION_MAJOR;
+  const int nseg = (pm && lo < g.HW && end > g.HW) ? 2 : 1;
+#pragma nounroll
+  for (int s = 0; s < nseg; ++s) {
+    const bool rest = pm && (s == 1 || lo >= g.HW);
+    const Order o = rest ? pm_rest_order(g) : main_order(g);
+    const int a = rest ? imax(lo, g.HW) - g.HW : lo;
+    const int b = rest ? end - g.HW : (pm ? imin(end, g.HW) : end);
+    order_boxes(o, a, b, emit);
   }
-  if (end > g.HW) nb += decompose_pm_rest(g, imax(lo, g.HW) - g.HW, end - g.HW, out + nb);
+}
+
+// The boxes of executed positions [lo, end) as an array (at most 11).
+VSA_HD int decompose(const Geom& g, int lo, int end, Box* out) {
+  int nb = 0;
+  for_each_box(g, lo, end, [&](const Box& b) { out[nb++] = b; });
   return nb;
 }
 
-// Padded grid: cut boxes of padded coordinates down to the real tokens, dropping
-// boxes with none; `clipped` is set when some position was padding.
+// Padded grid: cut a box of padded coordinates down to the real tokens; false when none
+// is left.  `clipped` is set when some position was padding.
+VSA_HD bool clip_box(const Geom& g, Box& c, bool& clipped) {
+  const int t1 = imin(c.t1, g.T - 1), y1 = imin(c.y1, g.Hg - 1), x1 = imin(c.x1, g.Wg - 1);
+  if (t1 != c.t1 || y1 != c.y1 || x1 != c.x1) clipped = true;
+  if (c.t0 > t1 || c.y0 > y1 || c.x0 > x1) return false;
+  c.t1 = t1; c.y1 = y1; c.x1 = x1;
+  return true;
+}
+
 VSA_HD int clip_real(const Geom& g, Box* b, int n, bool& clipped) {
   int k = 0;
   for (int i = 0; i < n; ++i) {
     Box c = b[i];
-    const int t1 = imin(c.t1, g.T - 1), y1 = imin(c.y1, g.Hg - 1), x1 = imin(c.x1, g.Wg - 1);
-    if (t1 != c.t1 || y1 != c.y1 || x1 != c.x1) clipped = true;
-    if (c.t0 > t1 || c.y0 > y1 || c.x0 > x1) continue;
-    c.t1 = t1; c.y1 = y1; c.x1 = x1;
-    b[k++] = c;
+    if (clip_box(g, c, clipped)) b[k++] = c;
   }
   return k;
 }
@@ -421,44 +427,88 @@ VSA_HD long long box_pair_kept(const Geom& g, const DevMask& m, const Box& r, Bo
   }
 }
 
+// Frame range [q0, q1] covered by boxes R[nr] (nr > 0).
+VSA_HD void frame_range(const Box* R, int nr, int& q0, int& q1) {
+  q0 = R[0].t0;
+  q1 = R[0].t1;
+  for (int i = 1; i < nr; ++i) { q0 = imin(q0, R[i].t0); q1 = imax(q1, R[i].t1); }
+}
+
+// Add key box c to a tile pair's class: `all` stays true while every pair seen is kept,
+// `any` turns true once one is.  R[nr] are the query boxes, [q0, q1] their frame range.
+VSA_HD void class_add(const Geom& g, const DevMask& m, const Box* R, int nr, int q0, int q1, Box c, bool& all,
+                      bool& any) {
+  if (nr == 0) return;
+  // Frame pre-test: with no sink frame in c and no pair of frames passing the temporal
+  // part of the mask, no pair with c is kept.
+  if (c.t0 >= m.sink && (m.kind == VSA_MASK_STRIPE || (m.kind == VSA_MASK_BOX && m.rt >= 0))) {
+    bool a, n;
+    if (m.kind == VSA_MASK_STRIPE)
+      periodic_test(c.t0 - q1, c.t1 - q0, m.To, m.Ts, m.Tw, a, n);
+    else
+      radius_test(c.t0 - q1, c.t1 - q0, m.rt, a, n);
+    if (!n) {
+      all = false;
+      return;
+    }
+  }
+  if (c.t0 < m.sink) {  // key frames below the sink are kept for every query
+    any = true;
+    if (c.t1 < m.sink) return;
+    c.t0 = m.sink;
+  }
+  for (int i = 0; i < nr; ++i) {
+    bool a, n;
+    box_pair_test(g, m, R[i], c, a, n);
+    all = all && a;
+    any = any || n;
+    if (!all && any) return;
+  }
+}
+
+VSA_HD int class_of(bool all, bool any, bool padded) {
+  if (!any) return VSA_TILE_EMPTY;
+  return (all && !padded) ? VSA_TILE_FULL : VSA_TILE_BOUNDARY;
+}
+
 // Tile class of query boxes R[nr] x key boxes C[nc] (padded: the tile reaches past S).
 VSA_HD int tile_class(const Geom& g, const DevMask& m, const Box* R, int nr, const Box* C, int nc,
                       bool padded) {
-  // Frame pre-test: when no key frame is a sink frame and no pair of the two tiles'
-  // frame ranges passes the temporal part of the mask, nothing is kept.  (Tiles of the
-  // position-major order span all frames, where the test never decides.)
-  if (g.layout != VSA_LAYOUT_POSITION_MAJOR && nr > 0 && nc > 0 &&
-      (m.kind == VSA_MASK_STRIPE || (m.kind == VSA_MASK_BOX && m.rt >= 0))) {
-    int q0 = R[0].t0, q1 = R[0].t1, k0 = C[0].t0, k1 = C[0].t1;
-    for (int i = 1; i < nr; ++i) { q0 = imin(q0, R[i].t0); q1 = imax(q1, R[i].t1); }
-    for (int j = 1; j < nc; ++j) { k0 = imin(k0, C[j].t0); k1 = imax(k1, C[j].t1); }
-    if (k0 >= m.sink) {
-      bool a, n;
-      if (m.kind == VSA_MASK_STRIPE)
-        periodic_test(k0 - q1, k1 - q0, m.To, m.Ts, m.Tw, a, n);
-      else
-        radius_test(k0 - q1, k1 - q0, m.rt, a, n);
-      if (!n) return VSA_TILE_EMPTY;
-    }
-  }
   bool all = true, any = false;
-  for (int i = 0; i < nr; ++i) {
-    for (int j = 0; j < nc; ++j) {
-      Box c = C[j];
-      if (c.t0 < m.sink) {  // key frames below the sink are kept for every query
-        any = true;
-        if (c.t1 < m.sink) continue;
-        c.t0 = m.sink;
-      }
-      bool a, n;
-      box_pair_test(g, m, R[i], c, a, n);
-      all = all && a;
-      any = any || n;
-      if (!all && any) return VSA_TILE_BOUNDARY;
-    }
-  }
-  if (!any) return VSA_TILE_EMPTY;
-  return (all && !padded) ? VSA_TILE_FULL : VSA_TILE_BOUNDARY;
+  if (nr == 0) return VSA_TILE_EMPTY;
+  int q0, q1;
+  frame_range(R, nr, q0, q1);
+  for (int j = 0; j < nc && (all || !any); ++j) class_add(g, m, R, nr, q0, q1, C[j], all, any);
+  return class_of(all, any, padded);
+}
+
+// Tile class of query boxes R[nr] (real tokens, frame range [q0, q1]) x the key tile of
+// executed positions [c0, c1), whose boxes are visited one at a time and clipped to the
+// real grid.  `padded`: the query tile or the key tile reaches past S.
+VSA_HD int tile_class_range(const Geom& g, const DevMask& m, const Box* R, int nr, int q0, int q1, int c0, int c1,
+                            bool padded) {
+  bool all = true, any = false;
+  if (nr == 0) return VSA_TILE_EMPTY;
+  for_each_box(g, c0, c1, [&](Box c) {
+    if (!all && any) return;  // boundary whatever follows
+    if (g.padded && !clip_box(g, c, padded)) return;
+    class_add(g, m, R, nr, q0, q1, c, all, any);
+  });
+  return class_of(all, any, padded);
+}
+
+// Real keys of the key tile [c0, c1) and, for masks that are a product over the axes,
+// its pairs kept with query boxes R[nr].  `padded` is set when a key position is padding.
+VSA_HD void tile_counts(const Geom& g, const DevMask& m, const Box* R, int nr, int c0, int c1, bool by_boxes,
+                        long long& kept, long long& k_real, bool& padded) {
+  kept = 0;
+  k_real = 0;
+  for_each_box(g, c0, c1, [&](Box c) {
+    if (g.padded && !clip_box(g, c, padded)) return;
+    k_real += box_volume(c);
+    if (by_boxes)
+      for (int i = 0; i < nr; ++i) kept += box_pair_kept(g, m, R[i], c);
+  });
 }
 
 // ---------------------------------------------------------------------------

@@ -1,11 +1,14 @@
 // Host build of the GPU classification geometry (vsa_geom.h) against brute force.
 //
 // For random grids, token orders (frame-, tile-, position-major, tile-major over a padded
-// grid), mask kinds and tile sizes, every (query tile, key tile) class of tile_class and
-// every kept-pair count of box_pair_kept is compared with an enumeration of all pairs
-// under a per-pair predicate written out here, and every bit of the 64-key row masks
-// (tile_row_mask, real_key_mask) with the same predicate.  The coordinates of the padded
-// and position-major orders are also checked against nested loops that state them.
+// grid), mask kinds and tile sizes: the boxes of every query and key range are checked
+// to hold exactly the range's positions; every (query tile, key tile) class and kept-pair
+// count, over box arrays (tile_class, box_pair_kept) and in the streamed form the GPU
+// kernel runs (tile_class_range, tile_counts), is compared with an enumeration of all
+// pairs under a per-pair predicate written out here; and every bit of the 64-key row
+// masks (tile_row_mask, real_key_mask) with the same predicate.  The coordinates of the
+// padded and position-major orders are also checked against nested loops that state
+// them.
 //
 // usage: geometry_check TRIALS SEED [focus]; "focus" draws one-column tiles and stripe
 // periods of one row or one frame (the closed-form stripe paths).  Exit status 1 on any
@@ -70,21 +73,36 @@ int main(int argc, char** argv){
         if(T[p]!=t||Y[p]!=s2/g.Wg||X[p]!=s2%g.Wg){ if(nbad<5) printf("BAD coords p %d\n",p); nbad++; } }
     }
     int nQ=(S+Bq-1)/Bq, nK=(S+Bk-1)/Bk;
+    // boxes of every query and key range: they hold exactly the range's positions
+    for(int pass=0;pass<2;++pass){ int B=pass?Bk:Bq;
+      for(int lo=0;lo<S;lo+=B){ int hi=std::min(S,lo+B); Box bx[64]; int nb=decompose(g,lo,hi,bx);  // at most one box per position (B <= 64)
+        long long vol=0; for(int i=0;i<nb;++i) vol+=box_volume(bx[i]);
+        bool ok = nb<=11 && vol==hi-lo;
+        for(int p=lo;p<hi&&ok;++p){ int in=0; for(int i=0;i<nb;++i) in += T[p]>=bx[i].t0&&T[p]<=bx[i].t1&&Y[p]>=bx[i].y0&&Y[p]<=bx[i].y1&&X[p]>=bx[i].x0&&X[p]<=bx[i].x1; ok = in==1; }
+        if(!ok){ if(nbad<5) printf("BAD boxes trial %d layout %d range [%d,%d) boxes %d volume %lld\n",trial,layout,lo,hi,nb,vol); nbad++; } } }
     for(int qt=0;qt<nQ;++qt){
       Box R[11]; int nr=decompose(g,qt*Bq,std::min(S,(qt+1)*Bq),R);
       bool qpad=(qt+1)*Bq>S;
       if(g.padded) nr=clip_real(g,R,nr,qpad);
+      int q0=0,q1=0; if(nr>0) frame_range(R,nr,q0,q1);
       for(int kt=0;kt<nK;++kt){
-        Box C[11]; int nc=decompose(g,kt*Bk,std::min(S,(kt+1)*Bk),C);
+        const int c0=kt*Bk, c1=std::min(S,(kt+1)*Bk);
+        Box C[11]; int nc=decompose(g,c0,c1,C);
         bool pad=qpad||(kt+1)*Bk>S;
+        bool pad_s=pad;  // the streamed form (the kernel's) sets its own copy
+        int cs = tile_class_range(g,m,R,nr,q0,q1,c0,c1,pad_s);
         if(g.padded) nc=clip_real(g,C,nc,pad);
         int c = tile_class(g,m,R,nr,C,nc,pad);
         long long kept=0;
         for(int i=qt*Bq;i<(qt+1)*Bq;++i) for(int j=kt*Bk;j<(kt+1)*Bk;++j) if(i<S&&j<S&&real[i]&&real[j]&&keep_bf(g,m,T[i],Y[i],X[i],T[j],Y[j],X[j])) kept++;
         int ref = kept==0?0:(kept==(long long)Bq*Bk?1:2);
+        long long kr=0; for(int j=kt*Bk;j<c1;++j) kr+=real[j];
+        long long ks=0, krs=0; bool pad_c=qpad||(kt+1)*Bk>S;
+        tile_counts(g,m,R,nr,c0,c1,m.kind!=2,ks,krs,pad_c);
+        if(krs!=kr||pad_c!=pad){ if(nbad<5) printf("BAD real keys trial %d layout %d kt %d got %lld ref %lld\n",trial,layout,kt,krs,kr); nbad++; }
         if(m.kind!=2){ long long kb=0; for(int i=0;i<nr;++i) for(int j=0;j<nc;++j) kb+=box_pair_kept(g,m,R[i],C[j]);
-          if(kb!=kept){ if(nbad<5) printf("BAD box count trial %d kind %d layout %d got %lld ref %lld\n",trial,m.kind,layout,kb,kept); nbad++; } }
-        ntile++; if(c!=ref){ if(nbad<5) printf("BAD class trial %d kind %d layout %d qt %d kt %d got %d ref %d\n",trial,m.kind,layout,qt,kt,c,ref); nbad++; }
+          if(kb!=kept||ks!=kept){ if(nbad<5) printf("BAD box count trial %d kind %d layout %d got %lld/%lld ref %lld\n",trial,m.kind,layout,kb,ks,kept); nbad++; } }
+        ntile++; if(c!=ref||cs!=ref){ if(nbad<5) printf("BAD class trial %d kind %d layout %d qt %d kt %d got %d/%d ref %d\n",trial,m.kind,layout,qt,kt,c,cs,ref); nbad++; }
       }
     }
     // element masks for tiles of 64 keys
