@@ -5,15 +5,16 @@
 // head is routed to the candidate with the smallest deviation ("supporting dynamic
 // routing with fixed tensor shapes": one flag per head, no variable-size head groups).
 //
-// Pass 1 (profile_part_kernel): one workgroup per (candidate, key chunk, b, h).  It
-// holds the sampled query rows of (b, h) in registers (32 per wave) and runs the
-// attention pipeline of the bf16 forward kernel over its chunk of key tiles: K and V
-// tiles reach LDS by DMA, double-buffered, S^T = K Q^T on the matrix cores overlaps the
-// softmax of the previous tile, and the candidate's element mask applies to every tile
-// (the all-keep reference only at the sequence tail).  V stays row-major and is read
-// with transposing LDS reads.  The chunk's unnormalised output, running max and row
-// sum go to the workspace.  The candidates of one (chunk, b, h) are adjacent on one
-// XCD, so K and V are fetched from memory about once and re-read from that XCD's L2.
+// Pass 1 (profile_part_kernel): one workgroup per (sample group, key chunk, b, h), with
+// one group of waves per candidate.  Each wave holds 32 sampled query rows of (b, h) in
+// registers and runs the attention pipeline of the bf16 forward kernel over the chunk's
+// key tiles: K and V tiles reach LDS by DMA (issued by the first 2, 4 or 8 waves),
+// double-buffered and shared by every candidate, S^T = K Q^T on the matrix cores
+// overlaps the softmax of the previous tile, and the wave's candidate mask applies to
+// every tile (the all-keep reference only at the sequence tail).  V stays row-major and
+// is read with transposing LDS reads.  The chunk's unnormalised output, running max and
+// row sum go to the workspace.  At most 8 waves per workgroup (two per SIMD); the
+// sample groups of one (chunk, b, h) are adjacent on one XCD.
 // Pass 2 (profile_merge_kernel, profile_route_kernel): groups of 16 samples merge their
 // chunk partials with the softmax statistics (lanes over channels) into sums of
 // (o_c - o_0)^2; per head these are added in a fixed order, err[h][c] = sqrt(.) and
@@ -31,10 +32,16 @@ using namespace pipe;
 template <int D>
 constexpr int kProfRow = D + 4;
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// waves that issue a workgroup's K/V DMAs: the largest power of two up to its waves
+constexpr int dma_waves(int nw) { return nw >= 8 ? 8 : (nw >= 4 ? 4 : 2); }
+
+template <int D, int NWS, int NC>
+__global__ __launch_bounds__(NWS * NC * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void profile_part_kernel(ProfArgs a, MaskTable cands) {
-  using C = Cfg<D, NW>;
+  constexpr int NWT = NWS * NC;  // NWS waves of 32 samples per candidate
+  constexpr int SG = NWS * 32;   // samples per workgroup
+  constexpr int NWD = dma_waves(NWT);
+  using C = Cfg<D, NWD>;
   constexpr int KSTEPS = C::KSTEPS;
   constexpr int DB = C::DB;
   constexpr int NI = C::NI;
@@ -44,28 +51,32 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   __shared__ __attribute__((aligned(1024))) char vbuf1[C::TILE_B];
 
   const Geom& g = a.g;
-  const int S = a.S, H = a.H, n = a.n, NC = a.n_cand;
-  // workgroup -> (candidate, chunk, b, h): XCD x = blockIdx & 7 takes units u = j*8 + x
-  // of (chunk, b*H + h), each as NC consecutive workgroups
+  const int S = a.S, H = a.H, n = a.n;
+  const int n_sg = (n + SG - 1) / SG;
+  // workgroup -> (sample group, chunk, b, h): XCD x = blockIdx & 7 takes units u = j*8 + x
+  // of (chunk, b*H + h), each as n_sg consecutive workgroups
   const int xcd = blockIdx.x & 7;
   const int local = blockIdx.x >> 3;
-  const int c = local % NC;
-  const int u = (local / NC) * 8 + xcd;
+  const int sg = local % n_sg;
+  const int u = (local / n_sg) * 8 + xcd;
   if (u >= a.n_chunks * a.B * H) return;
   const int chunk = u % a.n_chunks;
   const int bh = u / a.n_chunks;
   const int h = bh % H, b = bh / H;
-  const DevMask m = cands.m[c];
   const int nK = (S + BK - 1) / BK;
   const int kt_begin = chunk * a.chunk_tiles;
   const int n_tiles = imax(imin(nK, kt_begin + a.chunk_tiles) - kt_begin, 0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = wv / NWS;                    // this wave's candidate
+  const bool dma_wave = wv < dma_waves(NWT);
+  const int wave = dma_wave ? wv : 0;        // DMA slot (unused by the other waves)
+  const DevMask m = cands.m[c];
   const int g2 = lane >> 5;
   const int l32 = lane & 31;
-  const int si = wave * 32 + l32;  // sample slot of this lane's query row
+  const int si = sg * SG + (wv % NWS) * 32 + l32;  // sample slot of this lane's query row
   const int qrow = imin(imax(a.sample_idx[(size_t)h * n + imin(si, n - 1)], 0), S - 1);
 
   const uint16_t* qp = (const uint16_t*)a.q;
@@ -88,7 +99,7 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
     const int R = (wave * NI + i) * C::ROWS_PER_DMA + lane / C::CH;
     const int p = lane % C::CH;
     return is_v ? imin(R, lim) * tok_stride + (p ^ vsw<D>(R)) * 8
-                : imin(swap_bits23(R), lim) * tok_stride + (p ^ ksw<D, NW>(R)) * 8;
+                : imin(swap_bits23(R), lim) * tok_stride + (p ^ ksw<D, NWD>(R)) * 8;
   };
   // Whole-tile DMA offsets, split into a wave-uniform part (added to the scalar base)
   // and a per-lane part, which the DMA takes as an unsigned 32-bit offset and so must
@@ -111,7 +122,7 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   const int vtab = 2 * dma_off(-wave * NI, true, BK);  // DMA j = 0; V's lane part is the same for all j
   int kofs[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) kofs[s] = l32 * C::ROWB + (((2 * s + g2) ^ ksw<D, NW>(l32)) * 16);
+  for (int s = 0; s < KSTEPS; ++s) kofs[s] = l32 * C::ROWB + (((2 * s + g2) ^ ksw<D, NWD>(l32)) * 16);
   // transposing V reads: within 16 lanes, lane i gets element i%4 of rows 4e + i/4
   int vofs[DB];
   {
@@ -127,6 +138,7 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
 
   // DMA of the K (or V) rows of key tile kt; rows past S read row S-1 (masked keys)
   auto issue = [&](int kt, char* buf, bool is_v) __attribute__((always_inline)) {
+    if (!dma_wave) return;
     const int c0 = kt * BK;
     const uint16_t* src = (is_v ? vp : kp) + base_bh + (size_t)c0 * tok_stride;
     const uint32_t lds0 = lds_addr(buf + wave * NI * 1024);
@@ -416,12 +428,14 @@ __global__ __launch_bounds__(64) void profile_route_kernel(ProfArgs a, int G) {
   a.route[h] = best;
 }
 
-template <int D, int NW, int NC>
+template <int D, int NWS, int NC>
 hipError_t launch_t(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
   const long long units = (long long)a.n_chunks * a.B * a.H;
-  const long long blocks = ((units + 7) / 8) * 8 * NC;
+  const int n_sg = (a.n + NWS * 32 - 1) / (NWS * 32);
+  const long long blocks = ((units + 7) / 8) * 8 * n_sg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((profile_part_kernel<D, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a, cands);
+  hipLaunchKernelGGL((profile_part_kernel<D, NWS, NC>), dim3((unsigned)blocks), dim3(NWS * NC * 64), 0, st, a,
+                     cands);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = (a.n + kMergeSamples - 1) / kMergeSamples;
@@ -433,13 +447,12 @@ hipError_t launch_t(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
 
 template <int D, int NC>
 hipError_t launch_nw(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
-  const int nw = (a.n + 31) / 32;
-  switch (nw) {
+  switch (profile_sample_waves(a.n, NC)) {
     case 1: return launch_t<D, 1, NC>(a, cands, st);
     case 2: return launch_t<D, 2, NC>(a, cands, st);
-    case 3:
-    case 4: return launch_t<D, 4, NC>(a, cands, st);
-    default: return launch_t<D, 8, NC>(a, cands, st);
+    default:
+      if constexpr (NC == 2) return launch_t<D, 4, NC>(a, cands, st);
+      return hipErrorInvalidValue;
   }
 }
 
@@ -455,13 +468,33 @@ hipError_t launch_nc(const ProfArgs& a, const MaskTable& cands, hipStream_t st) 
 
 }  // namespace
 
-int32_t profile_chunks(int32_t B, int32_t S, int32_t H) {
+int32_t profile_sample_waves(int32_t n, int32_t n_cand) {
+  const int cap = n_cand <= 2 ? 4 : 2;  // at most 8 waves per workgroup
+  const int need = (n + 31) / 32;
+  return need <= 1 ? 1 : (need <= 2 || cap == 2 ? 2 : 4);
+}
+
+// Key chunks per (b, h): the count that minimises rounds of resident workgroups times
+// key tiles per chunk (fewest chunks on ties), with 256 compute units holding one
+// workgroup of more than 4 waves or two smaller ones (LDS and registers), and at most
+// 8192 workgroups.
+int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t n, int32_t n_cand) {
   const int nK = (S + pipe::BK - 1) / pipe::BK;
-  const long long bh = (long long)B * H;
-  int chunks = (int)((1024 + bh - 1) / bh);
-  if (chunks < 1) chunks = 1;
-  if (chunks > nK) chunks = nK;
-  return chunks;
+  const int nws = profile_sample_waves(n, n_cand);
+  const long long per_chunk = (long long)B * H * ((n + nws * 32 - 1) / (nws * 32));
+  const long long slots = 256LL * (nws * n_cand > 4 ? 1 : 2);
+  const long long lim = 8192 / (per_chunk > 0 ? per_chunk : 1);
+  const long long c_max = lim < 1 ? 1 : (lim < nK ? lim : nK);
+  int best = 1;
+  long long best_cost = -1;
+  for (long long c = 1; c <= c_max; ++c) {
+    const long long cost = ((c * per_chunk + slots - 1) / slots) * ((nK + c - 1) / c);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = (int)c;
+    }
+  }
+  return best;
 }
 
 size_t profile_ws_floats(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand,

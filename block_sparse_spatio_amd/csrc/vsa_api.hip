@@ -543,7 +543,7 @@ vsa_status vsa_profile_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t 
   if (!bytes) return fail(VSA_ERR_INVALID_ARG, "bytes is NULL");
   if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || n_samples <= 0 || n_cand <= 0)
     return fail(VSA_ERR_INVALID_ARG, "sizes must be positive");
-  *bytes = vsa::profile_ws_floats(B, H, D, n_samples, n_cand, vsa::profile_chunks(B, S, H)) * sizeof(float);
+  *bytes = vsa::profile_ws_floats(B, H, D, n_samples, n_cand, vsa::profile_chunks(B, S, H, n_samples, n_cand)) * sizeof(float);
   return ok();
 }
 
@@ -577,7 +577,7 @@ vsa_status vsa_profile_heads(const void* q, const void* k, const void* v, vsa_dt
   }
   vsa::ProfArgs a;
   memset(&a, 0, sizeof a);
-  a.n_chunks = vsa::profile_chunks(B, S, H);
+  a.n_chunks = vsa::profile_chunks(B, S, H, n_samples, n_cand);
   const size_t need = vsa::profile_ws_floats(B, H, D, n_samples, n_cand, a.n_chunks) * sizeof(float);
   if (!workspace || ws_bytes < need)
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);

@@ -155,7 +155,8 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 size_t profile_ws_floats(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand,
                          int32_t n_chunks);
-int32_t profile_chunks(int32_t B, int32_t S, int32_t H);
+int32_t profile_sample_waves(int32_t n, int32_t n_cand);
+int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t n, int32_t n_cand);
 hipError_t launch_profile(const ProfArgs& a, const MaskTable& cands, hipStream_t stream);
 
 }  // namespace vsa

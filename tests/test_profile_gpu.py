@@ -55,7 +55,7 @@ def test_profiler_constructed_winner(gpu_lib, by, winner):
     _check(err, route, err_o, route_o)
 
 
-@pytest.mark.parametrize("n,nc", [(16, 2), (64, 3), (100, 4), (256, 3)])
+@pytest.mark.parametrize("n,nc", [(16, 2), (20, 3), (32, 4), (64, 3), (100, 4), (128, 2), (200, 2), (256, 3)])
 def test_profiler_iid_small(gpu_lib, n, nc):
     g = W.grid(6, 12, 14)
     S = W.seq_len(g)
