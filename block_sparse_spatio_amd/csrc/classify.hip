@@ -34,6 +34,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
   const Geom g = head_geom(g_call, m);
   const int r0 = qt * Bq;
   const int r1 = imin(r0 + Bq, g.S);
+  const PairDivs dv = pair_divs(g, m);
 
   // boxes of the query tile's real tokens (padding of a padded grid is never kept), the
   // same for every thread: built once into LDS
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
       const int c0 = kt * Bk;
       const int c1 = imin(c0 + Bk, g.S);
       bool padded = q_padded || (c0 + Bk) > g.S;
-      c = tile_class_range(g, m, R, nr, q0, q1, c0, c1, padded);
+      c = tile_class_range(g, m, dv, R, nr, q0, q1, c0, c1, padded);
       if (round_tiles && c == VSA_TILE_BOUNDARY) {
         // tile-aligned rounding: keep the tile's real pairs iff at least half are kept
         // kept pairs: summed over box pairs where the predicate is a product over the

@@ -236,14 +236,53 @@ VSA_HD long long box_volume(const Box& b) {
 // ---------------------------------------------------------------------------
 // predicates over intervals of a coordinate difference
 // ---------------------------------------------------------------------------
+// Division by a positive divisor that stays fixed over many calls (a mask's period, the
+// grid width): floor(n / d) for every 32-bit unsigned n by one multiply-high, a
+// subtraction, an addition and two shifts (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, unsigned division of section 4):
+// with l = ceil(log2 d), mul = floor(2^32 (2^l - d) / d) + 1.
+struct Divisor {
+  uint32_t d, mul;
+  int s1, s2;
+};
+
+VSA_HD Divisor make_divisor(int d) {
+  Divisor v;
+  v.d = (uint32_t)d;
+  int l = 0;
+  while ((1ull << l) < (unsigned long long)v.d) ++l;
+  v.mul = (uint32_t)(((1ull << 32) * ((1ull << l) - v.d)) / v.d + 1);
+  v.s1 = l < 1 ? l : 1;
+  v.s2 = l > 1 ? l - 1 : 0;
+  return v;
+}
+
+VSA_HD uint32_t udiv(const Divisor& v, uint32_t n) {
+  const uint32_t t = (uint32_t)(((uint64_t)n * v.mul) >> 32);
+  return (t + ((n - t) >> v.s1)) >> v.s2;
+}
+
+// floor(a / d) for a possibly negative a
+VSA_HD int floor_div_by(int a, const Divisor& v) {
+  return a >= 0 ? (int)udiv(v, (uint32_t)a) : -(int)udiv(v, (uint32_t)(-a) + v.d - 1);
+}
+
+// The divisors of one (head geometry, mask) pair's interval tests.
+struct PairDivs {
+  Divisor ts, ss, wg;
+  int per;  // stripes: rows after which a row's spatial differences repeat mod Ss
+};
+
 // #{v in [0, m] : v mod P < w}, m >= -1
-VSA_HD int band_prefix(int m, int P, int w) {
+VSA_HD int band_prefix(int m, const Divisor& P, int w) {
   if (m < 0) return 0;
-  int wc = imin(w, P);
-  return ((m + 1) / P) * wc + imin((m + 1) % P, wc);
+  const int wc = imin(w, (int)P.d);
+  const uint32_t x = (uint32_t)m + 1u;
+  const uint32_t q = udiv(P, x);
+  return (int)q * wc + imin((int)(x - q * P.d), wc);
 }
 // #{u in [a, b] : (|u| mod P) < w}
-VSA_HD int band_count(int a, int b, int P, int w) {
+VSA_HD int band_count(int a, int b, const Divisor& P, int w) {
   if (a > b || w <= 0) return 0;
   int c = 0;
   if (b >= 0) {
@@ -265,7 +304,7 @@ VSA_HD void radius_test(int a, int b, int r, bool& all, bool& any) {
 }
 
 // (|d - o| mod P) <= w - 1 over d in [a, b]
-VSA_HD void periodic_test(int a, int b, int o, int P, int w, bool& all, bool& any) {
+VSA_HD void periodic_test(int a, int b, int o, const Divisor& P, int w, bool& all, bool& any) {
   int c = band_count(a - o, b - o, P, w);
   all = (c == b - a + 1);
   any = (c > 0);
@@ -293,14 +332,24 @@ VSA_HD int floor_div(int a, int b) {  // b > 0
   return a >= 0 ? a / b : -((-a + b - 1) / b);
 }
 
+VSA_HD PairDivs pair_divs(const Geom& g, const DevMask& m) {
+  const bool stripe = m.kind == VSA_MASK_STRIPE;
+  PairDivs v;
+  v.ts = make_divisor(stripe ? m.Ts : 1);
+  v.ss = make_divisor(stripe ? m.Ss : 1);
+  v.wg = make_divisor(g.Wg);
+  v.per = stripe ? m.Ss / igcd(g.Wg, m.Ss) : 1;
+  return v;
+}
+
 // Stripe test over the spatial differences of two boxes that are not runs of s: the
 // rows dy in [dy0, dy1] each contribute the interval d = dy*Wg + [dx0, dx1] - So, kept
 // where (|d| mod Ss) < Sw.  While a row's interval lies wholly below 0, or wholly at or
 // above 0, moving dy by Ss / gcd(Wg, Ss) moves d by a multiple of Ss and repeats the
 // row's result, so each of those two ranges needs at most one period of rows; only the
 // rows whose interval contains 0 are tested one by one.
-VSA_HD void stripe_rows_test(const Geom& g, const DevMask& m, int dy0, int dy1, int dx0, int dx1, bool& all,
-                             bool& any) {
+VSA_HD void stripe_rows_test(const Geom& g, const DevMask& m, const PairDivs& dv, int dy0, int dy1, int dx0,
+                             int dx1, bool& all, bool& any) {
   // every |d| below Ss (no wrap): kept iff |d| <= Sw - 1, so "any" asks whether some row
   // interval meets [-(Sw-1), Sw-1] and "all" whether the extremes stay inside it
   const int dmin = dy0 * g.Wg + dx0 - m.So, dmax = dy1 * g.Wg + dx1 - m.So;
@@ -308,21 +357,21 @@ VSA_HD void stripe_rows_test(const Geom& g, const DevMask& m, int dy0, int dy1, 
     const int w = m.Sw - 1;
     if (w < 0) { all = false; any = false; return; }
     const int A = dx0 - m.So, B = dx1 - m.So;  // row dy spans [A + dy*Wg, B + dy*Wg]
-    const int lo = imax(dy0, -floor_div(w + B, g.Wg)), hi = imin(dy1, floor_div(w - A, g.Wg));
+    const int lo = imax(dy0, -floor_div_by(w + B, dv.wg)), hi = imin(dy1, floor_div_by(w - A, dv.wg));
     any = lo <= hi;
     all = dmin >= -w && dmax <= w;
     return;
   }
   all = true;
   any = false;
-  const int per = m.Ss / igcd(g.Wg, m.Ss);
+  const int per = dv.per;
   // rows with d < 0 throughout: dy*Wg + dx1 - So < 0; rows with d >= 0 throughout:
   // dy*Wg + dx0 - So >= 0
-  const int neg_end = imin(dy1, floor_div(m.So - dx1 - 1, g.Wg));
-  const int pos_begin = imax(dy0, -floor_div(dx0 - m.So, g.Wg));
+  const int neg_end = imin(dy1, floor_div_by(m.So - dx1 - 1, dv.wg));
+  const int pos_begin = imax(dy0, -floor_div_by(dx0 - m.So, dv.wg));
   auto row = [&](int dy) {
     bool a, n;
-    periodic_test(dy * g.Wg + dx0, dy * g.Wg + dx1, m.So, m.Ss, m.Sw, a, n);
+    periodic_test(dy * g.Wg + dx0, dy * g.Wg + dx1, m.So, dv.ss, m.Sw, a, n);
     all = all && a;
     any = any || n;
   };
@@ -332,8 +381,8 @@ VSA_HD void stripe_rows_test(const Geom& g, const DevMask& m, int dy0, int dy1, 
 }
 
 // all / any kept over query box r x key box c for the mask without its sink.
-VSA_HD void box_pair_test(const Geom& g, const DevMask& m, const Box& r, const Box& c, bool& all,
-                          bool& any) {
+VSA_HD void box_pair_test(const Geom& g, const DevMask& m, const PairDivs& dv, const Box& r, const Box& c,
+                          bool& all, bool& any) {
   switch (m.kind) {
     case VSA_MASK_ALL:
       all = true; any = true;
@@ -349,7 +398,7 @@ VSA_HD void box_pair_test(const Geom& g, const DevMask& m, const Box& r, const B
     }
     case VSA_MASK_STRIPE: {
       bool at, nt;
-      periodic_test(c.t0 - r.t1, c.t1 - r.t0, m.To, m.Ts, m.Tw, at, nt);
+      periodic_test(c.t0 - r.t1, c.t1 - r.t0, m.To, dv.ts, m.Tw, at, nt);
       if (!nt) {  // no key frame passes the temporal test: nothing kept
         all = false;
         any = false;
@@ -359,9 +408,9 @@ VSA_HD void box_pair_test(const Geom& g, const DevMask& m, const Box& r, const B
       if (s_contiguous(g, r) && s_contiguous(g, c)) {
         int sq0 = r.y0 * g.Wg + r.x0, sq1 = r.y1 * g.Wg + r.x1;
         int sk0 = c.y0 * g.Wg + c.x0, sk1 = c.y1 * g.Wg + c.x1;
-        periodic_test(sk0 - sq1, sk1 - sq0, m.So, m.Ss, m.Sw, as, ns);
+        periodic_test(sk0 - sq1, sk1 - sq0, m.So, dv.ss, m.Sw, as, ns);
       } else {
-        stripe_rows_test(g, m, c.y0 - r.y1, c.y1 - r.y0, c.x0 - r.x1, c.x1 - r.x0, as, ns);
+        stripe_rows_test(g, m, dv, c.y0 - r.y1, c.y1 - r.y0, c.x0 - r.x1, c.x1 - r.x0, as, ns);
       }
       all = at && as;
       any = nt && ns;
@@ -436,15 +485,15 @@ VSA_HD void frame_range(const Box* R, int nr, int& q0, int& q1) {
 
 // Add key box c to a tile pair's class: `all` stays true while every pair seen is kept,
 // `any` turns true once one is.  R[nr] are the query boxes, [q0, q1] their frame range.
-VSA_HD void class_add(const Geom& g, const DevMask& m, const Box* R, int nr, int q0, int q1, Box c, bool& all,
-                      bool& any) {
+VSA_HD void class_add(const Geom& g, const DevMask& m, const PairDivs& dv, const Box* R, int nr, int q0, int q1,
+                      Box c, bool& all, bool& any) {
   if (nr == 0) return;
   // Frame pre-test: with no sink frame in c and no pair of frames passing the temporal
   // part of the mask, no pair with c is kept.
   if (c.t0 >= m.sink && (m.kind == VSA_MASK_STRIPE || (m.kind == VSA_MASK_BOX && m.rt >= 0))) {
     bool a, n;
     if (m.kind == VSA_MASK_STRIPE)
-      periodic_test(c.t0 - q1, c.t1 - q0, m.To, m.Ts, m.Tw, a, n);
+      periodic_test(c.t0 - q1, c.t1 - q0, m.To, dv.ts, m.Tw, a, n);
     else
       radius_test(c.t0 - q1, c.t1 - q0, m.rt, a, n);
     if (!n) {
@@ -459,7 +508,7 @@ VSA_HD void class_add(const Geom& g, const DevMask& m, const Box* R, int nr, int
   }
   for (int i = 0; i < nr; ++i) {
     bool a, n;
-    box_pair_test(g, m, R[i], c, a, n);
+    box_pair_test(g, m, dv, R[i], c, a, n);
     all = all && a;
     any = any || n;
     if (!all && any) return;
@@ -478,21 +527,22 @@ VSA_HD int tile_class(const Geom& g, const DevMask& m, const Box* R, int nr, con
   if (nr == 0) return VSA_TILE_EMPTY;
   int q0, q1;
   frame_range(R, nr, q0, q1);
-  for (int j = 0; j < nc && (all || !any); ++j) class_add(g, m, R, nr, q0, q1, C[j], all, any);
+  const PairDivs dv = pair_divs(g, m);
+  for (int j = 0; j < nc && (all || !any); ++j) class_add(g, m, dv, R, nr, q0, q1, C[j], all, any);
   return class_of(all, any, padded);
 }
 
 // Tile class of query boxes R[nr] (real tokens, frame range [q0, q1]) x the key tile of
 // executed positions [c0, c1), whose boxes are visited one at a time and clipped to the
 // real grid.  `padded`: the query tile or the key tile reaches past S.
-VSA_HD int tile_class_range(const Geom& g, const DevMask& m, const Box* R, int nr, int q0, int q1, int c0, int c1,
-                            bool padded) {
+VSA_HD int tile_class_range(const Geom& g, const DevMask& m, const PairDivs& dv, const Box* R, int nr, int q0,
+                            int q1, int c0, int c1, bool padded) {
   bool all = true, any = false;
   if (nr == 0) return VSA_TILE_EMPTY;
   for_each_box(g, c0, c1, [&](Box c) {
     if (!all && any) return;  // boundary whatever follows
     if (g.padded && !clip_box(g, c, padded)) return;
-    class_add(g, m, R, nr, q0, q1, c, all, any);
+    class_add(g, m, dv, R, nr, q0, q1, c, all, any);
   });
   return class_of(all, any, padded);
 }

@@ -36,6 +36,18 @@ int main(int argc, char** argv){
   srand(argc > 2 ? atoi(argv[2]) : 1);
   const int focus = argc > 3;  // one-column tiles and stripe periods of a row or a frame
   long long ntile=0, nbad=0, nmask=0, nmbad=0;
+  // division by invariant divisors: every divisor up to 4096 and random ones up to 2^31
+  // against the hardware division, at multiples of d and their neighbours, the ends of
+  // the 32-bit range and random numerators; floor_div_by on both signs
+  for(int i=0;i<4096+20000;++i){
+    const uint32_t d = i<4096 ? (uint32_t)(i+1) : 1u+(uint32_t)(((uint64_t)rand()*RAND_MAX+rand())%2147483647u);
+    const Divisor v = make_divisor((int)d);
+    uint32_t ns[12] = {0u,1u,d-1u,d,d+1u,2u*d-1u,2u*d,0xffffffffu,0x7fffffffu,0x80000000u,
+                       (uint32_t)((uint64_t)rand()*RAND_MAX+rand()), (uint32_t)rand()};
+    for(uint32_t n: ns){ if(udiv(v,n)!=n/d){ if(nbad<5) printf("BAD udiv %u / %u got %u\n",n,d,udiv(v,n)); nbad++; } }
+    if(d<(1u<<20)) for(int a=-3*(int)d-2;a<=3*(int)d+2;a+=1+(int)d/7){ int ref=a>=0?a/(int)d:-((-a+(int)d-1)/(int)d);
+      if(floor_div_by(a,v)!=ref){ if(nbad<5) printf("BAD floor_div_by %d / %u\n",a,d); nbad++; } }
+  }
   for(int trial=0; trial<trials; ++trial){
     Geom g; int layout = rand()%4;  // 3: tile-major over the padded grid
     g.padded = 0;
@@ -90,7 +102,7 @@ int main(int argc, char** argv){
         Box C[11]; int nc=decompose(g,c0,c1,C);
         bool pad=qpad||(kt+1)*Bk>S;
         bool pad_s=pad;  // the streamed form (the kernel's) sets its own copy
-        int cs = tile_class_range(g,m,R,nr,q0,q1,c0,c1,pad_s);
+        int cs = tile_class_range(g,m,pair_divs(g,m),R,nr,q0,q1,c0,c1,pad_s);
         if(g.padded) nc=clip_real(g,C,nc,pad);
         int c = tile_class(g,m,R,nr,C,nc,pad);
         long long kept=0;
