@@ -9,11 +9,11 @@
 // and empty otherwise.
 //
 // One workgroup per (query tile, mask).  The query range's boxes are computed once, into
-// LDS; each thread classifies key tiles with interval arithmetic (vsa_geom.h), visiting
+// LDS; each thread classifies key tiles with interval arithmetic (vsa_classify_geom.h), visiting
 // the key tile's boxes one at a time so that nothing is held in private memory, and a
 // workgroup-wide prefix count keeps the lists in ascending key-tile order.
 // HBM-bound on the class map and list writes; integer-exact.
-#include "vsa_geom.h"
+#include "vsa_classify_geom.h"
 
 namespace vsa {
 

@@ -1,4 +1,4 @@
-// Host build of the GPU classification geometry (vsa_geom.h) against brute force.
+// Host build of the GPU geometry (vsa_classify_geom.h, vsa_geom.h) against brute force.
 //
 // For random grids, token orders (frame-, tile-, position-major, tile-major over a padded
 // grid), mask kinds and tile sizes: the boxes of every query and key range are checked
@@ -13,7 +13,7 @@
 // usage: geometry_check TRIALS SEED [focus]; "focus" draws one-column tiles and stripe
 // periods of one row or one frame (the closed-form stripe paths).  Exit status 1 on any
 // mismatch.
-#include "vsa_geom.h"
+#include "vsa_classify_geom.h"
 #include <cstdio>
 #include <cstdlib>
 #include <vector>

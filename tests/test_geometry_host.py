@@ -1,4 +1,4 @@
-"""The classification geometry of the GPU path (csrc/vsa_geom.h), built for the host
+"""The geometry of the GPU path (csrc/vsa_classify_geom.h, csrc/vsa_geom.h), built for the host
 with g++ and checked against brute-force enumeration (tests/geometry_check.cpp): tile
 classes, kept-pair counts and the 64-key row masks of every mask kind in every token
 order, on random small grids.  Needs g++ and the ROCm headers, no GPU."""
