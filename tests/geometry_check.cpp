@@ -86,8 +86,8 @@ int main(int argc, char** argv){
     }
     int nQ=(S+Bq-1)/Bq, nK=(S+Bk-1)/Bk;
     // boxes of every query and key range: they hold exactly the range's positions
-    for(int pass=0;pass<2;++pass){ int B=pass?Bk:Bq;
-      for(int lo=0;lo<S;lo+=B){ int hi=std::min(S,lo+B); Box bx[64]; int nb=decompose(g,lo,hi,bx);  // at most one box per position (B <= 64)
+    for(int pass=0;pass<3;++pass){ int B=pass==2?256:(pass?Bk:Bq);  // 256: the largest query tile
+      for(int lo=0;lo<S;lo+=B){ int hi=std::min(S,lo+B); Box bx[256]; int nb=decompose(g,lo,hi,bx);  // at most one box per position
         long long vol=0; for(int i=0;i<nb;++i) vol+=box_volume(bx[i]);
         bool ok = nb<=11 && vol==hi-lo;
         for(int p=lo;p<hi&&ok;++p){ int in=0; for(int i=0;i<nb;++i) in += T[p]>=bx[i].t0&&T[p]<=bx[i].t1&&Y[p]>=bx[i].y0&&Y[p]<=bx[i].y1&&X[p]>=bx[i].x0&&X[p]<=bx[i].x1; ok = in==1; }
