@@ -53,9 +53,8 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
   const int nr = s_nr;
   const bool q_padded = s_qpad;
   const Box* R = s_R;
-  int q0 = 0, q1 = 0;
+  const Box qb = nr > 0 ? bounding_box(R, nr) : Box{0, 0, 0, 0, 0, 0};
   long long q_real = 0;
-  if (nr > 0) frame_range(R, nr, q0, q1);
   for (int i = 0; i < nr; ++i) q_real += box_volume(R[i]);
 
   __shared__ int s_cnt[2][kWaves];
@@ -74,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
       const int c0 = kt * Bk;
       const int c1 = imin(c0 + Bk, g.S);
       bool padded = q_padded || (c0 + Bk) > g.S;
-      c = tile_class_range(g, m, dv, R, nr, q0, q1, c0, c1, padded);
+      c = tile_class_range(g, m, dv, R, nr, qb, c0, c1, padded);
       if (round_tiles && c == VSA_TILE_BOUNDARY) {
         // tile-aligned rounding: keep the tile's real pairs iff at least half are kept
         // kept pairs: summed over box pairs where the predicate is a product over the

@@ -212,7 +212,8 @@ VSA_HD int floor_div_by(int a, const Divisor& v) {
 // The divisors of one (head geometry, mask) pair's interval tests.
 struct PairDivs {
   Divisor ts, ss, wg;
-  int per;  // stripes: rows after which a row's spatial differences repeat mod Ss
+  int per;      // stripes: rows after which a row's spatial differences repeat mod Ss
+  bool x_only;  // stripes with Ss dividing Wg: s differences mod Ss depend on x alone
 };
 
 // #{v in [0, m] : v mod P < w}, m >= -1
@@ -246,6 +247,12 @@ VSA_HD void radius_test(int a, int b, int r, bool& all, bool& any) {
 }
 
 // (|d - o| mod P) <= w - 1 over d in [a, b]
+// Whether some u in [a, b] lies within w - 1 of a multiple of P (w <= 0: none).
+VSA_HD bool near_multiple(int a, int b, const Divisor& P, int w) {
+  if (w <= 0 || a > b) return false;
+  return floor_div_by(b + w - 1, P) >= -floor_div_by(-(a - w + 1), P);
+}
+
 VSA_HD void periodic_test(int a, int b, int o, const Divisor& P, int w, bool& all, bool& any) {
   int c = band_count(a - o, b - o, P, w);
   all = (c == b - a + 1);
@@ -275,6 +282,7 @@ VSA_HD PairDivs pair_divs(const Geom& g, const DevMask& m) {
   v.ss = make_divisor(stripe ? m.Ss : 1);
   v.wg = make_divisor(g.Wg);
   v.per = stripe ? m.Ss / igcd(g.Wg, m.Ss) : 1;
+  v.x_only = stripe && g.Wg % m.Ss == 0;
   return v;
 }
 
@@ -413,16 +421,20 @@ VSA_HD long long box_pair_kept(const Geom& g, const DevMask& m, const Box& r, Bo
   }
 }
 
-// Frame range [q0, q1] covered by boxes R[nr] (nr > 0).
-VSA_HD void frame_range(const Box* R, int nr, int& q0, int& q1) {
-  q0 = R[0].t0;
-  q1 = R[0].t1;
-  for (int i = 1; i < nr; ++i) { q0 = imin(q0, R[i].t0); q1 = imax(q1, R[i].t1); }
+// Bounding box of boxes R[nr] (nr > 0).
+VSA_HD Box bounding_box(const Box* R, int nr) {
+  Box q = R[0];
+  for (int i = 1; i < nr; ++i) {
+    q.t0 = imin(q.t0, R[i].t0); q.t1 = imax(q.t1, R[i].t1);
+    q.y0 = imin(q.y0, R[i].y0); q.y1 = imax(q.y1, R[i].y1);
+    q.x0 = imin(q.x0, R[i].x0); q.x1 = imax(q.x1, R[i].x1);
+  }
+  return q;
 }
 
 // Add key box c to a tile pair's class: `all` stays true while every pair seen is kept,
-// `any` turns true once one is.  R[nr] are the query boxes, [q0, q1] their frame range.
-VSA_HD void class_add(const Geom& g, const DevMask& m, const PairDivs& dv, const Box* R, int nr, int q0, int q1,
+// `any` turns true once one is.  R[nr] are the query boxes, qb their bounding box.
+VSA_HD void class_add(const Geom& g, const DevMask& m, const PairDivs& dv, const Box* R, int nr, const Box& qb,
                       Box c, bool& all, bool& any) {
   if (nr == 0) return;
   // Frame pre-test: with no sink frame in c and no pair of frames passing the temporal
@@ -432,9 +444,13 @@ VSA_HD void class_add(const Geom& g, const DevMask& m, const PairDivs& dv, const
   if (c.t0 >= m.sink && (m.kind == VSA_MASK_STRIPE || (m.kind == VSA_MASK_BOX && m.rt >= 0))) {
     bool a, n;
     if (m.kind == VSA_MASK_STRIPE)
-      periodic_test(c.t0 - q1, c.t1 - q0, m.To, dv.ts, m.Tw, a, n);
+      periodic_test(c.t0 - qb.t1, c.t1 - qb.t0, m.To, dv.ts, m.Tw, a, n);
     else
-      radius_test(c.t0 - q1, c.t1 - q0, m.rt, a, n);
+      radius_test(c.t0 - qb.t1, c.t1 - qb.t0, m.rt, a, n);
+    // Column pre-test for stripes whose period divides the row width: a difference
+    // dy*Wg + dx - So is congruent to dx - So mod Ss, so |.| mod Ss < Sw needs dx - So
+    // within Sw - 1 of a multiple of Ss.
+    if (n && dv.x_only) n = near_multiple(c.x0 - qb.x1 - m.So, c.x1 - qb.x0 - m.So, dv.ss, m.Sw);
     if (!n) {
       all = false;
       return;
@@ -465,24 +481,23 @@ VSA_HD int tile_class(const Geom& g, const DevMask& m, const Box* R, int nr, con
                       bool padded) {
   bool all = true, any = false;
   if (nr == 0) return VSA_TILE_EMPTY;
-  int q0, q1;
-  frame_range(R, nr, q0, q1);
+  const Box qb = bounding_box(R, nr);
   const PairDivs dv = pair_divs(g, m);
-  for (int j = 0; j < nc && (all || !any); ++j) class_add(g, m, dv, R, nr, q0, q1, C[j], all, any);
+  for (int j = 0; j < nc && (all || !any); ++j) class_add(g, m, dv, R, nr, qb, C[j], all, any);
   return class_of(all, any, padded);
 }
 
-// Tile class of query boxes R[nr] (real tokens, frame range [q0, q1]) x the key tile of
+// Tile class of query boxes R[nr] (real tokens, bounding box qb) x the key tile of
 // executed positions [c0, c1), whose boxes are visited one at a time and clipped to the
 // real grid.  `padded`: the query tile or the key tile reaches past S.
-VSA_HD int tile_class_range(const Geom& g, const DevMask& m, const PairDivs& dv, const Box* R, int nr, int q0,
-                            int q1, int c0, int c1, bool padded) {
+VSA_HD int tile_class_range(const Geom& g, const DevMask& m, const PairDivs& dv, const Box* R, int nr,
+                            const Box& qb, int c0, int c1, bool padded) {
   bool all = true, any = false;
   if (nr == 0) return VSA_TILE_EMPTY;
   for_each_box(g, c0, c1, [&](Box c) {
     if (!all && any) return;  // boundary whatever follows
     if (g.padded && !clip_box(g, c, padded)) return;
-    class_add(g, m, dv, R, nr, q0, q1, c, all, any);
+    class_add(g, m, dv, R, nr, qb, c, all, any);
   });
   return class_of(all, any, padded);
 }

@@ -96,13 +96,13 @@ int main(int argc, char** argv){
       Box R[11]; int nr=decompose(g,qt*Bq,std::min(S,(qt+1)*Bq),R);
       bool qpad=(qt+1)*Bq>S;
       if(g.padded) nr=clip_real(g,R,nr,qpad);
-      int q0=0,q1=0; if(nr>0) frame_range(R,nr,q0,q1);
+      const Box qb = nr>0 ? bounding_box(R,nr) : Box{0,0,0,0,0,0};
       for(int kt=0;kt<nK;++kt){
         const int c0=kt*Bk, c1=std::min(S,(kt+1)*Bk);
         Box C[11]; int nc=decompose(g,c0,c1,C);
         bool pad=qpad||(kt+1)*Bk>S;
         bool pad_s=pad;  // the streamed form (the kernel's) sets its own copy
-        int cs = tile_class_range(g,m,pair_divs(g,m),R,nr,q0,q1,c0,c1,pad_s);
+        int cs = tile_class_range(g,m,pair_divs(g,m),R,nr,qb,c0,c1,pad_s);
         if(g.padded) nc=clip_real(g,C,nc,pad);
         int c = tile_class(g,m,R,nr,C,nc,pad);
         long long kept=0;
