@@ -451,6 +451,15 @@ VSA_HD void class_add(const Geom& g, const DevMask& m, const PairDivs& dv, const
     // dy*Wg + dx - So is congruent to dx - So mod Ss, so |.| mod Ss < Sw needs dx - So
     // within Sw - 1 of a multiple of Ss.
     if (n && dv.x_only) n = near_multiple(c.x0 - qb.x1 - m.So, c.x1 - qb.x0 - m.So, dv.ss, m.Sw);
+    // Position pre-test for stripes: every s = y*Wg + x of a box lies in [y0*Wg + x0,
+    // y1*Wg + x1], so the spatial part over the two ranges' differences bounds every pair
+    // (narrow, and so deciding, when the tiles hold few positions).
+    if (n && m.kind == VSA_MASK_STRIPE) {
+      bool as, ns;
+      periodic_test(c.y0 * g.Wg + c.x0 - (qb.y1 * g.Wg + qb.x1), c.y1 * g.Wg + c.x1 - (qb.y0 * g.Wg + qb.x0), m.So,
+                    dv.ss, m.Sw, as, ns);
+      n = ns;
+    }
     if (!n) {
       all = false;
       return;
