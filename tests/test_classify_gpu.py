@@ -248,3 +248,30 @@ def test_classify_padded_full_config(gpu_lib):
     qts = _sampled_q_tiles(tiles["nQ"], rng, 6)
     ref = oracle.classify(g, "padded", cfg["masks"][0], Bq, Bk, q_tiles=qts)
     check_lists_against(tiles, 0, qts, ref["cls"])
+
+
+def test_classify_stripes_column_and_position_full_config(gpu_lib):
+    """The routed stripe layer in the orders its heads run in: stripes whose period is
+    the row width tile-major over one-column tiles (1x45x1, each frame read column by
+    column), the others position-major.  Sampled query tiles of several heads of each
+    order bit-exact against the oracle, and the lists agree with the class map."""
+    cfg = W.config("stripe_route")
+    g = W.grid(21, 45, 80, (1, 45, 1))
+    Bq, Bk = cfg["Bq"], cfg["Bk"]
+    masks = [W.with_head_layout(m, "tile" if m["Ss"] == 80 else "position") for m in cfg["masks"]]
+    say("classify stripe layer, column and position orders, full size")
+    tiles = gpu_lib.vsa_classify_tiles(g, "frame", masks, Bq, Bk, device=dev())
+    torch.cuda.synchronize()
+    hm, U = gpu_lib.vsa_unique_masks(masks)
+    lays = W.head_layouts(masks, "frame")
+    rng = np.random.default_rng(11)
+    picked = [h for h in range(len(masks)) if lays[h] == "tile"][:4] + \
+        [h for h in range(len(masks)) if lays[h] == "position"][:4]
+    assert len(picked) == 8
+    for h in picked:
+        qts = _sampled_q_tiles(tiles["nQ"], rng, 3)
+        ref = oracle.classify(g, lays[h], masks[h], Bq, Bk, q_tiles=qts)
+        check_lists_against(tiles, hm[h], qts, ref["cls"])
+    cls = tiles["cls"].cpu()
+    assert torch.equal((cls == 1).sum(-1).int(), tiles["n_full"].cpu())
+    assert torch.equal((cls == 2).sum(-1).int(), tiles["n_bnd"].cpu())
