@@ -178,32 +178,6 @@ VSA_HD long long box_volume(const Box& b) {
 // ---------------------------------------------------------------------------
 // predicates over intervals of a coordinate difference
 // ---------------------------------------------------------------------------
-// Division by a positive divisor that stays fixed over many calls (a mask's period, the
-// grid width): floor(n / d) for every 32-bit unsigned n by one multiply-high, a
-// subtraction, an addition and two shifts (Granlund and Montgomery, "Division by
-// invariant integers using multiplication", 1994, unsigned division of section 4):
-// with l = ceil(log2 d), mul = floor(2^32 (2^l - d) / d) + 1.
-struct Divisor {
-  uint32_t d, mul;
-  int s1, s2;
-};
-
-VSA_HD Divisor make_divisor(int d) {
-  Divisor v;
-  v.d = (uint32_t)d;
-  int l = 0;
-  while ((1ull << l) < (unsigned long long)v.d) ++l;
-  v.mul = (uint32_t)(((1ull << 32) * ((1ull << l) - v.d)) / v.d + 1);
-  v.s1 = l < 1 ? l : 1;
-  v.s2 = l > 1 ? l - 1 : 0;
-  return v;
-}
-
-VSA_HD uint32_t udiv(const Divisor& v, uint32_t n) {
-  const uint32_t t = (uint32_t)(((uint64_t)n * v.mul) >> 32);
-  return (t + ((n - t) >> v.s1)) >> v.s2;
-}
-
 // floor(a / d) for a possibly negative a
 VSA_HD int floor_div_by(int a, const Divisor& v) {
   return a >= 0 ? (int)udiv(v, (uint32_t)a) : -(int)udiv(v, (uint32_t)(-a) + v.d - 1);

@@ -28,6 +28,32 @@ VSA_HD int floor_div(int a, int b) {
   return a >= 0 ? a / b : -((-a + b - 1) / b);
 }
 
+// Division by a positive divisor that stays fixed over many calls (a mask's period, the
+// grid width): floor(n / d) for every 32-bit unsigned n by one multiply-high, a
+// subtraction, an addition and two shifts (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, unsigned division of section 4):
+// with l = ceil(log2 d), mul = floor(2^32 (2^l - d) / d) + 1.
+struct Divisor {
+  uint32_t d, mul;
+  int s1, s2;
+};
+
+VSA_HD Divisor make_divisor(int d) {
+  Divisor v;
+  v.d = (uint32_t)d;
+  int l = 0;
+  while ((1ull << l) < (unsigned long long)v.d) ++l;
+  v.mul = (uint32_t)(((1ull << 32) * ((1ull << l) - v.d)) / v.d + 1);
+  v.s1 = l < 1 ? l : 1;
+  v.s2 = l > 1 ? l - 1 : 0;
+  return v;
+}
+
+VSA_HD uint32_t udiv(const Divisor& v, uint32_t n) {
+  const uint32_t t = (uint32_t)(((uint64_t)n * v.mul) >> 32);
+  return (t + ((n - t) >> v.s1)) >> v.s2;
+}
+
 // first tile of the sliding window of width w around tile a on an axis of n tiles
 VSA_HD int sta_start(int a, int w, int n) { return imin(imax(a - w / 2, 0), imax(n - w, 0)); }
 
@@ -110,19 +136,28 @@ VSA_HD uint64_t bit_range(int lo, int hi) {  // bits lo..hi inclusive, 0 <= lo <
 
 // Bits off + (u - ua) for the u in [ua, ub] with (|u| mod P) < w (the stripe predicate
 // along one run of keys).
-VSA_HD uint64_t periodic_bits(int ua, int ub, int P, int w, int off) {
+// A stripe period for the row masks: a plain integer (divided on the fly) or a
+// multiply-high divisor prepared once per workgroup.
+VSA_HD int period_value(int P) { return P; }
+VSA_HD int period_value(const Divisor& P) { return (int)P.d; }
+VSA_HD int period_div(int a, int P) { return a / P; }  // a >= 0
+VSA_HD int period_div(int a, const Divisor& P) { return (int)udiv(P, (uint32_t)a); }
+
+template <typename Per>
+VSA_HD uint64_t periodic_bits(int ua, int ub, const Per& Pd, int w, int off) {
   // one division per sign of u: the periods are stepped from the first one
+  const int P = period_value(Pd);
   uint64_t bits = 0;
   if (ub >= 0) {
     int lo = imax(ua, 0);
-    for (int base = (lo / P) * P; base <= ub; base += P) {
+    for (int base = period_div(lo, Pd) * P; base <= ub; base += P) {
       int a = imax(lo, base), b = imin(ub, base + w - 1);
       if (a <= b) bits |= bit_range(off + a - ua, off + b - ua);
     }
   }
   if (ua < 0) {
     int lo = imax(-ub, 1), hi = -ua;  // |u| in [lo, hi]
-    for (int base = (lo / P) * P; base <= hi; base += P) {
+    for (int base = period_div(lo, Pd) * P; base <= hi; base += P) {
       int a = imax(lo, base), b = imin(hi, base + w - 1);
       if (a <= b) bits |= bit_range(off - b - ua, off - a - ua);
     }
@@ -131,8 +166,9 @@ VSA_HD uint64_t periodic_bits(int ua, int ub, int P, int w, int off) {
 }
 
 // kept keys of a run (fixed t, y; x in [x0, x1]; bit of x0 is off) for query q
+template <typename Per>
 VSA_HD uint64_t run_mask(const Geom& g, const DevMask& m, const QueryPos& q, int t, int y, int x0,
-                         int x1, int off) {
+                         int x1, int off, const Per& ss) {
   if (g.padded) {  // padding keys are never kept
     if (t >= g.T || y >= g.Hg || x0 >= g.Wg) return 0;
     x1 = imin(x1, g.Wg - 1);
@@ -150,7 +186,7 @@ VSA_HD uint64_t run_mask(const Geom& g, const DevMask& m, const QueryPos& q, int
       if (g.T <= 64 ? !((q.tkeep >> t) & 1) : !stripe_frame_kept(m, t, q.t)) return 0;
       // u = s_k - s_q - So over the run; kept where (|u| mod Ss) < Sw
       const int ubase = y * g.Wg - q.s - m.So;  // u = x + ubase
-      return periodic_bits(x0 + ubase, x1 + ubase, m.Ss, m.Sw, off);
+      return periodic_bits(x0 + ubase, x1 + ubase, ss, m.Sw, off);
     }
     case VSA_MASK_STA: {
       int at = t / g.bt, ay = y / g.bh;
@@ -166,8 +202,9 @@ VSA_HD uint64_t run_mask(const Geom& g, const DevMask& m, const QueryPos& q, int
 
 // kept keys of a frame run of position-major order (fixed y, x; t in [t0, t1]; bit of
 // t0 is off) for query q
+template <typename Per>
 VSA_HD uint64_t run_mask_t(const Geom& g, const DevMask& m, const QueryPos& q, int t0, int t1, int y,
-                           int x, int off) {
+                           int x, int off, const Per& ts) {
   uint64_t bits = 0;
   if (t0 < m.sink) {  // sink frames are kept for every query
     const int hi = imin(t1, m.sink - 1);
@@ -193,7 +230,7 @@ VSA_HD uint64_t run_mask_t(const Geom& g, const DevMask& m, const QueryPos& q, i
         return bits | (((q.tkeep >> t0) & (~0ull >> (63 - (t1 - t0)))) << off);
       // v = t_k - t_q - To over the run; kept where (|v| mod Ts) < Tw
       const int vbase = -q.t - m.To;
-      return bits | periodic_bits(t0 + vbase, t1 + vbase, m.Ts, m.Tw, off);
+      return bits | periodic_bits(t0 + vbase, t1 + vbase, ts, m.Tw, off);
     }
     case VSA_MASK_STA: {
       const int ay = y / g.bh, ax = x / g.bw;
@@ -387,7 +424,9 @@ VSA_HD uint64_t real_key_mask(const Geom& g, int c0, int nbits) {
 // Keep bits of keys [c0, min(c0 + nbits, S)) for query q (nbits <= 64): one loop for
 // the frame- and tile-major orders, one for position-major, chosen once per call so that
 // neither carries the other's per-run tests.
-VSA_HD uint64_t tile_row_mask_ft(const Geom& g, const DevMask& m, const QueryPos& q, int c0, int nbits) {
+template <typename Per>
+VSA_HD uint64_t tile_row_mask_ft(const Geom& g, const DevMask& m, const QueryPos& q, int c0, int nbits,
+                                 const Per& ss) {
   const int end = imin(c0 + nbits, g.S);
   uint64_t bits = 0;
   RunCursor c = run_begin(g, c0);
@@ -416,30 +455,39 @@ VSA_HD uint64_t tile_row_mask_ft(const Geom& g, const DevMask& m, const QueryPos
   }
   while (c.p < end) {
     const int len = run_len_ft(g, c, end);
-    bits |= run_mask(g, m, q, c.t, c.y, c.x, c.x + len - 1, c.p - c0);
+    bits |= run_mask(g, m, q, c.t, c.y, c.x, c.x + len - 1, c.p - c0, ss);
     run_advance_ft(g, c, len);
   }
   return bits;
 }
 
-VSA_HD uint64_t tile_row_mask_pm(const Geom& g, const DevMask& m, const QueryPos& q, int c0, int nbits) {
+template <typename Per>
+VSA_HD uint64_t tile_row_mask_pm(const Geom& g, const DevMask& m, const QueryPos& q, int c0, int nbits,
+                                 const Per& ss, const Per& ts) {
   const int end = imin(c0 + nbits, g.S);
   uint64_t bits = 0;
   RunCursor c = run_begin(g, c0);
   while (c.p < end) {
     const int len = run_len_pm(g, c, end);
     if (run_along_t(g, c))
-      bits |= run_mask_t(g, m, q, c.t, c.t + len - 1, c.y, c.x, c.p - c0);
+      bits |= run_mask_t(g, m, q, c.t, c.t + len - 1, c.y, c.x, c.p - c0, ts);
     else
-      bits |= run_mask(g, m, q, c.t, c.y, c.x, c.x + len - 1, c.p - c0);
+      bits |= run_mask(g, m, q, c.t, c.y, c.x, c.x + len - 1, c.p - c0, ss);
     run_advance_pm(g, c, len);
   }
   return bits;
 }
 
+template <typename Per>
+VSA_HD uint64_t tile_row_mask(const Geom& g, const DevMask& m, const QueryPos& q, int c0, int nbits, const Per& ss,
+                              const Per& ts) {
+  return g.layout == VSA_LAYOUT_POSITION_MAJOR ? tile_row_mask_pm(g, m, q, c0, nbits, ss, ts)
+                                               : tile_row_mask_ft(g, m, q, c0, nbits, ss);
+}
+
+// The same with the mask's own periods, divided on the fly.
 VSA_HD uint64_t tile_row_mask(const Geom& g, const DevMask& m, const QueryPos& q, int c0, int nbits) {
-  return g.layout == VSA_LAYOUT_POSITION_MAJOR ? tile_row_mask_pm(g, m, q, c0, nbits)
-                                               : tile_row_mask_ft(g, m, q, c0, nbits);
+  return tile_row_mask(g, m, q, c0, nbits, m.Ss, m.Ts);
 }
 
 }  // namespace vsa

@@ -33,6 +33,9 @@ __global__ __launch_bounds__(256) void boundary_words_kernel(Geom g_call, MaskTa
   const int qt = blockIdx.x, u = blockIdx.y;
   const DevMask m = masks.m[u];
   const Geom g = head_geom(g_call, m);
+  // stripe periods as multiply-high divisors, prepared once
+  const bool stripe = m.kind == VSA_MASK_STRIPE;
+  const Divisor dss = make_divisor(stripe ? m.Ss : 1), dts = make_divisor(stripe ? m.Ts : 1);
   const size_t row = (size_t)u * nQ + qt;
   const int nb = imin(imin(imax(n_bnd[row], 0), nK), cap);
   const int r = threadIdx.x;  // query row inside the tile
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void boundary_words_kernel(Geom g_call, MaskTa
     __syncthreads();
     for (int jj = blockIdx.z; jj < cnt; jj += kStride) {  // base is a multiple of kStride
       const int kt = s_kt[jj];
-      const uint64_t bits = tile_row_mask(g, m, qpos, kt * 64, 64);
+      const uint64_t bits = tile_row_mask(g, m, qpos, kt * 64, 64, dss, dts);
       const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {

@@ -117,11 +117,13 @@ int main(int argc, char** argv){
         ntile++; if(c!=ref||cs!=ref){ if(nbad<5) printf("BAD class trial %d kind %d layout %d qt %d kt %d got %d/%d ref %d\n",trial,m.kind,layout,qt,kt,c,cs,ref); nbad++; }
       }
     }
-    // element masks for tiles of 64 keys
+    // element masks for tiles of 64 keys (stripe periods also as prepared divisors)
+    const Divisor dss = make_divisor(m.kind==2 ? m.Ss : 1), dts = make_divisor(m.kind==2 ? m.Ts : 1);
     for(int p=0;p<S;++p){
       QueryPos q = make_query(g,m,p);
       for(int c0=0;c0<S;c0+=64){
         uint64_t bits=tile_row_mask(g,m,q,c0,64);
+        if(tile_row_mask(g,m,q,c0,64,dss,dts)!=bits){ if(nmbad<5) printf("BAD divisor row mask trial %d p %d c0 %d\n",trial,p,c0); nmbad++; }
         uint64_t rb=real_key_mask(g,c0,64);
         for(int j=0;j<64;++j){ int key=c0+j; bool ref = key<S && real[key] && keep_bf(g,m,T[p],Y[p],X[p],T[key],Y[key],X[key]); bool got=(bits>>j)&1; nmask++; if(got!=ref){ if(nmbad<5) printf("BAD mask trial %d kind %d p %d key %d got %d\n",trial,m.kind,p,key,got); nmbad++; }
           bool rref = key<S && real[key]; if(((rb>>j)&1)!=rref){ if(nmbad<5) printf("BAD real mask trial %d key %d\n",trial,key); nmbad++; } }
