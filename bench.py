@@ -122,38 +122,6 @@ def kept_pairs(g, masks, B):
     return total * B
 
 
-def choose_head_layouts(vsa, g, masks, Bq, Bk, dev, bnd_cost=1.2):
-    """Per-head token order with the lowest tile cost, from the GPU classifier's lists in
-    each candidate order: frame-major, position-major, and tile-major over one grid tile
-    of the form (1, Hg, w) for w dividing Wg (w <= 16: a frame read w columns at a time,
-    which makes column-band stripes contiguous).  The tile that gives the lowest total
-    is kept.  A full tile costs 1 and a boundary tile bnd_cost (its masks come from the
-    word table).  A per-shape decision made once, outside the timed step (the per-head
-    flags of Sparse VideoGen on TPU, chosen by cost).  Returns (grid, masks)."""
-    def per_head(grid, order):
-        om = [dict(m, head_layout=order) for m in masks]
-        t = vsa.vsa_classify_tiles(grid, "frame", om, Bq, Bk, device=dev, with_cls=False)
-        hm, _ = vsa.vsa_unique_masks(om)
-        nt = (t["n_full"].double() + bnd_cost * t["n_bnd"].double()).sum(dim=1).cpu().tolist()
-        return [nt[hm[h]] for h in range(len(masks))]
-
-    base = {"frame": per_head(g, "frame"), "position": per_head(g, "position")}
-    best_total, best = None, None
-    tiles = [None] + [(1, g["Hg"], w) for w in (1, 2, 4, 8, 16) if g["Wg"] % w == 0]
-    for tile in tiles:
-        cand = dict(base)
-        grid = g
-        if tile is not None:
-            grid = dict(g, tile_t=tile[0], tile_h=tile[1], tile_w=tile[2])
-            cand["tile"] = per_head(grid, "tile")
-        picks = [min(cand, key=lambda o: cand[o][h]) for h in range(len(masks))]
-        total = sum(cand[o][h] for h, o in enumerate(picks))
-        if best_total is None or total < best_total:
-            best_total, best = total, (grid if "tile" in picks else g, picks)
-    grid, picks = best
-    return grid, [dict(m, head_layout=o) if o != "frame" else m for m, o in zip(masks, picks)]
-
-
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
@@ -244,6 +212,7 @@ def main():
 
     import block_sparse_spatio_amd as vsa
     import workloads as W
+    from block_sparse_spatio_amd.layouts import choose_head_layouts
 
     vsa.load()
     dev = torch.device("cuda:0")
@@ -276,7 +245,7 @@ def main():
         if layout != "frame":
             print(f"--head-layouts auto needs a frame-major workload, not {args.config}", file=sys.stderr)
             return 2
-        g, masks = choose_head_layouts(vsa, g, masks, Bq, Bk, dev)
+        g, masks = choose_head_layouts(g, masks, Bq, Bk, dev)
     head_lays = W.head_layouts(masks, layout)
     reorder = any(x != "frame" for x in head_lays)
     flags = args.flags | (vsa.VSA_FWD_REORDER_IO if reorder else 0) | (vsa.VSA_FWD_TILE_ALIGNED if args.round_tiles else 0)
@@ -292,13 +261,16 @@ def main():
                                            flags)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream(dev)
-    # the boundary tiles' element masks, computed in every step; the table holds every
-    # key tile per list row (cap = nK), so the step needs no host read of the lists
+    # the boundary tiles' element masks, computed in every step into the compact table
+    # (one entry per listed boundary tile, rows indexed by the classifier's prefix sum of
+    # the list lengths); the masks are static per shape, so the table is sized once here,
+    # from one classification, and the timed step reads nothing back to the host
     use_words = cfg["dtype"] == "bf16" and not args.round_tiles and not args.no_mask_words
     words = None
     if use_words:
-        words = {"words": torch.empty((tiles["n_unique"], tiles["nQ"], tiles["nK"], Bq // 32, 64), dtype=torch.int32,
-                                      device=dev), "cap": tiles["nK"]}
+        vsa.vsa_classify_tiles(g, layout, masks, Bq, Bk, out=tiles, stream=stream)
+        words = vsa.vsa_boundary_words(g, layout, masks, tiles, stream=stream)
+        n_entries = int(words["words"].shape[0])
 
     # the sampled-query profiler is part of the step when the workload routes heads
     profile = "candidates" in cfg
@@ -318,7 +290,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if use_words:
-            vsa.vsa_boundary_words(g, layout, masks, tiles, cap=words["cap"], out=words["words"], stream=stream)
+            vsa.vsa_boundary_words(g, layout, masks, tiles, out=words["words"], stream=stream, n_entries=n_entries)
         if ev is not None:
             ev[4].record(stream)
         vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles, flags=flags, o=o, workspace=ws, stream=stream,
@@ -404,14 +376,15 @@ def main():
                             device=dev)
         pm_words = None
         if use_words:
-            pm_words = {"words": torch.empty((pm_tiles["n_unique"], pm_tiles["nQ"], pm_tiles["nK"], Bq // 32, 64),
-                                             dtype=torch.int32, device=dev), "cap": pm_tiles["nK"]}
+            vsa.vsa_classify_tiles(g, layout, pm, Bq, Bk, out=pm_tiles, stream=stream)
+            pm_words = vsa.vsa_boundary_words(g, layout, pm, pm_tiles, stream=stream)
+            pm_entries = int(pm_words["words"].shape[0])
 
         def pm_step():
             vsa.vsa_classify_tiles(g, layout, pm, Bq, Bk, out=pm_tiles, stream=stream)
             if use_words:
-                vsa.vsa_boundary_words(g, layout, pm, pm_tiles, cap=pm_words["cap"], out=pm_words["words"],
-                                       stream=stream)
+                vsa.vsa_boundary_words(g, layout, pm, pm_tiles, out=pm_words["words"], stream=stream,
+                                       n_entries=pm_entries)
             vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, pm, pm_tiles, flags=pm_flags, o=o, workspace=pm_ws,
                                     stream=stream, words=pm_words)
 

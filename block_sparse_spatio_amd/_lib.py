@@ -11,6 +11,7 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,6 +25,7 @@ VSA_MASK_ALL, VSA_MASK_BOX, VSA_MASK_STRIPE, VSA_MASK_STA = 0, 1, 2, 3
 VSA_TILE_EMPTY, VSA_TILE_FULL, VSA_TILE_BOUNDARY = 0, 1, 2
 VSA_FWD_FORCE_MASK, VSA_FWD_REORDER_IO, VSA_FWD_WRITE_LSE, VSA_FWD_TILE_ALIGNED = 1, 2, 4, 8
 VSA_CLASSIFY_ROUND_TILES = 1
+VSA_WORDS_COMPACT = -1
 
 _KINDS = {"all": VSA_MASK_ALL, "box": VSA_MASK_BOX, "stripe": VSA_MASK_STRIPE, "sta": VSA_MASK_STA}
 _LAYOUTS = {"frame": VSA_LAYOUT_FRAME_MAJOR, "tile": VSA_LAYOUT_TILE_MAJOR, "position": VSA_LAYOUT_POSITION_MAJOR,
@@ -44,7 +46,7 @@ class vsa_mask_desc(ctypes.Structure):
 
 class vsa_tile_lists(ctypes.Structure):
     _fields_ = [("cls", ctypes.c_void_p), ("n_full", ctypes.c_void_p), ("n_bnd", ctypes.c_void_p),
-                ("full_idx", ctypes.c_void_p), ("bnd_idx", ctypes.c_void_p)]
+                ("full_idx", ctypes.c_void_p), ("bnd_idx", ctypes.c_void_p), ("bnd_offs", ctypes.c_void_p)]
 
 
 class VsaError(RuntimeError):
@@ -62,6 +64,8 @@ _SIGNATURES = {
     "vsa_unique_masks": (_I, [ctypes.POINTER(vsa_mask_desc), _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "vsa_tile_counts": (_I, [ctypes.POINTER(vsa_grid), _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "vsa_seq_len": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(_I)]),
+    "vsa_tile_lists_bytes": (_I, [ctypes.POINTER(vsa_grid), _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
+    "vsa_tile_lists_carve": (_I, [ctypes.POINTER(vsa_grid), _I, _I, _I, _I, _P, ctypes.POINTER(vsa_tile_lists)]),
     "vsa_classify_tiles": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(vsa_mask_desc), _I, _I, _I,
                                 ctypes.POINTER(vsa_tile_lists), _P]),
     "vsa_classify_tiles_ex": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(vsa_mask_desc), _I, _I, _I, _I,
@@ -182,24 +186,46 @@ def vsa_seq_len(grid, layout):
     return s.value
 
 
+def vsa_tile_lists_bytes(grid, layout, n_unique, Bq, Bk):
+    """Bytes of one allocation holding every array of the tile lists (vsa_tile_lists_carve)."""
+    n = ctypes.c_size_t()
+    _check(load().vsa_tile_lists_bytes(ctypes.byref(make_grid(grid)), _layout(layout), n_unique, Bq, Bk,
+                                       ctypes.byref(n)))
+    return n.value
+
+
 def alloc_tile_lists(grid, masks, Bq, Bk, device, with_cls=True, layout="frame"):
+    """Tile lists for these masks in one device allocation, carved by the library
+    (vsa_tile_lists_bytes / vsa_tile_lists_carve); returns a dict of tensor views."""
     S = vsa_seq_len(grid, layout)
     nQ, nK = -(-S // Bq), -(-S // Bk)
     head_map, U = vsa_unique_masks(masks)
-    kw = dict(device=device)
+    nbytes = vsa_tile_lists_bytes(grid, layout, U, Bq, Bk)
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    pad = (-buf.data_ptr()) % 256
+    st = vsa_tile_lists()
+    _check(load().vsa_tile_lists_carve(ctypes.byref(make_grid(grid)), _layout(layout), U, Bq, Bk,
+                                       ctypes.c_void_p(buf.data_ptr() + pad), ctypes.byref(st)))
+
+    def view(ptr, dtype, shape):
+        off = ptr - buf.data_ptr()
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        return buf[off:off + n].view(dtype).view(shape)
+
     return {
-        "cls": torch.empty((U, nQ, nK), dtype=torch.uint8, **kw) if with_cls else None,
-        "n_full": torch.empty((U, nQ), dtype=torch.int32, **kw),
-        "n_bnd": torch.empty((U, nQ), dtype=torch.int32, **kw),
-        "full_idx": torch.empty((U, nQ, nK), dtype=torch.int32, **kw),
-        "bnd_idx": torch.empty((U, nQ, nK), dtype=torch.int32, **kw),
-        "head_map": head_map, "n_unique": U, "nQ": nQ, "nK": nK, "Bq": Bq, "Bk": Bk,
+        "cls": view(st.cls, torch.uint8, (U, nQ, nK)) if with_cls else None,
+        "n_full": view(st.n_full, torch.int32, (U, nQ)),
+        "n_bnd": view(st.n_bnd, torch.int32, (U, nQ)),
+        "full_idx": view(st.full_idx, torch.int32, (U, nQ, nK)),
+        "bnd_idx": view(st.bnd_idx, torch.int32, (U, nQ, nK)),
+        "bnd_offs": view(st.bnd_offs, torch.int64, (U * nQ + 1,)),
+        "head_map": head_map, "n_unique": U, "nQ": nQ, "nK": nK, "Bq": Bq, "Bk": Bk, "_buf": buf,
     }
 
 
 def _lists_struct(t):
-    return vsa_tile_lists(*[(t[n].data_ptr() if t[n] is not None else None)
-                            for n in ("cls", "n_full", "n_bnd", "full_idx", "bnd_idx")])
+    return vsa_tile_lists(*[(t[n].data_ptr() if t.get(n) is not None else None)
+                            for n in ("cls", "n_full", "n_bnd", "full_idx", "bnd_idx", "bnd_offs")])
 
 
 def vsa_classify_tiles(grid, layout, masks, Bq, Bk, out=None, device="cuda", stream=None, with_cls=True,
@@ -223,18 +249,29 @@ def vsa_fwd_workspace_bytes(B, S, H, D, dtype, flags):
     return n.value
 
 
-def vsa_boundary_words(grid, layout, masks, tiles, cap=None, out=None, stream=None):
-    """Element masks of the listed boundary tiles for the bf16 forward.  cap: entries per
-    list row; None (default) sizes the table to the longest boundary list, which reads
-    the list lengths back to the host (waits for the classification); pass nK to size it
-    without that read (every list fits).  Returns
-    {"words": int32 [U, nQ, cap, Bq/32, 64] device tensor (uint32 bit patterns), "cap": cap}."""
+def vsa_boundary_words(grid, layout, masks, tiles, cap="compact", out=None, stream=None, n_entries=None):
+    """Element masks of the listed boundary tiles for the bf16 forward.
+    cap="compact" (default): one entry per listed boundary tile, list row r from entry
+    tiles["bnd_offs"][r] (VSA_WORDS_COMPACT); the table size is the total of the lists,
+    read back from the device (waits for the classification) unless n_entries gives it.
+    cap=int: entries per list row (a forward derives the masks of entries past it);
+    cap=None: the longest boundary list (also read back).  Returns {"words": int32
+    device tensor (uint32 bit patterns) of shape [n_entries, Bq/32, 64] (compact) or
+    [U, nQ, cap, Bq/32, 64], "cap": cap (VSA_WORDS_COMPACT when compact)}."""
     U, nQ, nK, Bq = tiles["n_unique"], tiles["nQ"], tiles["nK"], tiles["Bq"]
-    if cap is None:
-        cap = max(1, int(tiles["n_bnd"].max()))
-    cap = int(cap)
-    shape = (U, nQ, cap, Bq // 32, 64)
     dev = tiles["n_bnd"].device
+    if cap == "compact":
+        if tiles.get("bnd_offs") is None:
+            raise ValueError("the compact table needs tile lists with bnd_offs")
+        if n_entries is None:
+            n_entries = int(tiles["bnd_offs"][-1])
+        cap = VSA_WORDS_COMPACT
+        shape = (max(1, int(n_entries)), Bq // 32, 64)
+    else:
+        if cap is None:
+            cap = max(1, int(tiles["n_bnd"].max()))
+        cap = int(cap)
+        shape = (U, nQ, cap, Bq // 32, 64)
     if out is None:
         out = torch.empty(shape, dtype=torch.int32, device=dev)
     if tuple(out.shape) != shape or out.dtype != torch.int32 or not out.is_contiguous():
@@ -279,7 +316,11 @@ def vsa_sparse_attn_fwd(q, k, v, grid, layout, masks, tiles, scale=0.0, flags=0,
             flags, _ptr(workspace), ws_bytes, _stream(stream, q.device)))
     else:
         w = words["words"]
-        if tuple(w.shape) != (tiles["n_unique"], tiles["nQ"], words["cap"], tiles["Bq"] // 32, 64):
+        if words["cap"] == VSA_WORDS_COMPACT:
+            ok = w.dim() == 3 and tuple(w.shape[1:]) == (tiles["Bq"] // 32, 64) and tiles.get("bnd_offs") is not None
+        else:
+            ok = tuple(w.shape) == (tiles["n_unique"], tiles["nQ"], words["cap"], tiles["Bq"] // 32, 64)
+        if not ok:
             raise ValueError("words do not match the tile lists")
         _check(load().vsa_sparse_attn_fwd_ex(
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dt, B, S, H, D, ctypes.byref(make_grid(grid)),

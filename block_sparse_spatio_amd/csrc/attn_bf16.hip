@@ -48,7 +48,11 @@ using namespace pipe;
 
 constexpr int kAllWords = -2;  // kind tag: every boundary mask of the workgroup comes from the word table
 
-template <int D, int NW>
+// WORDS: the instance for query tiles whose whole boundary list is in the word table
+// (no mask arithmetic at all); the other instance serves every other query tile.  Two
+// kernels rather than one, so that the registers of the mask-deriving bodies do not
+// constrain the allocation of the table-driven one.
+template <int D, int NW, bool WORDS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const int32_t* __restrict__ n_bnd_p,
                           const int32_t* __restrict__ full_idx_p, const int32_t* __restrict__ bnd_idx_p,
@@ -103,7 +107,10 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   // arguments so that these uniform loads are scalar loads that never wait on the
   // vector-memory counter.
   const int nf = imin(imax(n_full_p[lrow], 0), a.nK);
-  const int nb = imin(imax(n_bnd_p[lrow], 0), a.nK);
+  int nb = imin(imax(n_bnd_p[lrow], 0), a.nK);
+  // the table-driven instance runs a list row only when the table holds all of it; a
+  // row that the table would cut short (inconsistent lists) is cut to the table
+  if constexpr (ALL_WORDS) nb = imin(nb, a.words_cap < 0 ? row_entries(a.bnd_offs, lrow, a.nK) : a.words_cap);
   const int32_t* full_list = full_idx_p + lrow * a.nK;
   const int32_t* bnd_list = bnd_idx_p + lrow * a.nK;
   const int n_tiles = nf + nb;
@@ -121,16 +128,23 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   // q and o: the executed order, or the caller's frame-major rows (gathered / scattered)
   const size_t base_io = a.gather_io ? ((size_t)b * a.lse_S) * tok_stride + (size_t)h * D : base_bh;
 
-  // ---- this lane's query row: B operand of S^T = K Q^T ----
+  // ---- this lane's query row: B operand of S^T = K Q^T, pre-multiplied by
+  // c = scale * log2(e) (one more bf16 rounding of q), so that the products are scores
+  // in base-2 exponent units and the softmax needs no multiply per score ----
   const int qrow = qt * Bq + wave * 32 + l32;
   const int qrow_c = qrow < S ? qrow : S - 1;
+  const float c_log2 = a.scale * 1.4426950408889634f;
   bf16x8 qf[KSTEPS];
   {
     // a padding row of a padded grid reads row 0 (finite data; its output is dropped)
     const int qsrc = a.gather_io ? imax(frame_index(g, qrow_c), 0) : qrow_c;
     const uint16_t* src = qp + base_io + (size_t)qsrc * tok_stride + g2 * 8;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + s * 16));
+    for (int s = 0; s < KSTEPS; ++s) {
+      const bf16x8 raw = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + s * 16));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)raw[e] * c_log2);
+    }
   }
   const QueryPos qpos = make_query(g, m, qrow_c);
 
@@ -155,10 +169,14 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   for (int j = 0; j < 4; ++j) vofs[j] = l32 * (BK * 2) + (((2 * j + g2) ^ vtsw(l32)) * 16);
 
   // list entry it of a boundary tile with precomputed words (uniform); its words
-  const uint32_t* words_row = a.words ? a.words + (lrow * a.words_cap) * (NW * 64) : nullptr;
+  // (a compact table, words_cap < 0, holds entries [bnd_offs[lrow], bnd_offs[lrow + 1])
+  // of each list row)
+  const uint32_t* words_row =
+      a.words ? a.words + (a.words_cap < 0 ? a.bnd_offs[lrow] : (int64_t)lrow * a.words_cap) * (NW * 64) : nullptr;
+  const int words_n = !a.words ? 0 : a.words_cap < 0 ? row_entries(a.bnd_offs, lrow, a.nK) : a.words_cap;
   auto has_words = [&](int it) -> bool {
     if constexpr (ALL_WORDS) return it >= nf && it < n_tiles;
-    return words_row != nullptr && !a.pad_only && it >= nf && it < n_tiles && it - nf < a.words_cap;
+    return words_row != nullptr && !a.pad_only && it >= nf && it < n_tiles && it - nf < words_n;
   };
   auto issue_words = [&](int it, char* mb) __attribute__((always_inline)) {
     dma4(words_row + (size_t)(it - nf) * (NW * 64) + wave * 64, 4u * (uint32_t)lane, lds_addr(mb + wave * 256));
@@ -193,17 +211,24 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     }
   };
 
-  // S^T (64 keys x this wave's 32 queries) = K Q^T from one K buffer.  The two 32-key
-  // halves alternate, so consecutive MFMAs never depend on each other.
+  // Running softmax reference of this lane's row, in base-2 units of c*s: R (-inf until
+  // a kept score is seen).  Products start from the accumulator 'bias' = -R (0 while
+  // R = -inf) through the MFMA's C operand, so the scores come out already relative to
+  // R and a probability is one exp2: no per-score subtraction.
+  f32x16 bias = f32x16{};
+  float R = -INFINITY;
+  float lim = -INFINITY;  // rescale when the tile max exceeds this (kLazyLog2 once R is set)
+
+  // S^T (64 keys x this wave's 32 queries) = K Q^T - R from one K buffer.  The two
+  // 32-key halves alternate, so consecutive MFMAs never depend on each other.
   auto qk = [&](const char* kb_, f32x16* s) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const u32x4 kf = *(const u32x4*)(kb_ + kb * 32 * C::ROWB + kofs[ks]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[ks], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[ks],
+                                                        ks == 0 ? bias : s[kb], 0, 0, 0);
       }
   };
   // Register (kb, i) of S^T holds key kb*32 + (i>>3)*16 + 8*g2 + (i&7) of the tile: gather
@@ -234,10 +259,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   f32x16 acc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;  // reference max, raw score units
   float l_run = 0.f;        // this lane's share of the row sum
-  const float c_log2 = a.scale * 1.4426950408889634f;
-  const float lazy = kLazyLog2 / c_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // ---- software pipeline over the listed key tiles.  Entering step i, S(i) is in
@@ -311,19 +333,27 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
         w_next = mask_word(kt1);
     }
 
-    // running max with lazy rescaling
-    const bool grow = mt_cur > m_run + lazy;
+    // lazy rescaling: the reference moves only when a row's tile max (relative to R)
+    // exceeds kLazyLog2, or when the row sees its first kept score
+    const bool grow = mt_cur > lim;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       // lanes that do not grow keep their reference and scale by exactly 1 (their
-      // reference may still be -inf, which must not meet a -inf - -inf)
-      const float m_new = grow ? mt_cur : m_run;
-      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c_log2) : 1.f;
+      // reference may still be -inf, which must not meet a -inf - -inf); the scores of
+      // S(it) already in registers move to the new reference
+      const float sh = grow ? mt_cur : 0.f;
+      const float R_new = grow ? mt_cur - bias[0] : R;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(R - R_new) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s_cur[i >> 4][i & 15] -= sh;
+      R = R_new;
+      lim = R == -INFINITY ? -INFINITY : kLazyLog2;
+      const float bv = R == -INFINITY ? 0.f : -R;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bias[i] = bv;
     }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c_log2;
     __builtin_amdgcn_sched_barrier(0);
 
     // stage A.  On the last tile the product runs on the stale buffer and is discarded:
@@ -345,7 +375,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
       for (int i = 0; i < NQK; ++i) {
         if (i + 3 < NQK) kr[(i + 3) % 4] = kread(k_use, i + 3);
         s_next[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[i % 4]),
-                                                                qf[i >> 1], s_next[i & 1], 0, 0, 0);
+                                                                qf[i >> 1], i < 2 ? bias : s_next[i & 1], 0, 0, 0);
         if (i % (NQK / C::NI) == 0) {
           const int d = i / (NQK / C::NI);
           dma16(ksrc, koff[d], kl0 + d * 1024);
@@ -354,8 +384,8 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 #pragma unroll
         for (int e = 0; e < EA; e += 2) {
           const int v = i * EA + e;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][v & 15], c_log2, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][(v & 15) + 1], c_log2, -mc));
+          const float p0 = __builtin_amdgcn_exp2f(s_cur[v >> 4][v & 15]);
+          const float p1 = __builtin_amdgcn_exp2f(s_cur[v >> 4][(v & 15) + 1]);
           pk[v >> 1] = pack_bf16x2(p0, p1);
           // the row sum adds exactly the rounded probabilities the PV product uses
           l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[v >> 1], ones, l_run, false);
@@ -493,7 +523,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
     if (a.write_lse && g2 == 0) {
       const int lpos = a.lse_frame_major ? (a.gather_io ? orow : frame_index(g, qrow)) : qrow;  // -1: padding
       if (lpos >= 0)
-        a.lse[((size_t)b * H + h) * a.lse_S + lpos] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+        a.lse[((size_t)b * H + h) * a.lse_S + lpos] = l_tot > 0.f ? R * 0.69314718055994531f + logf(l_tot) : -INFINITY;
     }
   }
   };
@@ -506,19 +536,26 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   using AllWords = std::integral_constant<int, kAllWords>;
   // a word table that holds this query tile's whole boundary list serves every order and
   // kind (the per-workgroup choice is uniform)
-  const int nb_row = imin(imax(n_bnd_p[(size_t)slot * a.nQ + qt], 0), a.nK);
-  if (a.words && nb_row <= a.words_cap && !a.pad_only && !a.force_mask)
-    run(AnyOrder{}, AllWords{});
-  else if (m_head.layout == VSA_LAYOUT_FRAME_MAJOR && m_head.kind == VSA_MASK_BOX)
-    run(Frame{}, Box{});
-  else if (m_head.layout == VSA_LAYOUT_FRAME_MAJOR && m_head.kind == VSA_MASK_STRIPE)
-    run(Frame{}, Stripe{});
-  else if (m_head.layout == VSA_LAYOUT_POSITION_MAJOR && m_head.kind == VSA_MASK_BOX)
-    run(Position{}, Box{});
-  else if (m_head.layout == VSA_LAYOUT_POSITION_MAJOR && m_head.kind == VSA_MASK_STRIPE)
-    run(Position{}, Stripe{});
-  else
-    run(AnyOrder{}, Any{});
+  const size_t row = (size_t)slot * a.nQ + qt;
+  const int nb_row = imin(imax(n_bnd_p[row], 0), a.nK);
+  const bool table_row = a.words && !a.pad_only && !a.force_mask &&
+                         (a.words_cap < 0 || nb_row <= a.words_cap);
+  if constexpr (WORDS) {
+    if (table_row) run(AnyOrder{}, AllWords{});
+  } else {
+    if (table_row)
+      return;
+    else if (m_head.layout == VSA_LAYOUT_FRAME_MAJOR && m_head.kind == VSA_MASK_BOX)
+      run(Frame{}, Box{});
+    else if (m_head.layout == VSA_LAYOUT_FRAME_MAJOR && m_head.kind == VSA_MASK_STRIPE)
+      run(Frame{}, Stripe{});
+    else if (m_head.layout == VSA_LAYOUT_POSITION_MAJOR && m_head.kind == VSA_MASK_BOX)
+      run(Position{}, Box{});
+    else if (m_head.layout == VSA_LAYOUT_POSITION_MAJOR && m_head.kind == VSA_MASK_STRIPE)
+      run(Position{}, Stripe{});
+    else
+      run(AnyOrder{}, Any{});
+  }
 }
 
 template <int D, int NW>
@@ -526,8 +563,19 @@ hipError_t launch_t(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
   const int cq = (a.nQ + 7) / 8;
   const long long n_blocks = 8LL * cq * a.B * a.H;
   if (n_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)n_blocks), dim3(NW * 64), 0, st, a, a.n_full,
-                     a.n_bnd, a.full_idx, a.bnd_idx, masks, hm);
+  // query tiles whose boundary list is in the word table run the table-driven kernel;
+  // with a compact table (cap < 0) or cap >= nK that is every query tile
+  const bool use_table = a.words && !a.pad_only && !a.force_mask;
+  const bool all_in_table = use_table && (a.words_cap < 0 || a.words_cap >= a.nK);
+  if (use_table) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, true>), dim3((unsigned)n_blocks), dim3(NW * 64), 0, st, a,
+                       a.n_full, a.n_bnd, a.full_idx, a.bnd_idx, masks, hm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!all_in_table)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, false>), dim3((unsigned)n_blocks), dim3(NW * 64), 0, st, a,
+                       a.n_full, a.n_bnd, a.full_idx, a.bnd_idx, masks, hm);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ template <int D, int BKT>
 __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(FwdArgs a, MaskTable masks, HeadMap hm) {
   __shared__ float ks[BKT][D];
   __shared__ float vs[BKT][D];
+  __shared__ int key_real[BKT];
   const int S = a.S, H = a.H;
   const int qt = blockIdx.x;
   const int h = blockIdx.y;
@@ -54,11 +55,15 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(FwdArgs a, MaskTable 
     const bool boundary = it >= nf || a.force_mask;
     const int c0 = kt * BKT;
     __syncthreads();
+    // padding keys of a padded grid (never kept) stage zero values, so that whatever
+    // the caller's padding rows hold cannot turn 0 * v into NaN
+    for (int r = tid; r < BKT; r += nthr) key_real[r] = !g.padded || frame_index(g, imin(c0 + r, S - 1)) >= 0;
+    __syncthreads();
     for (int e = tid; e < BKT * D; e += nthr) {
       const int r = e / D, d = e % D;
       const int key = imin(c0 + r, S - 1);
       ks[r][d] = kp[base + (size_t)key * tok + d];
-      vs[r][d] = vp[base + (size_t)key * tok + d];
+      vs[r][d] = key_real[r] ? vp[base + (size_t)key * tok + d] : 0.f;
     }
     __syncthreads();
     uint64_t bits = ~0ull;

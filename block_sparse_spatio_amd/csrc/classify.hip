@@ -122,6 +122,38 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geom g_call, MaskTab
   }
 }
 
+// Exclusive prefix sum of the boundary-list lengths over the n = U*nQ list rows:
+// offs[r] = sum of n_bnd[0 .. r-1] (each clamped to [0, nK], as the lists are read),
+// offs[n] = the total.  It indexes the compact boundary-word table.  One workgroup: each
+// thread sums a contiguous segment, the segment sums are scanned in LDS, then every
+// thread writes its segment's running sums.
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void bnd_offsets_kernel(const int32_t* __restrict__ n_bnd, int64_t n,
+                                                                   int nK, int64_t* __restrict__ offs) {
+  __shared__ int64_t s[kScanThreads];
+  const int t = threadIdx.x;
+  const int64_t per = (n + kScanThreads - 1) / kScanThreads;
+  const int64_t i0 = t * per < n ? t * per : n;
+  const int64_t i1 = i0 + per < n ? i0 + per : n;
+  int64_t sum = 0;
+  for (int64_t i = i0; i < i1; ++i) sum += imin(imax(n_bnd[i], 0), nK);
+  s[t] = sum;
+  __syncthreads();
+  for (int d = 1; d < kScanThreads; d <<= 1) {  // inclusive scan of the segment sums
+    const int64_t v = t >= d ? s[t - d] : 0;
+    __syncthreads();
+    s[t] += v;
+    __syncthreads();
+  }
+  int64_t run = s[t] - sum;
+  for (int64_t i = i0; i < i1; ++i) {
+    offs[i] = run;
+    run += imin(imax(n_bnd[i], 0), nK);
+  }
+  if (t == kScanThreads - 1) offs[n] = s[t];
+}
+
 }  // namespace
 
 hipError_t launch_classify(const Geom& g, const MaskTable& masks, int32_t U, int32_t Bq,
@@ -130,6 +162,10 @@ hipError_t launch_classify(const Geom& g, const MaskTable& masks, int32_t U, int
   dim3 grid(nQ, U);
   hipLaunchKernelGGL(classify_kernel, grid, dim3(kThreads), 0, stream, g, masks, Bq, Bk, round_tiles, nQ, nK,
                      out.cls, out.n_full, out.n_bnd, out.full_idx, out.bnd_idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !out.bnd_offs) return e;
+  hipLaunchKernelGGL(bnd_offsets_kernel, dim3(1), dim3(kScanThreads), 0, stream, out.n_bnd, (int64_t)U * nQ, nK,
+                     out.bnd_offs);
   return hipGetLastError();
 }
 

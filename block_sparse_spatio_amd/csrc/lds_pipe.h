@@ -66,9 +66,15 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 }
 
 // One wave-wide 16-byte-per-lane DMA from global memory (wave-uniform base + per-lane
-// 32-bit byte offset) into LDS at m0 + 16*lane (global_load_lds_dwordx4).  Issued through asm so that the compiler does not guard
-// every later LDS read with a wait for all DMAs in flight: the kernel waits for the
-// DMAs of a stage itself (wait_vmcnt) before the barrier that publishes the stage.
+// 32-bit byte offset) into LDS at m0 + 16*lane (global_load_lds_dwordx4).  Issued through
+// asm so that the compiler does not guard every later LDS read with a wait for all DMAs in
+// flight: the kernel waits for the DMAs of a stage itself (wait_vmcnt) before the barrier
+// that publishes the stage.
+// m0 is written here without being named as clobbered: the compiler reserves m0 (it
+// refuses it in a clobber list) and allocates no value to it, and nothing else in the
+// kernels that include this header reads m0, so no live value can be overwritten.
+// tests/test_asm_m0.py keeps that true: it builds the kernels to gfx950 assembly and
+// checks that every m0 reference is one of these writes, directly followed by its DMA.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory");
 }

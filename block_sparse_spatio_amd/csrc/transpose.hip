@@ -10,10 +10,10 @@
 //
 // One workgroup per (b, h, 64-key block): the 64 x D block is read with 16-byte
 // coalesced loads (one 2*D-byte row per key), staged in LDS, and written as D rows of
-// 64 keys (128 contiguous bytes each).  With a gather geometry, V is the caller's
-// frame-major tensor and key p of head h (in that head's executed order) is read from
-// its frame-major row, so the V^T of a reordering call needs no reordered copy of V
-// (padding keys of a padded grid read as zeros).
+// 64 keys (128 contiguous bytes each).  With gather set, V is the caller's frame-major
+// tensor and key p of head h (in that head's executed order) is read from its
+// frame-major row, so the V^T of a reordering call needs no reordered copy of V.
+// Padding keys of a padded grid read as zeros in both cases.
 #include "vsa_geom.h"
 
 namespace vsa {
@@ -38,10 +38,15 @@ __global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* _
   if (threadIdx.x < kKeys) {
     const int key = k0 + threadIdx.x;
     int sr = key < S ? key : -1;
-    if (gather && sr >= 0) {
+    if ((gather || g.padded) && sr >= 0) {
+      // gather: the frame-major row of the key; a padded grid in place: the key itself,
+      // unless it is padding.  Padding keys become zeros either way: they are never
+      // kept, and whatever the caller's padding rows hold (uninitialised memory, NaN)
+      // must not reach the PV product, where 0 * NaN would be NaN.
       Geom gh = g;
       gh.layout = hl.lay[h];
-      sr = frame_index(gh, key);
+      const int fi = frame_index(gh, key);
+      sr = gather ? fi : (fi >= 0 ? key : -1);
     }
     src_row[threadIdx.x] = sr;
   }
@@ -72,22 +77,16 @@ __global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* _
 }  // namespace
 
 hipError_t launch_transpose_v(const void* v, void* vt, int32_t B, int32_t S, int32_t H, int32_t D,
-                              int32_t s_pad, const Geom* gather, const HeadLayouts* hl, int32_t S_src,
+                              int32_t s_pad, const Geom& g, const HeadLayouts& lay, int32_t gather, int32_t S_src,
                               hipStream_t stream) {
   dim3 grid(s_pad / kKeys, H, B);
-  Geom g{};
-  HeadLayouts lay{};
-  if (gather) {
-    g = *gather;
-    lay = *hl;
-  }
   const int src_len = gather ? S_src : S;
   if (D == 128)
     hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(kThreads), 0, stream, (const uint16_t*)v,
-                       (uint16_t*)vt, S, H, s_pad, g, lay, gather ? 1 : 0, src_len);
+                       (uint16_t*)vt, S, H, s_pad, g, lay, gather, src_len);
   else if (D == 64)
     hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(kThreads), 0, stream, (const uint16_t*)v,
-                       (uint16_t*)vt, S, H, s_pad, g, lay, gather ? 1 : 0, src_len);
+                       (uint16_t*)vt, S, H, s_pad, g, lay, gather, src_len);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

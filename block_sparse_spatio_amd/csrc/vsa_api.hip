@@ -204,6 +204,27 @@ vsa_status build_table(const vsa_mask_desc* masks, int32_t H, const vsa_grid* g,
 
 int elem_size(vsa_dtype dt) { return dt == VSA_BF16 ? 2 : 4; }
 
+// Byte sizes of the arrays of vsa_tile_lists, each rounded up to 256 bytes, in struct
+// order: cls, n_full, n_bnd, full_idx, bnd_idx, bnd_offs.
+vsa_status tile_list_sizes(const vsa_grid* grid, vsa_layout layout, int32_t U, int32_t Bq, int32_t Bk,
+                           size_t sz[6]) {
+  long long S;
+  vsa_status st = check_grid(grid, layout, false, &S);
+  if (st != VSA_OK) return st;
+  if (U < 1 || U > VSA_MAX_UNIQUE_MASKS) return fail(VSA_ERR_INVALID_ARG, "U=%d (1..%d)", U, VSA_MAX_UNIQUE_MASKS);
+  if (Bq < 1 || Bk < 1 || Bq > 4096 || Bk > 4096) return fail(VSA_ERR_INVALID_ARG, "tile sizes must be in 1..4096");
+  S = exec_len(grid, layout);
+  const size_t nQ = (size_t)((S + Bq - 1) / Bq), nK = (size_t)((S + Bk - 1) / Bk), rows = (size_t)U * nQ;
+  auto a256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  sz[0] = a256(rows * nK);
+  sz[1] = a256(rows * 4);
+  sz[2] = a256(rows * 4);
+  sz[3] = a256(rows * nK * 4);
+  sz[4] = a256(rows * nK * 4);
+  sz[5] = a256((rows + 1) * 8);
+  return VSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -247,6 +268,38 @@ vsa_status vsa_seq_len(const vsa_grid* grid, vsa_layout layout, int32_t* S) {
   return ok();
 }
 
+vsa_status vsa_tile_lists_bytes(const vsa_grid* grid, vsa_layout layout, int32_t U, int32_t Bq, int32_t Bk,
+                                size_t* bytes) {
+  if (!bytes) return fail(VSA_ERR_INVALID_ARG, "bytes is NULL");
+  size_t sz[6];
+  vsa_status st = tile_list_sizes(grid, layout, U, Bq, Bk, sz);
+  if (st != VSA_OK) return st;
+  *bytes = sz[0] + sz[1] + sz[2] + sz[3] + sz[4] + sz[5];
+  return ok();
+}
+
+vsa_status vsa_tile_lists_carve(const vsa_grid* grid, vsa_layout layout, int32_t U, int32_t Bq, int32_t Bk,
+                                void* base, vsa_tile_lists* out) {
+  if (!base || !out) return fail(VSA_ERR_INVALID_ARG, "base and out must be non-NULL");
+  if ((uintptr_t)base & 255) return fail(VSA_ERR_INVALID_ARG, "base must be 256-byte aligned");
+  size_t sz[6];
+  vsa_status st = tile_list_sizes(grid, layout, U, Bq, Bk, sz);
+  if (st != VSA_OK) return st;
+  char* p = (char*)base;
+  out->cls = (uint8_t*)p;
+  p += sz[0];
+  out->n_full = (int32_t*)p;
+  p += sz[1];
+  out->n_bnd = (int32_t*)p;
+  p += sz[2];
+  out->full_idx = (int32_t*)p;
+  p += sz[3];
+  out->bnd_idx = (int32_t*)p;
+  p += sz[4];
+  out->bnd_offs = (int64_t*)p;
+  return ok();
+}
+
 vsa_status vsa_classify_tiles(const vsa_grid* grid, vsa_layout layout, const vsa_mask_desc* masks, int32_t H,
                               int32_t Bq, int32_t Bk, const vsa_tile_lists* out, void* stream) {
   return vsa_classify_tiles_ex(grid, layout, masks, H, Bq, Bk, 0, out, stream);
@@ -286,8 +339,10 @@ vsa_status vsa_boundary_words(const vsa_grid* grid, vsa_layout layout, const vsa
     return fail(VSA_ERR_UNSUPPORTED, "mask words for tiles Bq=%d Bk=%d (supported: Bq 64/128/256, Bk 64)", Bq, Bk);
   if (!tiles || !tiles->n_bnd || !tiles->bnd_idx)
     return fail(VSA_ERR_INVALID_ARG, "tile lists (n_bnd, bnd_idx) must be non-NULL");
-  if (cap < 0) return fail(VSA_ERR_INVALID_ARG, "cap=%d is negative", cap);
-  if (cap > 0 && !words) return fail(VSA_ERR_INVALID_ARG, "words is NULL");
+  if (cap < 0 && cap != VSA_WORDS_COMPACT) return fail(VSA_ERR_INVALID_ARG, "cap=%d is negative", cap);
+  if (cap == VSA_WORDS_COMPACT && !tiles->bnd_offs)
+    return fail(VSA_ERR_INVALID_ARG, "the compact table (cap = VSA_WORDS_COMPACT) needs tiles->bnd_offs");
+  if (cap != 0 && !words) return fail(VSA_ERR_INVALID_ARG, "words is NULL");
   if (((uintptr_t)words & 15)) return fail(VSA_ERR_INVALID_ARG, "words must be 16-byte aligned");
   vsa::MaskTable table;
   vsa::HeadMap hm;
@@ -298,7 +353,7 @@ vsa_status vsa_boundary_words(const vsa_grid* grid, vsa_layout layout, const vsa
   const int32_t nQ = (int32_t)((S + Bq - 1) / Bq), nK = (int32_t)((S + Bk - 1) / Bk);
   if (cap > nK) return fail(VSA_ERR_INVALID_ARG, "cap=%d above the %d key tiles", cap, nK);
   hipError_t e = vsa::launch_boundary_words(make_geom(grid, layout), table, U, Bq, nQ, nK, tiles->n_bnd,
-                                            tiles->bnd_idx, words, cap, (hipStream_t)stream);
+                                            tiles->bnd_idx, tiles->bnd_offs, words, cap, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "mask words launch");
   return ok();
 }
@@ -366,8 +421,10 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   if (!tiles || !tiles->n_full || !tiles->n_bnd || !tiles->full_idx || !tiles->bnd_idx)
     return fail(VSA_ERR_INVALID_ARG, "tile lists must be non-NULL");
   if (!isfinite(scale)) return fail(VSA_ERR_INVALID_ARG, "scale is not finite");
-  if (words_cap < 0 || (words_cap > 0 && !words) || (words && words_cap == 0))
+  if ((words_cap < 0 && words_cap != VSA_WORDS_COMPACT) || (words_cap != 0 && !words) || (words && words_cap == 0))
     return fail(VSA_ERR_INVALID_ARG, "words and words_cap must be both set or both unset (words_cap=%d)", words_cap);
+  if (words_cap == VSA_WORDS_COMPACT && !tiles->bnd_offs)
+    return fail(VSA_ERR_INVALID_ARG, "the compact word table (VSA_WORDS_COMPACT) needs tiles->bnd_offs");
   if (words && dtype != VSA_BF16) return fail(VSA_ERR_UNSUPPORTED, "precomputed mask words are for bf16 only");
   if (words && (flags & VSA_FWD_TILE_ALIGNED))
     return fail(VSA_ERR_INVALID_ARG, "precomputed mask words do not apply to VSA_FWD_TILE_ALIGNED lists");
@@ -375,6 +432,14 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   const bool reorder = (flags & VSA_FWD_REORDER_IO) != 0;
   const size_t eb = elem_size(dtype);
   const size_t nelem = (size_t)B * S_exec * H * D;  // one reordered tensor
+  // every limit of the kernels is checked here, before anything is enqueued: offsets
+  // inside one batch item are 32-bit, batch items are a grid dimension (<= 65535), and
+  // the bf16 kernel's one-dimensional grid holds 8*ceil(nQ/8)*B*H workgroups
+  if (S_exec * H * D >= (1LL << 31))
+    return fail(VSA_ERR_UNSUPPORTED, "S*H*D = %lld elements per batch item (must be below 2^31)", S_exec * H * D);
+  if (B > 65535) return fail(VSA_ERR_UNSUPPORTED, "B=%d above 65535", B);
+  if (dtype == VSA_BF16 && 8LL * ((S_exec + Bq - 1) / Bq + 7) / 8 * B * H > 0x7fffffffLL)
+    return fail(VSA_ERR_UNSUPPORTED, "B*H*ceil(S/Bq) = %lld workgroups above 2^31", (S_exec + Bq - 1) / Bq * B * H);
   vsa::MaskTable table;
   vsa::HeadMap hm;
   int32_t U = 0;
@@ -389,7 +454,6 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   }
   if (reorder && !any_permuted)
     return fail(VSA_ERR_INVALID_ARG, "VSA_FWD_REORDER_IO needs a head whose layout is not frame-major");
-  if (reorder && B > 65535) return fail(VSA_ERR_UNSUPPORTED, "VSA_FWD_REORDER_IO with B=%d above 65535", B);
   const size_t need = fwd_ws_bytes(B, (int32_t)S_exec, H, D, dtype, flags);
   if (need && (!workspace || ws_bytes < need))
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
@@ -415,6 +479,7 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   a.full_idx = tiles->full_idx; a.bnd_idx = tiles->bnd_idx;
   a.words = words;
   a.words_cap = words ? words_cap : 0;
+  a.bnd_offs = tiles->bnd_offs;
   if (words_cap > a.nK) return fail(VSA_ERR_INVALID_ARG, "words_cap=%d above the %d key tiles", words_cap, a.nK);
   hipStream_t hs = (hipStream_t)stream;
   const vsa::Geom& G = a.g;
@@ -430,8 +495,7 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
     }
     a.s_pad = (int32_t)vt_pad(a.S);
     void* vt = ws + (reorder ? nelem * eb : 0);
-    if ((e = vsa::launch_transpose_v(v, vt, B, a.S, H, D, a.s_pad, reorder ? &G : nullptr, &hl, S, hs)) !=
-        hipSuccess)
+    if ((e = vsa::launch_transpose_v(v, vt, B, a.S, H, D, a.s_pad, G, hl, reorder ? 1 : 0, S, hs)) != hipSuccess)
       return hip_fail(e, "transpose v");
     a.vt = vt;
     e = vsa::launch_attn_bf16(a, table, hm, hs);

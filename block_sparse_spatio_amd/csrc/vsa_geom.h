@@ -23,6 +23,12 @@ namespace vsa {
 VSA_HD int imin(int a, int b) { return a < b ? a : b; }
 VSA_HD int imax(int a, int b) { return a > b ? a : b; }
 VSA_HD int iabs(int a) { return a < 0 ? -a : a; }
+// entries of list row r in a table indexed by an exclusive prefix sum offs, clamped to
+// [0, n] (offs comes from the classifier; the clamp keeps a malformed table in bounds)
+VSA_HD int row_entries(const int64_t* offs, size_t r, int n) {
+  const int64_t d = offs[r + 1] - offs[r];
+  return d < 0 ? 0 : d > n ? n : (int)d;
+}
 // floor division for a possibly negative numerator and a positive divisor
 VSA_HD int floor_div(int a, int b) {
   return a >= 0 ? a / b : -((-a + b - 1) / b);

@@ -109,9 +109,11 @@ struct FwdArgs {
   // head's order; only k is reordered (v is gathered by the transpose)
   int32_t gather_io;
   // bf16 path, optional: precomputed mask words of boundary list entries j < words_cap,
-  // [U][nQ][words_cap][Bq/32 waves][64 lanes] (launch_boundary_words)
+  // [U][nQ][words_cap][Bq/32 waves][64 lanes] (launch_boundary_words); words_cap < 0:
+  // the compact table, entry j of list row r at bnd_offs[r] + j
   const uint32_t* words;
   int32_t words_cap;
+  const int64_t* bnd_offs;
   Geom g;
 };
 
@@ -119,13 +121,16 @@ hipError_t launch_attn_bf16(const FwdArgs& a, const MaskTable& masks, const Head
                             hipStream_t stream);
 hipError_t launch_attn_f32(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
                            hipStream_t stream);
+// cap < 0: the compact table indexed by bnd_offs
 hipError_t launch_boundary_words(const Geom& g, const MaskTable& masks, int32_t U, int32_t Bq, int32_t nQ,
-                                 int32_t nK, const int32_t* n_bnd, const int32_t* bnd_idx, uint32_t* words,
-                                 int32_t cap, hipStream_t stream);
-// gather (may be NULL): v is frame-major with S_src rows per batch item and key p of
-// head h is its frame-major row under layout hl->lay[h] of *gather (zeros for padding)
+                                 int32_t nK, const int32_t* n_bnd, const int32_t* bnd_idx, const int64_t* bnd_offs,
+                                 uint32_t* words, int32_t cap, hipStream_t stream);
+// g, hl: the call's geometry and every head's executed order.  gather != 0: v is
+// frame-major with S_src rows per batch item and key p of head h is its frame-major row
+// under layout hl.lay[h]; else v is in the executed order.  Padding keys of a padded grid
+// are written as zeros either way.
 hipError_t launch_transpose_v(const void* v, void* vt, int32_t B, int32_t S, int32_t H, int32_t D,
-                              int32_t s_pad, const Geom* gather, const HeadLayouts* hl, int32_t S_src,
+                              int32_t s_pad, const Geom& g, const HeadLayouts& hl, int32_t gather, int32_t S_src,
                               hipStream_t stream);
 hipError_t launch_reorder(const void* src, void* dst, int32_t elem_bytes, int32_t B,
                           int32_t H, int32_t D, const Geom& g, const HeadLayouts& hl,

@@ -7,11 +7,13 @@
 // register layout the bf16 forward consumes, so that the forward reads one 32-bit word
 // per lane from the lists' side table instead.
 //
-// Layout of the output: [U][nQ][cap][Bq/32][64] words.  Word (w, lane) of boundary entry
-// j of query tile qt belongs to query row qt*Bq + w*32 + (lane & 31) and holds keys
-// 8*(lane >> 5) + {0..7}, + {16..23}, + {32..39}, + {48..55} of the key tile, in that
-// order from bit 0 (the keys of that lane's score registers).  Rows past S take row S-1,
-// as in the forward.  Entries j >= min(n_bnd, cap) are not written.
+// Layout of the output: [U][nQ][cap][Bq/32][64] words, or with cap < 0 the compact
+// [N][Bq/32][64] whose list row r starts at entry bnd_offs[r] (the exclusive prefix sum
+// of the list lengths, N their total).  Word (w, lane) of boundary entry j of query tile
+// qt belongs to query row qt*Bq + w*32 + (lane & 31) and holds keys 8*(lane >> 5) +
+// {0..7}, + {16..23}, + {32..39}, + {48..55} of the key tile, in that order from bit 0
+// (the keys of that lane's score registers).  Rows past S take row S-1, as in the
+// forward.  Entries j >= min(n_bnd, cap) are not written.
 //
 // One thread per query row computes its 64-bit row mask (vsa_geom.h) and writes both
 // lanes' words; gridDim.z strides over the entries.  The list row is staged in LDS with
@@ -29,6 +31,7 @@ constexpr int kStage = 1024;  // list entries staged in LDS at a time (a multipl
 __global__ __launch_bounds__(256) void boundary_words_kernel(Geom g_call, MaskTable masks, int Bq, int nQ, int nK,
                                                              const int32_t* __restrict__ n_bnd,
                                                              const int32_t* __restrict__ bnd_idx,
+                                                             const int64_t* __restrict__ bnd_offs,
                                                              uint32_t* __restrict__ words, int cap) {
   const int qt = blockIdx.x, u = blockIdx.y;
   const DevMask m = masks.m[u];
@@ -37,13 +40,16 @@ __global__ __launch_bounds__(256) void boundary_words_kernel(Geom g_call, MaskTa
   const bool stripe = m.kind == VSA_MASK_STRIPE;
   const Divisor dss = make_divisor(stripe ? m.Ss : 1), dts = make_divisor(stripe ? m.Ts : 1);
   const size_t row = (size_t)u * nQ + qt;
-  const int nb = imin(imin(imax(n_bnd[row], 0), nK), cap);
+  const int nb_list = imin(imax(n_bnd[row], 0), nK);
+  // compact table: the row owns entries [bnd_offs[row], bnd_offs[row + 1])
+  const int nb = imin(nb_list, cap < 0 ? row_entries(bnd_offs, row, nK) : cap);
   const int r = threadIdx.x;  // query row inside the tile
   const int qrow = qt * Bq + r;
   const QueryPos qpos = make_query(g, m, qrow < g.S ? qrow : g.S - 1);
   const int nw = Bq / 32;
   const int32_t* list = bnd_idx + row * nK;
-  uint32_t* out = words + row * cap * (size_t)(nw * 64) + (r >> 5) * 64 + (r & 31);
+  const size_t entry0 = cap < 0 ? (size_t)bnd_offs[row] : row * (size_t)cap;  // first entry of the row
+  uint32_t* out = words + entry0 * (size_t)(nw * 64) + (r >> 5) * 64 + (r & 31);
   __shared__ int s_kt[kStage];
   for (int base = 0; base < nb; base += kStage) {
     const int cnt = imin(kStage, nb - base);
@@ -67,12 +73,12 @@ __global__ __launch_bounds__(256) void boundary_words_kernel(Geom g_call, MaskTa
 }  // namespace
 
 hipError_t launch_boundary_words(const Geom& g, const MaskTable& masks, int32_t U, int32_t Bq, int32_t nQ,
-                                 int32_t nK, const int32_t* n_bnd, const int32_t* bnd_idx, uint32_t* words,
-                                 int32_t cap, hipStream_t stream) {
+                                 int32_t nK, const int32_t* n_bnd, const int32_t* bnd_idx, const int64_t* bnd_offs,
+                                 uint32_t* words, int32_t cap, hipStream_t stream) {
   if (Bq % 32 || Bq > 256 || Bq <= 0) return hipErrorInvalidValue;
   if (nQ == 0 || U == 0 || cap == 0) return hipSuccess;
   hipLaunchKernelGGL(boundary_words_kernel, dim3(nQ, U, kStride), dim3(Bq), 0, stream, g, masks, Bq, nQ, nK, n_bnd,
-                     bnd_idx, words, cap);
+                     bnd_idx, bnd_offs, words, cap);
   return hipGetLastError();
 }
 

@@ -134,15 +134,23 @@ enum { VSA_TILE_EMPTY = 0, VSA_TILE_FULL = 1, VSA_TILE_BOUNDARY = 2 };
  *   full_idx  int32 [U][nQ][nK]  ascending FULL key-tile indices in the first
  *                                n_full entries of each row; the rest is unspecified
  *   bnd_idx   int32 [U][nQ][nK]  same for BOUNDARY tiles
+ *   bnd_offs  int64 [U*nQ + 1]   exclusive prefix sum of n_bnd over the list rows in
+ *                                (u, qt) order, bnd_offs[U*nQ] = total boundary entries
+ *                                (may be NULL: not written); it indexes the compact
+ *                                boundary-word table (vsa_boundary_words, cap
+ *                                VSA_WORDS_COMPACT)
  * A tile reaching past S is padded and never FULL (Sparse VideoGen on TPU,
  * "aligning the sparse mask with execution": padding contributes zero weight).
- * Unique descriptors are numbered in order of first appearance in masks[]. */
+ * Unique descriptors are numbered in order of first appearance in masks[]; the
+ * head -> descriptor map is vsa_unique_masks' head_map (a host array: the kernels take
+ * it as a launch argument, so no device copy exists). */
 typedef struct {
   uint8_t* cls;
   int32_t* n_full;
   int32_t* n_bnd;
   int32_t* full_idx;
   int32_t* bnd_idx;
+  int64_t* bnd_offs;
 } vsa_tile_lists;
 
 /* Limits. */
@@ -163,6 +171,17 @@ vsa_status vsa_tile_counts(const vsa_grid* grid, int32_t Bq, int32_t Bk, int32_t
 /* Executed sequence length of a layout: T*Hg*Wg, or T'*H'*W' for VSA_LAYOUT_TILE_PADDED.
  * Tile lists of that layout have nQ = ceil(S/Bq), nK = ceil(S/Bk). */
 vsa_status vsa_seq_len(const vsa_grid* grid, vsa_layout layout, int32_t* S);
+
+/* Device bytes of one allocation that holds every array of vsa_tile_lists for U
+ * distinct masks on this grid, layout and tile size (cls, n_full, n_bnd, full_idx,
+ * bnd_idx, bnd_offs, each starting on a 256-byte boundary), and the carving of such an
+ * allocation into the struct.  `base` is only offset, never dereferenced, so it may be
+ * any caller-owned device pointer (256-byte aligned).  INVALID_ARG for a bad grid,
+ * U outside 1..VSA_MAX_UNIQUE_MASKS or tiles outside 1..4096. */
+vsa_status vsa_tile_lists_bytes(const vsa_grid* grid, vsa_layout layout, int32_t U, int32_t Bq,
+                                int32_t Bk, size_t* bytes);
+vsa_status vsa_tile_lists_carve(const vsa_grid* grid, vsa_layout layout, int32_t U, int32_t Bq,
+                                int32_t Bk, void* base, vsa_tile_lists* out);
 
 /* Tile classification -------------------------------------------------------- */
 
@@ -236,7 +255,10 @@ vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D,
  *   workspace, ws_bytes: device scratch, 16-byte aligned, owned by the caller and
  *             free again once the stream has run the call; see
  *             vsa_fwd_workspace_bytes (may be NULL when 0 bytes are needed)
- * Output rows whose query has no kept key are 0.  D must be 64 or 128.
+ * Output rows whose query has no kept key are 0.  D must be 64 or 128.  The kernels
+ * index one batch item's [S][H][D] elements with 32-bit offsets, so S*H*D (S the
+ * executed length) must be below 2^31: larger calls return UNSUPPORTED before anything
+ * is enqueued.
  * The full tiles take an unmasked path and boundary tiles an element-masked path;
  * both feed one online softmax per query row, so the result does not depend on
  * the split (Sparse VideoGen on TPU, "avoid in-tile masking ..."). */
@@ -260,12 +282,17 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
  *          lists, not rounded ones); Bq in {64, 128, 256}, Bk = 64
  *   words: device uint32 [U][nQ][cap][Bq/32][64] (U unique masks, nQ = ceil(S/Bq) with
  *          S the executed length); entry j < min(n_bnd, cap) of a list row holds the
- *          masks of that row's j-th boundary tile; other entries are not written
- *   cap:   entries per list row, 0..nK (a forward masks entries past cap itself)
+ *          masks of that row's j-th boundary tile; other entries are not written.
+ *          Compact form (cap = VSA_WORDS_COMPACT): uint32 [N][Bq/32][64] with
+ *          N = tiles->bnd_offs[U*nQ], the total of the boundary lists; entry j of list
+ *          row r is entry bnd_offs[r] + j.  Needs tiles->bnd_offs from the classifier.
+ *   cap:   entries per list row, 0..nK (a forward masks entries past cap itself), or
+ *          VSA_WORDS_COMPACT
  * Word (w, l) of an entry belongs to query row w*32 + (l mod 32) of the query tile
  * (rows past S use row S-1) and holds, from bit 0, whether keys 8*(l div 32) + {0..7},
  * {16..23}, {32..39}, {48..55} of the key tile are kept.  16-byte aligned.  Asynchronous
  * on stream; integer-exact. */
+#define VSA_WORDS_COMPACT (-1)
 vsa_status vsa_boundary_words(const vsa_grid* grid, vsa_layout layout,
                               const vsa_mask_desc* masks, int32_t H, int32_t Bq,
                               int32_t Bk, const vsa_tile_lists* tiles, uint32_t* words,
@@ -274,9 +301,11 @@ vsa_status vsa_boundary_words(const vsa_grid* grid, vsa_layout layout,
 /* vsa_sparse_attn_fwd reading the boundary masks of list entries j < words_cap from
  * words (vsa_boundary_words with the same arguments and cap = words_cap); the output is
  * identical.  Query tiles whose boundary list fits in the table (n_bnd <= words_cap, so
- * every list with cap = nK or cap = the longest list) run with no mask arithmetic at
- * all; the others derive the masks of the entries past the cap.  words = NULL with
- * words_cap = 0 is vsa_sparse_attn_fwd.  bf16 only, not with VSA_FWD_TILE_ALIGNED. */
+ * every list with cap = nK or cap = the longest list, and every list of a compact table,
+ * words_cap = VSA_WORDS_COMPACT, which reads tiles->bnd_offs) run with no mask
+ * arithmetic at all; the others derive the masks of the entries past the cap.
+ * words = NULL with words_cap = 0 is vsa_sparse_attn_fwd.  bf16 only, not with
+ * VSA_FWD_TILE_ALIGNED. */
 vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
                                   float* lse, vsa_dtype dtype, int32_t B, int32_t S,
                                   int32_t H, int32_t D, const vsa_grid* grid,

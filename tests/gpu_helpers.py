@@ -43,21 +43,6 @@ def assert_close(got, ref, dtype, what=""):
     return err.max(), err.mean()
 
 
-def sample_rows_per_tile(S, Bq, seed, per_tile=1, max_tiles=None):
-    """A seeded row sample covering query tiles: the first and last row of each chosen
-    tile plus per_tile random rows, sorted and unique."""
-    rng = np.random.default_rng(seed)
-    nQ = -(-S // Bq)
-    tiles = np.arange(nQ)
-    if max_tiles is not None and nQ > max_tiles:
-        tiles = np.unique(np.concatenate([[0, nQ - 1], rng.choice(nQ, max_tiles - 2, replace=False)]))
-    rows = []
-    for t in tiles:
-        lo, hi = t * Bq, min(S, (t + 1) * Bq) - 1
-        rows += [lo, hi] + list(rng.integers(lo, hi + 1, per_tile))
-    return np.unique(np.array(rows))
-
-
 def oracle_lists(cls_row):
     return (np.flatnonzero(cls_row == oracle.FULL), np.flatnonzero(cls_row == oracle.BOUNDARY))
 

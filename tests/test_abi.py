@@ -37,7 +37,7 @@ def test_header_compiles_as_c(tmp_path):
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(_lib.vsa_grid) == 24
     assert ctypes.sizeof(_lib.vsa_mask_desc) == 60
-    assert ctypes.sizeof(_lib.vsa_tile_lists) == 40
+    assert ctypes.sizeof(_lib.vsa_tile_lists) == 48
 
 
 def test_unique_masks_and_counts():
@@ -87,7 +87,7 @@ def _call_fwd(**over):
     args = dict(q=0x1000, k=0x2000, v=0x3000, o=0x4000, lse=None, dtype=vsa.VSA_BF16, B=1, S=256, H=2, D=64,
                 layout=0, Bq=64, Bk=64, scale=0.0, flags=0, ws=0xA000, ws_bytes=1 << 40)
     args.update(over)
-    lists = _lib.vsa_tile_lists(0x5000, 0x6000, 0x7000, 0x8000, 0x9000)
+    lists = _lib.vsa_tile_lists(0x5000, 0x6000, 0x7000, 0x8000, 0x9000, None)
     arr = _lib.make_masks(masks)
     st = lib.vsa_sparse_attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dtype"],
                                  args["B"], args["S"], args["H"], args["D"], ctypes.byref(_lib.make_grid(g)),
@@ -134,14 +134,59 @@ def test_fwd_validation(over, status, needle):
     assert needle in msg
 
 
+def test_fwd_size_limits_enqueue_nothing():
+    """Kernel-side limits are checked before anything is enqueued: S*H*D at or above
+    2^31 (32-bit offsets inside a batch item) and B above 65535 (a grid dimension) are
+    UNSUPPORTED.  The pointers are not device memory, so an enqueued launch or copy
+    could not have returned this status."""
+    g = W.grid(64, 64, 64)  # 262144 tokens; 64 heads of 128 channels: 2^31 elements
+    masks = [W.mask_all()] * 64
+    st, msg = _call_fwd(grid=g, S=262144, H=64, D=128, masks=masks)
+    assert st == -2 and "2^31" in msg, msg
+    st, msg = _call_fwd(grid=g, S=262144, H=64, D=128, masks=masks, dtype=vsa.VSA_F32, Bq=64, Bk=64)
+    assert st == -2 and "2^31" in msg, msg
+    st, msg = _call_fwd(B=65536)
+    assert st == -2 and "65535" in msg, msg
+    # the padded layout counts its padded length
+    gp = W.grid(63, 64, 64, (2, 1, 1))
+    st, msg = _call_fwd(grid=gp, layout=3, S=64 * 64 * 64, H=64, D=128, masks=masks)
+    assert st == -2 and "2^31" in msg, msg
+
+
+def test_tile_lists_bytes_and_carve():
+    """One allocation for every array of the tile lists: sizes and 256-byte aligned
+    offsets in struct order, bnd_offs with U*nQ + 1 entries."""
+    lib = vsa.load()
+    g = _lib.make_grid(W.grid(21, 45, 80))
+    n = ctypes.c_size_t()
+    assert lib.vsa_tile_lists_bytes(ctypes.byref(g), 0, 2, 128, 64, ctypes.byref(n)) == 0
+    nQ, nK, U = 591, 1182, 2
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    sizes = [a(U * nQ * nK), a(U * nQ * 4), a(U * nQ * 4), a(U * nQ * nK * 4), a(U * nQ * nK * 4), a((U * nQ + 1) * 8)]
+    assert n.value == sum(sizes)
+    out = _lib.vsa_tile_lists()
+    base = 0x10000000
+    assert lib.vsa_tile_lists_carve(ctypes.byref(g), 0, 2, 128, 64, base, ctypes.byref(out)) == 0
+    offs = [out.cls, out.n_full, out.n_bnd, out.full_idx, out.bnd_idx, out.bnd_offs]
+    assert offs == [base + sum(sizes[:i]) for i in range(6)]
+    assert lib.vsa_tile_lists_carve(ctypes.byref(g), 0, 2, 128, 64, base + 8, ctypes.byref(out)) == -1
+    assert "aligned" in vsa.vsa_last_error()
+    assert lib.vsa_tile_lists_bytes(ctypes.byref(g), 0, 0, 128, 64, ctypes.byref(n)) == -1
+    assert lib.vsa_tile_lists_bytes(ctypes.byref(g), 0, 2, 0, 64, ctypes.byref(n)) == -1
+    # the padded layout sizes the lists by its padded length
+    gp = _lib.make_grid(W.grid(21, 45, 80, (3, 8, 16)))
+    assert lib.vsa_tile_lists_bytes(ctypes.byref(gp), 3, 1, 128, 64, ctypes.byref(n)) == 0
+    assert n.value == a(630 * 1260) + 2 * a(630 * 4) + 2 * a(630 * 1260 * 4) + a(631 * 8)
+
+
 def test_classify_validation():
     lib = vsa.load()
     arr = _lib.make_masks([W.mask_spatial(1)])
-    lists = _lib.vsa_tile_lists(None, None, None, None, None)
+    lists = _lib.vsa_tile_lists(None, None, None, None, None, None)
     st = lib.vsa_classify_tiles(ctypes.byref(_lib.make_grid(W.grid(4, 8, 8))), 0, arr, 1, 64, 64,
                                 ctypes.byref(lists), None)
     assert st == -1 and "non-NULL" in vsa.vsa_last_error()
-    lists = _lib.vsa_tile_lists(0x10, 0x20, 0x30, 0x40, 0x50)
+    lists = _lib.vsa_tile_lists(0x10, 0x20, 0x30, 0x40, 0x50, None)
     st = lib.vsa_classify_tiles(ctypes.byref(_lib.make_grid(W.grid(0, 8, 8))), 0, arr, 1, 64, 64,
                                 ctypes.byref(lists), None)
     assert st == -1 and "positive" in vsa.vsa_last_error()
@@ -231,7 +276,7 @@ def test_merge_validation(kw, status, needle):
 def test_classify_ex_validation():
     lib = vsa.load()
     arr = _lib.make_masks([W.mask_spatial(1)])
-    lists = _lib.vsa_tile_lists(0x10, 0x20, 0x30, 0x40, 0x50)
+    lists = _lib.vsa_tile_lists(0x10, 0x20, 0x30, 0x40, 0x50, None)
     g = ctypes.byref(_lib.make_grid(W.grid(4, 8, 8)))
     st = lib.vsa_classify_tiles_ex(g, 0, arr, 1, 64, 64, 2, ctypes.byref(lists), None)
     assert st == -1 and "flag" in vsa.vsa_last_error()
@@ -245,7 +290,7 @@ def _call_fwd_ex(words, cap, **over):
     arr = _lib.make_masks([W.mask_spatial(1), W.mask_temporal(1)])
     args = dict(dtype=vsa.VSA_BF16, flags=0, Bq=64)
     args.update(over)
-    lists = _lib.vsa_tile_lists(0x5000, 0x6000, 0x7000, 0x8000, 0x9000)
+    lists = _lib.vsa_tile_lists(0x5000, 0x6000, 0x7000, 0x8000, 0x9000, None)
     st = lib.vsa_sparse_attn_fwd_ex(0x1000, 0x2000, 0x3000, 0x4000, None, args["dtype"], 1, 256, 2, 64,
                                     ctypes.byref(_lib.make_grid(g)), 0, arr, ctypes.byref(lists), args["Bq"], 64,
                                     0.0, args["flags"], words, cap, 0xA000, 1 << 40, None)
@@ -255,7 +300,9 @@ def _call_fwd_ex(words, cap, **over):
 @pytest.mark.parametrize("words,cap,over,status,needle", [
     (None, 3, {}, -1, "both set"),
     (0xB000, 0, {}, -1, "both set"),
-    (0xB000, -1, {}, -1, "both set"),
+    (0xB000, -2, {}, -1, "both set"),
+    (None, -1, {}, -1, "both set"),
+    (0xB000, -1, {}, -1, "bnd_offs"),  # the compact table needs the list offsets
     (0xB000, 5, {}, -1, "above the 4 key tiles"),
     (0xB004, 2, {}, -1, "aligned"),
     (0xB000, 2, dict(dtype=vsa.VSA_F32), -2, "bf16 only"),
@@ -271,15 +318,16 @@ def test_boundary_words_validation():
     lib = vsa.load()
     arr = _lib.make_masks([W.mask_spatial(1), W.mask_stripe(1, 0, 2, 1, 0, 5)])
     g = ctypes.byref(_lib.make_grid(W.grid(4, 8, 8)))
-    lists = _lib.vsa_tile_lists(0x10, 0x20, 0x30, 0x40, 0x50)
+    lists = _lib.vsa_tile_lists(0x10, 0x20, 0x30, 0x40, 0x50, None)
     cases = [
         (dict(Bk=32), -2, "Bk 64"),
         (dict(Bq=32), -2, "Bq 64/128/256"),
         (dict(cap=5), -1, "above the 4 key tiles"),
-        (dict(cap=-1), -1, "negative"),
+        (dict(cap=-2), -1, "negative"),
+        (dict(cap=-1), -1, "bnd_offs"),  # VSA_WORDS_COMPACT without list offsets
         (dict(words=None), -1, "words is NULL"),
         (dict(words=0x1008), -1, "aligned"),
-        (dict(lists=_lib.vsa_tile_lists(0x10, 0x20, None, 0x40, 0x50)), -1, "non-NULL"),
+        (dict(lists=_lib.vsa_tile_lists(0x10, 0x20, None, 0x40, 0x50, None)), -1, "non-NULL"),
         (dict(grid=ctypes.byref(_lib.make_grid(W.grid(0, 8, 8)))), -1, "positive"),
     ]
     for over, status, needle in cases:

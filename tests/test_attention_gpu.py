@@ -8,7 +8,7 @@ import torch
 import block_sparse_spatio_amd as vsa
 import oracle
 import workloads as W
-from tests.gpu_helpers import assert_close, dev, run_attention, sample_rows_per_tile, say
+from tests.gpu_helpers import assert_close, dev, run_attention, say
 
 pytestmark = pytest.mark.gpu
 
@@ -161,52 +161,6 @@ def test_tile_aligned_forward(gpu_lib, case):
         assert np.abs(got[fin] - ref_lse[fin]).max() <= (5e-3 if dtype == "bf16" else 1e-5)
 
 
-# ---------------------------------------------------------------------------
-# full-size configurations, in the launch configuration the benchmark times
-# ---------------------------------------------------------------------------
-_FULL = {}
-
-
-def _full_inputs(name):
-    if name not in _FULL:
-        _FULL.clear()
-        cfg = W.config(name)
-        S = W.seq_len(cfg["grid"])
-        say(f"drawing inputs for {name}")
-        _FULL[name] = (cfg, W.qkv(cfg["B"], S, cfg["H"], cfg["D"], cfg["dtype"], seed=cfg["seed"]))
-    return _FULL[name]
-
-
-@pytest.mark.parametrize("name,Bq,which", [
-    ("wan_mixed", 128, "masks"), ("wan_single", 128, "masks"), ("wan_single", 64, "masks"),
-    ("wan_single", 256, "masks"), ("wan_single", 128, "extra_masks"), ("sta_hunyuan", 128, "masks"),
-    ("stripe_route", 128, "masks")])
-def test_full_config_sampled_rows(gpu_lib, name, Bq, which):
-    """Full-size workloads in the launch configuration the benchmark times (boundary
-    masks from the word table, cap = nK): sampled rows against the oracle."""
-    cfg, (q, k, v) = _full_inputs(name)
-    g, layout, masks = cfg["grid"], cfg["layout"], cfg[which]
-    S = W.seq_len(g)
-    say(f"full config {name} Bq={Bq} {which}: S={S} H={cfg['H']} B={cfg['B']}")
-    d = dev()
-    qd, kd, vd = q.to(d), k.to(d), v.to(d)
-    reorder = layout == "tile"
-    tiles = vsa.vsa_classify_tiles(g, layout, masks, Bq, cfg["Bk"], device=d, with_cls=False)
-    words = vsa.vsa_boundary_words(g, layout, masks, tiles, cap=tiles["nK"])
-    o, lse = vsa.vsa_sparse_attn_fwd(qd, kd, vd, g, layout, masks, tiles, words=words,
-                                     flags=vsa.VSA_FWD_WRITE_LSE | (vsa.VSA_FWD_REORDER_IO if reorder else 0))
-    torch.cuda.synchronize()
-    del words
-    assert torch.isfinite(o).all()
-    # oracle on sampled rows (frame-major indices: the reorder is inside the call)
-    rows = sample_rows_per_tile(S, Bq, seed=3, per_tile=0, max_tiles=24)
-    heads = list(range(0, cfg["H"], max(1, cfg["H"] // 8)))
-    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
-    got = o[:, rows][:, :, heads]
-    assert_close(got, ref_o, "bf16", f"{name} sampled rows")
-    assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3
-
-
 def _head_layout_case(dtype):
     """Grid, masks and inputs with heads in frame-, position- and tile-major order."""
     g = W.grid(6, 16, 16, (2, 8, 8))
@@ -248,30 +202,6 @@ def test_head_layouts_in_place(gpu_lib):
         assert np.abs(lse[:, h] - ref_lse[:, h][:, p.numpy()]).max() <= 5e-3
 
 
-def test_full_config_position_major_sampled_rows(gpu_lib):
-    """Wan 2.1 720p mixed heads, temporal heads position-major with the reorder inside
-    the call (the launch configuration the benchmark times): sampled frame-major rows
-    against the oracle."""
-    name = "wan_mixed"
-    cfg, (q, k, v) = _full_inputs(name)
-    g, masks, Bq = cfg["grid"], cfg["position_masks"], cfg["Bq"]
-    S = W.seq_len(g)
-    say(f"full config {name} position-major temporal heads Bq={Bq}")
-    d = dev()
-    tiles = vsa.vsa_classify_tiles(g, "frame", masks, Bq, cfg["Bk"], device=d, with_cls=False)
-    words = vsa.vsa_boundary_words(g, "frame", masks, tiles, cap=tiles["nK"])
-    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "frame", masks, tiles, words=words,
-                                     flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
-    torch.cuda.synchronize()
-    del words
-    assert torch.isfinite(o).all()
-    rows = sample_rows_per_tile(S, Bq, seed=4, per_tile=0, max_tiles=24)
-    heads = [0, 7, 19, 20, 27, 39]
-    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
-    assert_close(o[:, rows][:, :, heads], ref_o, "bf16", f"{name} position-major sampled rows")
-    assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3
-
-
 def _padded_case(dtype):
     g = W.grid(5, 6, 10, (2, 4, 4))  # padded to 6 x 8 x 12
     masks = [W.mask_sta(3, 1, 3), W.mask_box(1, 2, 3, sink_frames=1), W.mask_stripe(1, 0, 2, 2, 1, 7)]
@@ -308,6 +238,27 @@ def test_padded_in_place(gpu_lib):
     assert np.abs(lse.cpu().numpy()[:, :, real] - ref_lse[:, :, perm[real]]).max() <= 5e-3
 
 
+@pytest.mark.parametrize("dtype,Bq,Bk", [("bf16", 128, 64), ("bf16", 64, 64), ("f32", 64, 32)])
+def test_padded_in_place_nan_padding(gpu_lib, dtype, Bq, Bk):
+    """Padding rows of q, k and v in the padded order may hold anything, here NaN: they
+    are never kept, and the real rows' o and lse equal those with zero padding bit for
+    bit (a padding value must not reach the PV product, where 0 * NaN is NaN)."""
+    g, masks, q, k, v = _padded_case(dtype)
+    pad = torch.from_numpy(oracle.layout_permutation(g, "padded") < 0)
+    zero = [torch.from_numpy(oracle.reorder_tokens(x.float().numpy(), g, layout="padded")).to(x.dtype)
+            for x in (q, k, v)]
+    nan = [x.clone() for x in zero]
+    for x in nan:
+        x[:, pad] = float("nan")
+    say(f"padded in place, NaN padding, {dtype} Bq={Bq} Bk={Bk}")
+    o0, l0, _ = run_attention(*zero, g, "padded", masks, Bq, Bk, flags=vsa.VSA_FWD_WRITE_LSE)
+    o1, l1, _ = run_attention(*nan, g, "padded", masks, Bq, Bk, flags=vsa.VSA_FWD_WRITE_LSE)
+    real = (~pad).to(o0.device)
+    assert torch.isfinite(o1[:, real]).all()
+    assert torch.equal(o0[:, real], o1[:, real])
+    assert torch.equal(l0[:, :, real], l1[:, :, real])
+
+
 def test_padded_tile_aligned_forward(gpu_lib):
     """B3 rounding on the padded order, forward with VSA_FWD_TILE_ALIGNED: equals the
     oracle's attention under the rounded mask (padding keys masked, interior too)."""
@@ -324,29 +275,6 @@ def test_padded_tile_aligned_forward(gpu_lib):
     real = np.flatnonzero(oracle.layout_permutation(g, "padded") >= 0)
     ref_o, _ = oracle.attention(qp, kp, vp, g, "padded", masks, rows=real, round_tiles=(Bq, Bk))
     assert_close(o.cpu()[:, torch.from_numpy(real)], ref_o, "bf16", "padded B3")
-
-
-def test_full_config_padded_sampled_rows(gpu_lib):
-    """Sliding tiles on the padded Wan 2.1 720p latent, reorder in and out inside the
-    call (the launch configuration the benchmark times): sampled rows against the oracle."""
-    cfg = W.config("wan_sta_padded")
-    g, masks, Bq = cfg["grid"], cfg["masks"], cfg["Bq"]
-    S = W.seq_len(g)
-    say("full config wan_sta_padded")
-    q, k, v = W.qkv(cfg["B"], S, cfg["H"], cfg["D"], cfg["dtype"], seed=cfg["seed"])
-    d = dev()
-    tiles = vsa.vsa_classify_tiles(g, "padded", masks, Bq, cfg["Bk"], device=d, with_cls=False)
-    words = vsa.vsa_boundary_words(g, "padded", masks, tiles, cap=tiles["nK"])
-    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "padded", masks, tiles, words=words,
-                                     flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
-    torch.cuda.synchronize()
-    del words
-    assert torch.isfinite(o).all()
-    rows = sample_rows_per_tile(S, Bq, seed=5, per_tile=0, max_tiles=24)
-    heads = [0, 13, 39]
-    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
-    assert_close(o[:, rows][:, :, heads], ref_o, "bf16", "wan_sta_padded sampled rows")
-    assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3
 
 
 @pytest.mark.parametrize("tile", [(1, 9, 1), (1, 9, 2), (2, 3, 4)])
@@ -372,30 +300,3 @@ def test_column_strip_tiles_reorder_io(gpu_lib, tile):
         torch.cuda.synchronize()
         assert_close(o, ref_o, "bf16", f"column strips {tile}, words={words is not None}")
         assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 5e-3
-
-
-def test_full_config_stripes_chosen_orders_sampled_rows(gpu_lib):
-    """The stripe layer with every head in the order the benchmark's cost-based chooser
-    picks (frame-, position- or tile-major over a column-strip grid tile), reorder inside
-    the call and mask words, as the benchmark times it: sampled frame-major rows of heads
-    in every chosen order against the oracle."""
-    import bench
-    name = "stripe_route"
-    cfg, (q, k, v) = _full_inputs(name)
-    d = dev()
-    g, masks = bench.choose_head_layouts(vsa, cfg["grid"], cfg["masks"], cfg["Bq"], cfg["Bk"], d)
-    lays = W.head_layouts(masks, "frame")
-    say(f"full config {name} chosen orders {sorted(set(lays))} grid tile {g['tile_t'], g['tile_h'], g['tile_w']}")
-    tiles = vsa.vsa_classify_tiles(g, "frame", masks, cfg["Bq"], cfg["Bk"], device=d, with_cls=False)
-    words = vsa.vsa_boundary_words(g, "frame", masks, tiles, cap=tiles["nK"])
-    o, lse = vsa.vsa_sparse_attn_fwd(q.to(d), k.to(d), v.to(d), g, "frame", masks, tiles, words=words,
-                                     flags=vsa.VSA_FWD_WRITE_LSE | vsa.VSA_FWD_REORDER_IO)
-    torch.cuda.synchronize()
-    del words
-    assert torch.isfinite(o).all()
-    S = W.seq_len(g)
-    rows = sample_rows_per_tile(S, cfg["Bq"], seed=6, per_tile=0, max_tiles=16)
-    heads = sorted({lays.index(x) for x in set(lays)} | {0, 39})
-    ref_o, ref_lse = oracle.attention(q, k, v, g, "frame", masks, rows=rows, heads=heads)
-    assert_close(o[:, rows][:, :, heads], ref_o, "bf16", f"{name} chosen orders sampled rows")
-    assert np.abs(lse[:, heads][:, :, rows].cpu().numpy() - ref_lse).max() <= 5e-3

@@ -63,8 +63,13 @@ def _case(seed):
 
 
 def _words(g, layout, masks, tiles, cap):
-    out = torch.full((tiles["n_unique"], tiles["nQ"], cap, tiles["Bq"] // 32, 64), SENTINEL, dtype=torch.int32,
-                     device=dev())
+    """A word table pre-filled with a sentinel; cap="compact" for the compact table."""
+    if cap == "compact":
+        n = max(1, int(tiles["bnd_offs"][-1]))
+        out = torch.full((n, tiles["Bq"] // 32, 64), SENTINEL, dtype=torch.int32, device=dev())
+    else:
+        out = torch.full((tiles["n_unique"], tiles["nQ"], cap, tiles["Bq"] // 32, 64), SENTINEL, dtype=torch.int32,
+                         device=dev())
     return vsa.vsa_boundary_words(g, layout, masks, tiles, cap=cap, out=out)
 
 
@@ -74,9 +79,20 @@ def _check_words(g, layout, masks, tiles, words):
     lays = W.head_layouts(masks, layout)
     S = oracle.seq_len(g, layout)
     Bq, nQ, nK, cap = tiles["Bq"], tiles["nQ"], tiles["nK"], words["cap"]
-    w_all = words["words"].cpu().numpy().view(np.uint32)
     n_bnd = tiles["n_bnd"].cpu().numpy()
     bnd_idx = tiles["bnd_idx"].cpu().numpy()
+    compact = cap == vsa.VSA_WORDS_COMPACT
+    if compact:
+        # list row r owns entries [offs[r], offs[r] + n_bnd[r]) of the table
+        offs = tiles["bnd_offs"].cpu().numpy()
+        assert offs[0] == 0 and np.array_equal(np.diff(offs), n_bnd.reshape(-1)), "bnd_offs is not the prefix sum"
+        flat = words["words"].cpu().numpy().view(np.uint32)
+        assert flat.shape[0] == max(1, int(offs[-1]))
+        if offs[-1] == 0:
+            assert np.all(flat == SENTINEL)
+        w_all = None
+    else:
+        w_all = words["words"].cpu().numpy().view(np.uint32)
     cols = np.arange(S)
     checked = 0
     for u in range(U):
@@ -90,18 +106,20 @@ def _check_words(g, layout, masks, tiles, words):
             keep = np.zeros((len(rows), nK * 64), dtype=bool)
             keep[:, :S] = oracle.keep_matrix(desc, g, cq, ck) & col_real[None, :]
             real_rows = oracle.is_real(g, *cq)
-            nb = min(int(n_bnd[u, qt]), cap)
+            nb = int(n_bnd[u, qt]) if compact else min(int(n_bnd[u, qt]), cap)
             for j in range(nb):
                 kt = int(bnd_idx[u, qt, j])
                 bits = keep[:, kt * 64:(kt + 1) * 64][:, _KEY_OF_BIT]  # [rows, 2, 32]
                 want = (bits.astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(-1).astype(np.uint32)
                 r = np.arange(len(rows))
-                got = np.stack([w_all[u, qt, j, r // 32, g2 * 32 + r % 32] for g2 in range(2)], axis=1)
+                ent = flat[offs[u * nQ + qt] + j] if compact else w_all[u, qt, j]
+                got = np.stack([ent[r // 32, g2 * 32 + r % 32] for g2 in range(2)], axis=1)
                 bad = np.nonzero((got != want).any(axis=1) & real_rows)[0]
                 assert bad.size == 0, (f"mask {u} query tile {qt} entry {j} (key tile {kt}): row "
                                        f"{rows[bad[0]]} words {got[bad[0]]} expected {want[bad[0]]}")
                 checked += 1
-            assert np.all(w_all[u, qt, nb:] == SENTINEL), f"mask {u} query tile {qt}: entries past {nb} written"
+            if not compact:
+                assert np.all(w_all[u, qt, nb:] == SENTINEL), f"mask {u} query tile {qt}: entries past {nb} written"
     return checked
 
 
@@ -118,6 +136,11 @@ def test_words_match_oracle(gpu_lib, seed):
     short = _words(g, layout, masks, tiles, max(1, cap // 2))
     torch.cuda.synchronize()
     _check_words(g, layout, masks, tiles, short)
+    # the compact table: exactly one entry per listed boundary tile, every one written
+    compact = _words(g, layout, masks, tiles, "compact")
+    torch.cuda.synchronize()
+    assert compact["cap"] == vsa.VSA_WORDS_COMPACT
+    _check_words(g, layout, masks, tiles, compact)
 
 
 @pytest.mark.parametrize("seed", range(16))
@@ -138,7 +161,7 @@ def test_forward_with_words_is_identical(gpu_lib, seed):
     cap = max(1, int(tiles["n_bnd"].max()))
     # nK and the longest list: every workgroup's list fits (the instance without any mask
     # arithmetic); shorter tables mix it with workgroups that derive the masks past the cap
-    for c in sorted({tiles["nK"], cap, max(1, cap // 2), 1}):
+    for c in sorted({tiles["nK"], cap, max(1, cap // 2), 1}) + ["compact"]:
         words = _words(g, layout, masks, tiles, c)
         o1, l1 = vsa.vsa_sparse_attn_fwd(q, k, v, g, layout, masks, tiles, flags=flags, words=words)
         torch.cuda.synchronize()
@@ -168,7 +191,9 @@ def test_forward_with_words_full_config(gpu_lib, name):
     words = vsa.vsa_boundary_words(g, layout, masks, tiles, cap=cap)
     o1, _ = vsa.vsa_sparse_attn_fwd(q, k, v, g, layout, masks, tiles, words=words)
     del words
-    full = vsa.vsa_boundary_words(g, layout, masks, tiles, cap=tiles["nK"])
+    # the compact table (one entry per listed boundary tile), as the benchmark runs it
+    full = vsa.vsa_boundary_words(g, layout, masks, tiles)
+    say(f"compact table: {full['words'].numel() * 4 / 2**20:.1f} MiB for {int(tiles['bnd_offs'][-1])} entries")
     o2, _ = vsa.vsa_sparse_attn_fwd(q, k, v, g, layout, masks, tiles, words=full)
     torch.cuda.synchronize()
     if layout == "padded":
