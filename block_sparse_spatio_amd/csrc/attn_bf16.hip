@@ -75,18 +75,22 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   const int Bq = 32 * NW;
 
   // ---- workgroup -> (b, h, query tile).  Workgroups are dealt to the 8 XCDs
-  // round-robin; XCD x takes query tiles [x*cq, (x+1)*cq) of every head, so every XCD
-  // sees the same head mix and its resident workgroups share K/V in its L2. ----
-  const int cq = (a.nQ + 7) / 8;
+  // round-robin; XCD x runs, head after head (heaviest first), one contiguous range of
+  // each head's query tiles, the ranges of equal listed cost (the per-call schedule), so
+  // that every XCD gets the same share of work and its resident workgroups share K/V in
+  // its L2.  Workgroups past the end of their range exit at once. ----
+  const int cq = a.cq;
   const int xcd = blockIdx.x & 7;
   const int kk = blockIdx.x >> 3;
-  const int bh = kk / cq;
-  const int qt = xcd * cq + (kk - bh * cq);
-  if (qt >= a.nQ || bh >= a.B * H) return;
-  const int h = bh % H;
-  const int b = bh / H;
-
+  const int rank = kk / cq;  // (head rank, batch item)
+  if (rank >= a.B * H) return;
+  const int h = imin(imax(a.sched[VSA_MAX_UNIQUE_MASKS * 9 + rank / a.B], 0), H - 1);
+  const int b = rank % a.B;
   const int slot = hm.slot[h];
+  const int q_lo = a.sched[slot * 9 + xcd], q_hi = imin(a.sched[slot * 9 + xcd + 1], a.nQ);
+  const int qt = q_lo + (kk - rank * cq);
+  if (qt >= q_hi || qt < 0) return;
+
   const DevMask m_head = masks.m[slot];
   // The body is instantiated for the common (order, mask kind) pairs with both fixed at
   // compile time, so that the per-tile mask arithmetic of a boundary tile carries no
@@ -560,8 +564,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 
 template <int D, int NW>
 hipError_t launch_t(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm, hipStream_t st) {
-  const int cq = (a.nQ + 7) / 8;
-  const long long n_blocks = 8LL * cq * a.B * a.H;
+  const long long n_blocks = 8LL * a.cq * a.B * a.H;
   if (n_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // query tiles whose boundary list is in the word table run the table-driven kernel;
   // with a compact table (cap < 0) or cap >= nK that is every query tile
@@ -579,7 +582,94 @@ hipError_t launch_t(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
   return hipGetLastError();
 }
 
+// Per-call schedule, one workgroup.  Cost of a query tile = 5 per full and 6 per
+// boundary key tile (a boundary tile is about 1.2 full tiles) plus 10 for the per-tile
+// prologue and epilogue.  For every distinct mask u: the prefix sum P of the costs over
+// its query tiles, raw splits s_x = min{k : P(k) >= x*P(nQ)/8}, then the ranges clamped
+// to at most cq tiles each (sched_cq), so that the grid covers every tile.  Then the
+// heads in descending order of their mask's total cost (ties by head index).
+constexpr int kSchedThreads = 1024;
+
+__global__ __launch_bounds__(kSchedThreads) void fwd_schedule_kernel(const int32_t* __restrict__ n_full,
+                                                                     const int32_t* __restrict__ n_bnd, int U,
+                                                                     int nQ, int nK, int H, int cq, HeadMap hm,
+                                                                     int32_t* __restrict__ sched) {
+  __shared__ long long seg[kSchedThreads];
+  __shared__ long long tot[VSA_MAX_UNIQUE_MASKS];
+  __shared__ int raw[8];
+  const int t = threadIdx.x;
+  const int per = (nQ + kSchedThreads - 1) / kSchedThreads;
+  const int i0 = imin(t * per, nQ), i1 = imin(i0 + per, nQ);
+  auto cost = [&](size_t r) -> long long {
+    return 10 + 5LL * imin(imax(n_full[r], 0), nK) + 6LL * imin(imax(n_bnd[r], 0), nK);
+  };
+  for (int u = 0; u < U; ++u) {
+    const size_t row0 = (size_t)u * nQ;
+    long long sum = 0;
+    for (int i = i0; i < i1; ++i) sum += cost(row0 + i);
+    seg[t] = sum;
+    __syncthreads();
+    for (int d = 1; d < kSchedThreads; d <<= 1) {
+      const long long v = t >= d ? seg[t - d] : 0;
+      __syncthreads();
+      seg[t] += v;
+      __syncthreads();
+    }
+    const long long total = seg[kSchedThreads - 1];
+    // P(i0) = seg[t] - sum; raw split x (1..7): the first k with P(k) >= x*total/8
+    long long p = seg[t] - sum;
+    for (int i = i0; i < i1; ++i) {
+      const long long pn = p + cost(row0 + i);
+      for (int x = 1; x < 8; ++x) {
+        const long long tgt = (total * x + 7) / 8;  // P(k) >= x*total/8 <=> 8*P(k) >= x*total
+        if (p < tgt && pn >= tgt) raw[x] = i + 1;
+      }
+      p = pn;
+    }
+    if (t == 0) {
+      tot[u] = total;
+      for (int x = 1; x < 8; ++x)
+        if (total <= 0) raw[x] = 0;
+    }
+    __syncthreads();
+    if (t == 0) {
+      int sp = 0;
+      sched[u * 9] = 0;
+      for (int x = 0; x < 8; ++x) {
+        const int tgt = x < 7 ? raw[x + 1] : nQ;
+        int nx = imin(sp + cq, imax(tgt, nQ - (7 - x) * cq));
+        nx = imax(imin(nx, nQ), sp);
+        sched[u * 9 + x + 1] = nx;
+        sp = nx;
+      }
+    }
+    __syncthreads();
+  }
+  if (t < H) {
+    const long long c = tot[hm.slot[t]];
+    int rank = 0;
+    for (int j = 0; j < H; ++j) {
+      const long long cj = tot[hm.slot[j]];
+      rank += (cj > c) || (cj == c && j < t);
+    }
+    sched[VSA_MAX_UNIQUE_MASKS * 9 + rank] = t;
+  }
+}
+
 }  // namespace
+
+// Query tiles per XCD and head the grid provides: half again the even share, so that a
+// range of equal cost may hold up to 1.5x the average count (the schedule clamps to it).
+int32_t sched_cq(int32_t nQ) { return (int32_t)((3LL * nQ + 15) / 16); }
+
+size_t sched_ints(int32_t U, int32_t H) { return (size_t)VSA_MAX_UNIQUE_MASKS * 9 + VSA_MAX_HEADS; }
+
+hipError_t launch_fwd_schedule(const FwdArgs& a, int32_t U, const HeadMap& hm, int32_t* sched, hipStream_t stream) {
+  if (U < 1 || U > VSA_MAX_UNIQUE_MASKS || a.H > VSA_MAX_HEADS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fwd_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a.n_full, a.n_bnd, U, a.nQ, a.nK,
+                     a.H, a.cq, hm, sched);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_bf16(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm, hipStream_t stream) {
   // element offsets inside one (b, h) slab use 32-bit arithmetic

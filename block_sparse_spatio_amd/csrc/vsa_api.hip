@@ -360,14 +360,17 @@ vsa_status vsa_boundary_words(const vsa_grid* grid, vsa_layout layout, const vsa
 
 // bf16: V^T [B][H][D][S rounded up to 64] (the PV operand, transposed once per call);
 // with VSA_FWD_REORDER_IO, k in each head's executed order before it (q and v are
-// gathered and o scattered by row).  f32 with VSA_FWD_REORDER_IO: reordered copies of
-// q, k and v.
+// gathered and o scattered by row); then the per-call schedule of the grid (a few KB).
+// f32 with VSA_FWD_REORDER_IO: reordered copies of q, k and v.
 static size_t vt_pad(int32_t S) { return ((size_t)S + 63) / 64 * 64; }
+static size_t sched_bytes() {
+  return (vsa::sched_ints(VSA_MAX_UNIQUE_MASKS, VSA_MAX_HEADS) * sizeof(int32_t) + 255) / 256 * 256;
+}
 static size_t fwd_ws_bytes(int32_t B, int32_t S, int32_t H, int32_t D, vsa_dtype dtype, int32_t flags) {
   const size_t eb = elem_size(dtype);
   const size_t copies = dtype == VSA_BF16 ? 1 : 3;
   size_t n = (flags & VSA_FWD_REORDER_IO) ? copies * B * S * H * D * eb : 0;
-  if (dtype == VSA_BF16) n += (size_t)B * H * D * vt_pad(S) * eb;
+  if (dtype == VSA_BF16) n += (size_t)B * H * D * vt_pad(S) * eb + sched_bytes();
   return n;
 }
 
@@ -438,8 +441,9 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   if (S_exec * H * D >= (1LL << 31))
     return fail(VSA_ERR_UNSUPPORTED, "S*H*D = %lld elements per batch item (must be below 2^31)", S_exec * H * D);
   if (B > 65535) return fail(VSA_ERR_UNSUPPORTED, "B=%d above 65535", B);
-  if (dtype == VSA_BF16 && 8LL * ((S_exec + Bq - 1) / Bq + 7) / 8 * B * H > 0x7fffffffLL)
-    return fail(VSA_ERR_UNSUPPORTED, "B*H*ceil(S/Bq) = %lld workgroups above 2^31", (S_exec + Bq - 1) / Bq * B * H);
+  if (dtype == VSA_BF16 && 8LL * vsa::sched_cq((int32_t)((S_exec + Bq - 1) / Bq)) * B * H > 0x7fffffffLL)
+    return fail(VSA_ERR_UNSUPPORTED, "B*H*ceil(S/Bq) = %lld query tiles: the grid would exceed 2^31 workgroups",
+                (S_exec + Bq - 1) / Bq * B * H);
   vsa::MaskTable table;
   vsa::HeadMap hm;
   int32_t U = 0;
@@ -495,6 +499,10 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
     }
     a.s_pad = (int32_t)vt_pad(a.S);
     void* vt = ws + (reorder ? nelem * eb : 0);
+    int32_t* sched = (int32_t*)((char*)vt + (size_t)B * H * D * a.s_pad * eb);
+    a.cq = vsa::sched_cq(a.nQ);
+    a.sched = sched;
+    if ((e = vsa::launch_fwd_schedule(a, U, hm, sched, hs)) != hipSuccess) return hip_fail(e, "schedule");
     if ((e = vsa::launch_transpose_v(v, vt, B, a.S, H, D, a.s_pad, G, hl, reorder ? 1 : 0, S, hs)) != hipSuccess)
       return hip_fail(e, "transpose v");
     a.vt = vt;

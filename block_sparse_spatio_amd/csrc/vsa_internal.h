@@ -114,11 +114,25 @@ struct FwdArgs {
   const uint32_t* words;
   int32_t words_cap;
   const int64_t* bnd_offs;
+  // bf16 path: the per-call schedule (launch_fwd_schedule): for every distinct mask the
+  // query tiles that XCD x runs, [sched[u*9 + x], sched[u*9 + x + 1]), and after the
+  // U*9 entries the heads in descending order of cost; cq = query tiles per XCD and
+  // head that the grid provides (sched_cq, at least every chunk's length)
+  const int32_t* sched;
+  int32_t cq;
   Geom g;
 };
 
 hipError_t launch_attn_bf16(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
                             hipStream_t stream);
+// The bf16 forward's grid serves 8 XCDs; each XCD runs one contiguous range of query
+// tiles of every head (neighbouring tiles share key tiles in that XCD's L2).  The
+// schedule splits each distinct mask's query tiles into 8 ranges of equal listed cost and
+// orders the heads heaviest first; it is written by one small kernel per call.
+int32_t sched_cq(int32_t nQ);
+size_t sched_ints(int32_t U, int32_t H);
+hipError_t launch_fwd_schedule(const FwdArgs& a, int32_t U, const HeadMap& hm, int32_t* sched,
+                               hipStream_t stream);
 hipError_t launch_attn_f32(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
                            hipStream_t stream);
 // cap < 0: the compact table indexed by bnd_offs

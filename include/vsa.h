@@ -233,8 +233,9 @@ vsa_status vsa_classify_tiles_ex(const vsa_grid* grid, vsa_layout layout,
  * B*H*D*S64 elements (S64 = S rounded up to a multiple of 64) that hold V
  * transposed per 64-key block to [B][H][S64/64][D][64], and with VSA_FWD_REORDER_IO
  * B*S*H*D elements more (k in each head's executed order; q and v are gathered and o
- * scattered by row); f32 with VSA_FWD_REORDER_IO: 3*B*S*H*D elements (q, k, v in each
- * head's executed order), without it none. */
+ * scattered by row), plus 3,328 bytes for the per-call schedule that deals each head's
+ * query tiles to the 8 XCDs in ranges of equal listed cost; f32 with VSA_FWD_REORDER_IO: 3*B*S*H*D elements (q, k, v in each head's executed
+ * order), without it none. */
 vsa_status vsa_fwd_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D,
                                    vsa_dtype dtype, int32_t flags, size_t* bytes);
 

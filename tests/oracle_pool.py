@@ -59,3 +59,28 @@ def attention_rows(q, k, v, g, layout, masks, rows, pairs, round_tiles=None):
         for b, h, o, lse in ex.map(_task, tasks):
             out[(b, h)] = (o, lse)
     return out
+
+
+def _profile_task(args):
+    h, qh, kh, vh, g, layout, idx, cands = args
+    err, route = oracle.profile_heads(qh[:, :, None, :], kh[:, :, None, :], vh[:, :, None, :], g, layout,
+                                      idx[None, :], cands)
+    return h, err[0], int(route[0])
+
+
+def profile_heads(q, k, v, g, layout, sample_idx, cands, heads):
+    """oracle.profile_heads for each head in `heads`, one head per task.  q, k, v:
+    [B, S, H, D]; sample_idx: int [H, n].  Returns (err fp64 [len(heads), n_cand], route
+    int32 [len(heads)])."""
+    qa, ka, va = _f32_bhsd(q), _f32_bhsd(k), _f32_bhsd(v)
+    idx = np.asarray(sample_idx)
+    tasks = [(h, qa[:, h], ka[:, h], va[:, h], g, layout, idx[h], cands) for h in heads]
+    err = np.zeros((len(heads), len(cands)))
+    route = np.zeros(len(heads), dtype=np.int32)
+    pos = {h: i for i, h in enumerate(heads)}
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(min(workers(), len(tasks)), mp_context=ctx, initializer=_init) as ex:
+        for h, e, r in ex.map(_profile_task, tasks):
+            err[pos[h]] = e
+            route[pos[h]] = r
+    return err, route

@@ -53,9 +53,10 @@ def test_unique_masks_and_counts():
 
 
 def test_workspace_sizes():
-    vt = 24 * 128 * 115200 * 2  # V^T, S already a multiple of 64
+    sched = 3328  # the per-call schedule of the bf16 grid
+    vt = 24 * 128 * 115200 * 2 + sched  # V^T, S already a multiple of 64
     assert vsa.vsa_fwd_workspace_bytes(1, 115200, 24, 128, vsa.VSA_BF16, 0) == vt
-    assert vsa.vsa_fwd_workspace_bytes(2, 100, 3, 64, vsa.VSA_BF16, 0) == 2 * 3 * 64 * 128 * 2
+    assert vsa.vsa_fwd_workspace_bytes(2, 100, 3, 64, vsa.VSA_BF16, 0) == 2 * 3 * 64 * 128 * 2 + sched
     assert vsa.vsa_fwd_workspace_bytes(2, 100, 3, 64, vsa.VSA_F32, 0) == 0
     assert vsa.vsa_fwd_workspace_bytes(1, 115200, 24, 128, vsa.VSA_BF16, vsa.VSA_FWD_REORDER_IO) \
         == 115200 * 24 * 128 * 2 + vt  # k reordered; q, v gathered, o scattered

@@ -1,30 +1,42 @@
-"""Head profiler on the GPU against the oracle: errors within 1% relative (fp32
-accumulation of bf16-rounded probabilities against fp64), routes equal wherever the
-oracle's margin between the candidates exceeds that tolerance, and the GPU's own
-route is the argmin of the GPU's own errors."""
+"""Head profiler on the GPU against the oracle: every deviation within 1e-3 relative of
+the oracle's (fp32 accumulation of bf16-rounded probabilities against fp64: measured at
+most 5e-5 on these cases), and the route equal to the oracle's on every head; where the
+two best candidates are closer than the tolerance allows to separate, the test says so
+instead of skipping the head.  The GPU's own route is the argmin of its own errors."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads as W
+from tests import oracle_pool
 from tests.gpu_helpers import dev, say
 
 pytestmark = pytest.mark.gpu
 
-REL = 1e-2
+REL = 1e-3
+ATOL = 1e-5
 
 
-def _check(err_g, route_g, err_o, route_o):
+def _check(err_g, route_g, err_o, route_o, what=""):
     err_g = err_g.cpu().numpy().astype(np.float64)
     route_g = route_g.cpu().numpy()
     assert np.all(err_g[:, 0] == 0)
-    assert np.allclose(err_g, err_o, rtol=REL, atol=1e-4), np.abs(err_g - err_o).max()
+    # relative to the oracle's deviation, with a small absolute floor for a candidate
+    # that (nearly) equals full attention on constructed inputs
+    bad = np.abs(err_g[:, 1:] - err_o[:, 1:]) > REL * err_o[:, 1:] + ATOL
+    rel = np.abs(err_g[:, 1:] - err_o[:, 1:]) / np.maximum(err_o[:, 1:], ATOL / REL)
+    assert not bad.any(), f"{what}: relative error {rel.max():.3e} > {REL} (+{ATOL} absolute)"
+    margins = []
     for h in range(err_g.shape[0]):
         assert route_g[h] == 1 + int(np.argmin(err_g[h, 1:]))
         e = np.sort(err_o[h, 1:])
-        if len(e) < 2 or e[1] - e[0] > 3 * REL * e[1]:
-            assert route_g[h] == route_o[h], (h, err_g[h], err_o[h])
+        margin = (e[1] - e[0]) / e[1] if len(e) > 1 and e[1] > 0 else 1.0
+        margins.append(margin)
+        # a route may legitimately differ only where the candidates are within 2*REL
+        assert route_g[h] == route_o[h] or margin <= 2 * REL, (h, err_g[h], err_o[h])
+    say(f"{what}: max relative error {rel.max():.2e}; routes equal on {int((route_g == route_o).sum())}/"
+        f"{len(route_g)} heads; smallest margin between the two best candidates {min(margins):.3f}")
 
 
 def _coded(g, H, D, by, alpha, seed):
@@ -52,7 +64,7 @@ def test_profiler_constructed_winner(gpu_lib, by, winner):
     torch.cuda.synchronize()
     assert torch.all(route.cpu() == winner)
     err_o, route_o = oracle.profile_heads(q, k, v, g, "frame", idx, cands)
-    _check(err, route, err_o, route_o)
+    _check(err, route, err_o, route_o, f"constructed {by}")
 
 
 @pytest.mark.parametrize("n,nc", [(16, 2), (20, 3), (32, 4), (64, 3), (100, 4), (128, 2), (200, 2), (256, 3)])
@@ -68,10 +80,11 @@ def test_profiler_iid_small(gpu_lib, n, nc):
                                            torch.from_numpy(idx).to(d), cands)
     torch.cuda.synchronize()
     err_o, route_o = oracle.profile_heads(q, k, v, g, "frame", idx, cands)
-    _check(err, route, err_o, route_o)
+    _check(err, route, err_o, route_o, f"iid n={n} n_cand={nc}")
 
 
 def test_profiler_full_config(gpu_lib):
+    """The routed stripe layer (B = 2, 40 heads, 64 samples per head): all 40 heads."""
     cfg = W.config("stripe_route")
     g = cfg["grid"]
     S = W.seq_len(g)
@@ -82,7 +95,5 @@ def test_profiler_full_config(gpu_lib):
     err, route = gpu_lib.vsa_profile_heads(q.to(d), k.to(d), v.to(d), g, "frame",
                                            torch.from_numpy(idx).to(d), cfg["candidates"])
     torch.cuda.synchronize()
-    heads = list(range(0, cfg["H"], 5))
-    err_o, route_o = oracle.profile_heads(q[:, :, heads], k[:, :, heads], v[:, :, heads], g, "frame",
-                                          idx[heads], cfg["candidates"])
-    _check(err[heads], route[heads], err_o, route_o)
+    err_o, route_o = oracle_pool.profile_heads(q, k, v, g, "frame", idx, cfg["candidates"], list(range(cfg["H"])))
+    _check(err, route, err_o, route_o, "stripe_route, 40 heads")
