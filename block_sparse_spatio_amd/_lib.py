@@ -77,6 +77,9 @@ _SIGNATURES = {
     "vsa_sparse_attn_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I,
                                     ctypes.POINTER(vsa_mask_desc), ctypes.POINTER(vsa_tile_lists), _I, _I,
                                     ctypes.c_float, _I, _P, _I, _P, ctypes.c_size_t, _P]),
+    "vsa_sparse_attn_fwd_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I,
+                                         ctypes.POINTER(vsa_mask_desc), ctypes.POINTER(vsa_tile_lists), _I, _I,
+                                         ctypes.c_float, _I, _P, _I, _P]),
     "vsa_boundary_words": (_I, [ctypes.POINTER(vsa_grid), _I, ctypes.POINTER(vsa_mask_desc), _I, _I, _I,
                                 ctypes.POINTER(vsa_tile_lists), _P, _I, _P]),
     "vsa_reorder_tokens": (_I, [_P, _P, _I, _I, _I, _I, ctypes.POINTER(vsa_grid), _I, _P]),
@@ -327,6 +330,30 @@ def vsa_sparse_attn_fwd(q, k, v, grid, layout, masks, tiles, scale=0.0, flags=0,
             _layout(layout), make_masks(masks), ctypes.byref(st), tiles["Bq"], tiles["Bk"], float(scale),
             flags, _ptr(w), words["cap"], _ptr(workspace), ws_bytes, _stream(stream, q.device)))
     return o, (lse if flags & VSA_FWD_WRITE_LSE else None)
+
+
+def vsa_sparse_attn_fwd_noalloc(q, k, v, grid, layout, masks, tiles, o, lse=None, scale=0.0, flags=0, words=None,
+                                stream=None):
+    """The forward with its workspace in the library's static per-GPU scratch
+    (vsa_sparse_attn_fwd_noalloc): the caller passes every output buffer (o, and lse with
+    VSA_FWD_WRITE_LSE), and nothing is allocated on either side of the call."""
+    for t in (q, k, v, o):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v and o must be contiguous [B, S, H, D]")
+    B, S, H, D = q.shape
+    for t in (k, v, o):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v and o must have one shape and dtype")
+    if (flags & VSA_FWD_WRITE_LSE) and (lse is None or tuple(lse.shape) != (B, H, S)
+                                        or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError(f"VSA_FWD_WRITE_LSE needs lse, a contiguous float32 tensor of shape {(B, H, S)}")
+    w, cap = (None, 0) if words is None else (words["words"], words["cap"])
+    st = _lists_struct(tiles)
+    _check(load().vsa_sparse_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype(q), B, S, H, D, ctypes.byref(make_grid(grid)),
+        _layout(layout), make_masks(masks), ctypes.byref(st), tiles["Bq"], tiles["Bk"], float(scale), flags,
+        _ptr(w), cap, _stream(stream, q.device)))
+    return o, lse
 
 
 def vsa_merge_partials(o_parts, lse_parts, o=None, lse=None, stream=None):

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "vsa_internal.h"
@@ -34,6 +35,7 @@ vsa_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr long long kMaxS = 1LL << 30;
+constexpr int kMaxDevices = 64;
 
 long long ceil_to(long long a, long long b) { return (a + b - 1) / b * b; }
 
@@ -391,11 +393,45 @@ vsa_status vsa_sparse_attn_fwd(const void* q, const void* k, const void* v, void
                                 nullptr, 0, workspace, ws_bytes, stream);
 }
 
-vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, vsa_dtype dtype,
-                                  int32_t B, int32_t S, int32_t H, int32_t D, const vsa_grid* grid, vsa_layout layout,
-                                  const vsa_mask_desc* masks, const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk,
-                                  float scale, int32_t flags, const uint32_t* words, int32_t words_cap,
-                                  void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// Scratch of vsa_sparse_attn_fwd_noalloc: a file-scope device array, one copy per GPU,
+// which holds what the forward's workspace holds (V^T per 64-key block, the reordered k
+// with VSA_FWD_REORDER_IO, the per-call schedule).  In host code `scratch` only names
+// the symbol; its device address on each GPU comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is ever passed on.
+static __device__ __align__(256) char scratch[VSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kScratchBytes = VSA_NOALLOC_SCRATCH_BYTES;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The calling thread's current device's copy of `scratch`.
+vsa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(VSA_ERR_UNSUPPORTED, "device %d above %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VSA_OK;
+}
+
+// The forward behind vsa_sparse_attn_fwd(_ex) and vsa_sparse_attn_fwd_noalloc: every
+// check first, then (use_scratch) the static scratch in place of a workspace argument.
+vsa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, vsa_dtype dtype, int32_t B,
+                    int32_t S, int32_t H, int32_t D, const vsa_grid* grid, vsa_layout layout,
+                    const vsa_mask_desc* masks, const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk, float scale,
+                    int32_t flags, const uint32_t* words, int32_t words_cap, void* workspace, size_t ws_bytes,
+                    bool use_scratch, void* stream) {
   long long S_grid;
   vsa_status st = check_grid(grid, layout, masks && H > 0 && H <= VSA_MAX_HEADS && needs_tile(masks, H), &S_grid);
   if (st != VSA_OK) return st;
@@ -459,10 +495,16 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   if (reorder && !any_permuted)
     return fail(VSA_ERR_INVALID_ARG, "VSA_FWD_REORDER_IO needs a head whose layout is not frame-major");
   const size_t need = fwd_ws_bytes(B, (int32_t)S_exec, H, D, dtype, flags);
-  if (need && (!workspace || ws_bytes < need))
-    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
-  if (need && ((uintptr_t)workspace & 15))
-    return fail(VSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (use_scratch) {
+    if (need > kScratchBytes)
+      return fail(VSA_ERR_WORKSPACE, "the call needs %zu bytes of scratch; the static scratch holds %zu", need,
+                  kScratchBytes);
+  } else {
+    if (need && (!workspace || ws_bytes < need))
+      return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    if (need && ((uintptr_t)workspace & 15))
+      return fail(VSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
 
   vsa::FwdArgs a;
   memset(&a, 0, sizeof a);
@@ -485,6 +527,10 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
   a.words_cap = words ? words_cap : 0;
   a.bnd_offs = tiles->bnd_offs;
   if (words_cap > a.nK) return fail(VSA_ERR_INVALID_ARG, "words_cap=%d above the %d key tiles", words_cap, a.nK);
+  if (use_scratch && need) {  // every argument is valid: the first HIP call may be made
+    st = scratch_of_current_device(&workspace);
+    if (st != VSA_OK) return st;
+  }
   hipStream_t hs = (hipStream_t)stream;
   const vsa::Geom& G = a.g;
   char* ws = (char*)workspace;
@@ -530,6 +576,28 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
     if (e != hipSuccess) return hip_fail(e, "inverse reorder o");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, vsa_dtype dtype,
+                                  int32_t B, int32_t S, int32_t H, int32_t D, const vsa_grid* grid, vsa_layout layout,
+                                  const vsa_mask_desc* masks, const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk,
+                                  float scale, int32_t flags, const uint32_t* words, int32_t words_cap,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  return fwd_impl(q, k, v, o, lse, dtype, B, S, H, D, grid, layout, masks, tiles, Bq, Bk, scale, flags, words,
+                  words_cap, workspace, ws_bytes, false, stream);
+}
+
+vsa_status vsa_sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                       vsa_dtype dtype, int32_t B, int32_t S, int32_t H, int32_t D,
+                                       const vsa_grid* grid, vsa_layout layout, const vsa_mask_desc* masks,
+                                       const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk, float scale,
+                                       int32_t flags, const uint32_t* words, int32_t words_cap, void* stream) {
+  return fwd_impl(q, k, v, o, lse, dtype, B, S, H, D, grid, layout, masks, tiles, Bq, Bk, scale, flags, words,
+                  words_cap, nullptr, 0, true, stream);
 }
 
 vsa_status vsa_merge_partials(const void* const* o_parts, const float* const* lse_parts, int32_t n_parts, void* o,

@@ -316,6 +316,30 @@ vsa_status vsa_sparse_attn_fwd_ex(const void* q, const void* k, const void* v, v
                                   int32_t words_cap, void* workspace, size_t ws_bytes,
                                   void* stream);
 
+/* Allocation-free forward ------------------------------------------------------ */
+
+/* For callers that cannot allocate device memory at call time: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same forward as
+ * vsa_sparse_attn_fwd_ex (same arguments without the workspace, same kernels, same
+ * output bit for bit), with its workspace taken from a scratch array that the library
+ * holds on each GPU it runs on, VSA_NOALLOC_SCRATCH_BYTES bytes, from the first call on
+ * that GPU (the calling thread's current device, which must own `stream`) until the
+ * process ends.  The call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  A call whose workspace (vsa_fwd_workspace_bytes) exceeds the scratch returns
+ * VSA_ERR_WORKSPACE and enqueues nothing; for bf16 that is B*H*D*S64*2 bytes (plus the
+ * reordered k with VSA_FWD_REORDER_IO), e.g. 10 heads of 75,600 tokens at D = 128.  Every
+ * call on one GPU shares that GPU's scratch and overwrites it completely (nothing in it
+ * needs to start at zero), so calls that overlap on one GPU, on concurrent streams or
+ * threads, race: serialise them.  Errors as for vsa_sparse_attn_fwd_ex. */
+#define VSA_NOALLOC_SCRATCH_BYTES (256u << 20)
+vsa_status vsa_sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, vsa_dtype dtype, int32_t B, int32_t S,
+                                       int32_t H, int32_t D, const vsa_grid* grid,
+                                       vsa_layout layout, const vsa_mask_desc* masks,
+                                       const vsa_tile_lists* tiles, int32_t Bq, int32_t Bk,
+                                       float scale, int32_t flags, const uint32_t* words,
+                                       int32_t words_cap, void* stream);
+
 /* Token reorder ---------------------------------------------------------------- */
 
 /* Permute the sequence axis of src [B][S][H][D] into dst (no aliasing), each head h

@@ -154,6 +154,22 @@ def test_fwd_size_limits_enqueue_nothing():
     assert st == -2 and "2^31" in msg, msg
 
 
+def test_noalloc_rejects_oversized_call():
+    """The allocation-free forward refuses a call whose workspace exceeds the static
+    scratch before anything is enqueued (the pointers are not device memory), and
+    validates its arguments like the forward with a workspace."""
+    lib = vsa.load()
+    g = W.grid(21, 45, 80)  # 40 heads of 128 channels: V^T alone is 774 MB
+    masks = _lib.make_masks([W.mask_spatial(1)] * 40)
+    lists = _lib.vsa_tile_lists(0x5000, 0x6000, 0x7000, 0x8000, 0x9000, None)
+    call = lambda **o: lib.vsa_sparse_attn_fwd_noalloc(  # noqa: E731
+        0x1000, 0x2000, 0x3000, o.get("o", 0x4000), None, vsa.VSA_BF16, 1, 75600, 40, o.get("D", 128),
+        ctypes.byref(_lib.make_grid(g)), 0, masks, ctypes.byref(lists), 128, 64, 0.0, 0, None, 0, None)
+    assert call() == -3 and "static scratch" in vsa.vsa_last_error()
+    assert call(o=0x1000) == -1 and "alias" in vsa.vsa_last_error()
+    assert call(D=96) == -2
+
+
 def test_tile_lists_bytes_and_carve():
     """One allocation for every array of the tile lists: sizes and 256-byte aligned
     offsets in struct order, bnd_offs with U*nQ + 1 entries."""
