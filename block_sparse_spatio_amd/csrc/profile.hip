@@ -5,16 +5,20 @@
 // head is routed to the candidate with the smallest deviation ("supporting dynamic
 // routing with fixed tensor shapes": one flag per head, no variable-size head groups).
 //
+// Pass 0 (profile_words_kernel): the element masks of the sampled rows under every
+// candidate that keeps a strict subset of the keys, one 32-bit word per (row, key tile,
+// half-wave) in the bit order of the score registers, shared by all batch items.
 // Pass 1 (profile_part_kernel): one workgroup per (sample group, key chunk, b, h), with
 // one group of waves per candidate.  Each wave holds 32 sampled query rows of (b, h) in
 // registers and runs the attention pipeline of the bf16 forward kernel over the chunk's
-// key tiles: K and V tiles reach LDS by DMA (issued by the first 2, 4 or 8 waves),
-// double-buffered and shared by every candidate, S^T = K Q^T on the matrix cores
-// overlaps the softmax of the previous tile, and the wave's candidate mask applies to
-// every tile (the all-keep reference only at the sequence tail).  V stays row-major and
-// is read with transposing LDS reads.  The chunk's unnormalised output, running max and
-// row sum go to the workspace.  At most 8 waves per workgroup (two per SIMD); the
-// sample groups of one (chunk, b, h) are adjacent on one XCD.
+// key tiles: K and V tiles (and the tile's mask words) reach LDS by DMA (issued by the
+// first 2, 4 or 8 waves) through a ring of kStages tiles, shared by every candidate;
+// S^T = K Q^T on the matrix cores overlaps the softmax of the previous tile, and the
+// wave's candidate mask applies to every tile (the all-keep reference only at the
+// sequence tail).  V stays row-major and is read with transposing LDS reads.  The
+// chunk's unnormalised output, running max and row sum go to the workspace.  At most 8
+// waves per workgroup (two per SIMD); the sample groups of one (chunk, b, h) are
+// adjacent on one XCD.
 // Pass 2 (profile_merge_kernel, profile_route_kernel): groups of 16 samples merge their
 // chunk partials with the softmax statistics (lanes over channels) into sums of
 // (o_c - o_0)^2; per head these are added in a fixed order, err[h][c] = sqrt(.) and
@@ -35,6 +39,37 @@ constexpr int kProfRow = D + 4;
 // waves that issue a workgroup's K/V DMAs: the largest power of two up to its waves
 constexpr int dma_waves(int nw) { return nw >= 8 ? 8 : (nw >= 4 ? 4 : 2); }
 
+// K and V ring depth in key tiles: with one workgroup per compute unit, four stages
+// (128 KB of LDS at D = 128) keep three tiles loading while one is computed on.
+constexpr int kStages = 4;
+
+// Score register (kb, i) of S^T holds key kb*32 + (i>>3)*16 + 8*g2 + (i&7) of the tile
+// for the lanes of half-wave g2: the 32 bits of a 64-key row mask that half-wave g2
+// needs, with bit kb*16 + i for register (kb, i).
+__device__ __forceinline__ uint32_t reg_order_word(uint64_t bits, int g2) {
+  const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
+  return ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) | (((hi >> (8 * g2)) & 0xffu) << 16) |
+         (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
+}
+
+// Pass 0: thread (x = kt * n_pad + sample slot, y = h * n_masked + table index) writes the
+// two half-wave words of that sampled row's mask over key tile kt.  Slots past the
+// samples repeat the last sample.
+__global__ __launch_bounds__(256) void profile_words_kernel(ProfArgs a, MaskTable cands) {
+  const int nK = (a.S + BK - 1) / BK;
+  const int cmi = blockIdx.y % a.n_masked;
+  const int h = blockIdx.y / a.n_masked;
+  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (x >= (long long)nK * a.n_pad) return;
+  const int kt = (int)(x / a.n_pad);
+  const int si = (int)(x % a.n_pad);
+  const DevMask m = cands.m[a.cand_of[cmi]];
+  const int qrow = imin(imax(a.sample_idx[(size_t)h * a.n + imin(si, a.n - 1)], 0), a.S - 1);
+  const uint64_t bits = tile_row_mask(a.g, m, make_query(a.g, m, qrow), kt * BK, BK);
+  const size_t t = (((size_t)h * nK + kt) * a.n_masked + cmi) * a.n_pad + si;
+  *(u32x2*)(a.words + 2 * t) = u32x2{reg_order_word(bits, 0), reg_order_word(bits, 1)};
+}
+
 template <int D, int NWS, int NC>
 __global__ __launch_bounds__(NWS * NC * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void profile_part_kernel(ProfArgs a, MaskTable cands) {
@@ -45,10 +80,11 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   constexpr int KSTEPS = C::KSTEPS;
   constexpr int DB = C::DB;
   constexpr int NI = C::NI;
-  __shared__ __attribute__((aligned(1024))) char kbuf0[C::TILE_B];
-  __shared__ __attribute__((aligned(1024))) char kbuf1[C::TILE_B];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[C::TILE_B];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[C::TILE_B];
+  constexpr int NS = kStages;
+  constexpr int ND = (NC * SG * 8 + 1023) / 1024;  // 1 KB DMAs for one tile's mask words
+  __shared__ __attribute__((aligned(1024))) char kring[NS * C::TILE_B];
+  __shared__ __attribute__((aligned(1024))) char vring[NS * C::TILE_B];
+  __shared__ __attribute__((aligned(1024))) char wring[NS * ND * 1024];
 
   const Geom& g = a.g;
   const int S = a.S, H = a.H, n = a.n;
@@ -91,7 +127,19 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + s * 16));
   }
-  const QueryPos qpos = make_query(g, m, qrow);
+  const int cm = a.cm[c];  // this candidate's rows in the word table, -1 for keep-all
+  // wave 0 DMAs each tile's mask words: the workgroup's block is [table index][SG][2]
+  // u32; 16 bytes per lane, lanes past the table read its first word (unused)
+  const bool wdma = wv == 0 && a.n_masked > 0;
+  const size_t wtile = (size_t)a.n_masked * a.n_pad * 8;  // bytes of one tile's words
+  const char* wsrc = (const char*)a.words + (size_t)h * nK * wtile;
+  uint32_t woff[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    const int byte = d * 1024 + lane * 16;
+    const int t = byte / (SG * 8);
+    woff[d] = t < a.n_masked ? (uint32_t)(t * a.n_pad * 8 + sg * SG * 8 + byte % (SG * 8)) : 0u;
+  }
 
   // DMA: K row R of LDS holds key swap_bits23(R) (chunks swizzled by ksw), V row R holds
   // key R (chunks swizzled by vsw for the transposing reads)
@@ -167,12 +215,18 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[ks], s[kb], 0, 0, 0);
       }
   };
-  // register (kb, i) of S^T holds key kb*32 + (i>>3)*16 + 8*g2 + (i&7) of the tile
-  auto mask_word = [&](int kt) __attribute__((always_inline)) -> uint32_t {
-    const uint64_t bits = tile_row_mask(g, m, qpos, kt * BK, BK);
-    const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
-    return ((lo >> (8 * g2)) & 0xffu) | (((lo >> (16 + 8 * g2)) & 0xffu) << 8) |
-           (((hi >> (8 * g2)) & 0xffu) << 16) | (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
+  // this lane's mask word of the chunk tile in word stage st (table candidates)
+  auto lds_word = [&](int st) __attribute__((always_inline)) -> uint32_t {
+    return *(const uint32_t*)(wring + st * ND * 1024 + ((cm * SG + (wv % NWS) * 32 + l32) * 2 + g2) * 4);
+  };
+  // keep-all candidates: only the keys past the sequence end are masked
+  auto tail_word = [&](int kt) __attribute__((always_inline)) -> uint32_t {
+    const int valid = S - kt * BK;
+    if (valid >= BK) return ~0u;
+    return reg_order_word(valid <= 0 ? 0ull : (1ull << valid) - 1, g2);
+  };
+  auto word = [&](int it) __attribute__((always_inline)) -> uint32_t {
+    return cm >= 0 ? lds_word(it % NS) : tail_word(kt_begin + it);
   };
   auto masked = [](float x, uint32_t w, int v) __attribute__((always_inline)) {
     const uint32_t f = (uint32_t)((int32_t)(w << (31 - v)) >> 31);
@@ -187,28 +241,52 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   const float lazy = kLazyLog2 / c_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   f32x16 s_cur[2];
-  int kt0 = 0, kt1 = 0, kt2 = 0;
 
   // the all-keep reference needs the element mask only on the tile that holds the
   // sequence tail
   const bool need_mask = m.kind != VSA_MASK_ALL || (kt_begin + n_tiles) * BK > S;
 
-  // One step per key tile (as in the forward kernel): entering step it, S(it) is
-  // masked in registers with its row max, K(it+1) and V(it) are in LDS.
+  // DMA batch j (j = 0, 1, ...) loads K of chunk tile j into K stage j % NS and V of
+  // chunk tile j - 1 into V stage (j - 1) % NS; the prologue issues batches 0 .. NS-1 and
+  // step it issues batch it + NS.  Entering step it, S(it) is masked in registers with
+  // its row max, and step it needs batch it + 1 (K(it+1) for the next scores, V(it) for
+  // the product): the stages it overwrites held K(it) and V(it-1), read in step it-1,
+  // which every wave has left at the barrier.
+  auto issue_batch = [&](int j) __attribute__((always_inline)) {
+    if (j < n_tiles) {
+      issue(kt_begin + j, kring + (j % NS) * C::TILE_B, false);
+      if (wdma) {
+        const char* src = wsrc + (size_t)(kt_begin + j) * wtile;
+        const uint32_t dst = lds_addr(wring + (j % NS) * ND * 1024);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dma16(src, woff[d], dst + d * 1024);
+      }
+    }
+    if (j >= 1 && j - 1 < n_tiles) issue(kt_begin + j - 1, vring + ((j - 1) % NS) * C::TILE_B, true);
+  };
+  // wait until batch j has landed: while every batch after it up to j + later is whole
+  // (2 NI DMAs per wave, and ND more for wave 0's mask words), the later batches may
+  // stay in flight, else wait for all
+  auto wait_batch = [&](int j, auto later_tag) __attribute__((always_inline)) {
+    constexpr int L = decltype(later_tag)::value;
+    if (j + L >= n_tiles)
+      wait_vmcnt<0>();
+    else if (wdma)
+      wait_vmcnt<L * (2 * NI + ND)>();
+    else
+      wait_vmcnt<L * 2 * NI>();
+  };
+
   auto run = [&](auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(mask_tag)::value;
-    auto step = [&](auto par_tag, int it) __attribute__((always_inline)) {
-      constexpr int P = decltype(par_tag)::value;
-      char* k_use = P == 0 ? kbuf1 : kbuf0;
-      char* k_fill = P == 0 ? kbuf0 : kbuf1;
-      char* v_use = P == 0 ? vbuf0 : vbuf1;
-      char* v_fill = P == 0 ? vbuf1 : vbuf0;
-      wait_vmcnt<0>();
+    auto step = [&](int it) __attribute__((always_inline)) {
+      const char* k_use = kring + ((it + 1) % NS) * C::TILE_B;
+      const char* v_use = vring + (it % NS) * C::TILE_B;
+      wait_batch(it + 1, std::integral_constant<int, NS - 2>{});
       barrier_lds();
-      if (it + 2 < n_tiles) issue(kt2, k_fill, false);
-      if (it + 1 < n_tiles) issue(kt1, v_fill, true);
+      issue_batch(it + NS);
       uint32_t w_next = ~0u;
-      if (MASKED && it + 1 < n_tiles) w_next = mask_word(kt1);
+      if (MASKED && it + 1 < n_tiles) w_next = word(it + 1);
 
       const bool grow = mt_cur > m_run + lazy;
       if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -222,7 +300,7 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
       const float mc = (m_run == -INFINITY) ? 0.f : m_run * c_log2;
 
       // S(it+1) on the matrix cores with the probabilities of S(it) (the product on the
-      // last tile reads a stale buffer and is discarded)
+      // last tile reads a stale stage and is discarded)
       f32x16 s_next[2];
       qk(k_use, s_next);
       bf16x2 pk[16];
@@ -266,25 +344,16 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
       mt_cur = pair_max(mx);
       s_cur[0] = s_next[0];
       s_cur[1] = s_next[1];
-      kt0 = kt1;
-      kt1 = kt2;
-      kt2 = it + 3 < n_tiles ? kt_begin + it + 3 : 0;
     };
 
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
     wait_vmcnt<0>();  // query fragments before the first DMA
     if (n_tiles > 0) {
-      kt0 = kt_begin;
-      kt1 = n_tiles > 1 ? kt_begin + 1 : 0;
-      kt2 = n_tiles > 2 ? kt_begin + 2 : 0;
-      issue(kt0, kbuf0, false);
-      wait_vmcnt<0>();
+#pragma unroll
+      for (int j = 0; j < NS; ++j) issue_batch(j);
+      wait_batch(0, std::integral_constant<int, NS - 1>{});
       barrier_lds();
-      if (n_tiles > 1) issue(kt1, kbuf1, false);
-      issue(kt0, vbuf0, true);
-      qk(kbuf0, s_cur);
-      const uint32_t w = MASKED ? mask_word(kt0) : ~0u;
+      qk(kring, s_cur);
+      const uint32_t w = MASKED ? word(0) : ~0u;
       float mx = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 32; ++v) {
@@ -297,12 +366,7 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
       }
       mt_cur = pair_max(mx);
     }
-    int it = 0;
-    for (; it + 1 < n_tiles; it += 2) {
-      step(P0{}, it);
-      step(P1{}, it + 1);
-    }
-    if (it < n_tiles) step(P0{}, it);
+    for (int it = 0; it < n_tiles; ++it) step(it);
     wait_vmcnt<0>();
   };
   if (need_mask)
@@ -434,10 +498,16 @@ hipError_t launch_t(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
   const int n_sg = (a.n + NWS * 32 - 1) / (NWS * 32);
   const long long blocks = ((units + 7) / 8) * 8 * n_sg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipError_t e;
+  if (a.n_masked > 0) {
+    const long long wblocks = ((long long)((a.S + BK - 1) / BK) * a.n_pad + 255) / 256;
+    if (wblocks > 0x7fffffffLL || (long long)a.H * a.n_masked > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(profile_words_kernel, dim3((unsigned)wblocks, a.H * a.n_masked), dim3(256), 0, st, a, cands);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((profile_part_kernel<D, NWS, NC>), dim3((unsigned)blocks), dim3(NWS * NC * 64), 0, st, a,
                      cands);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int G = (a.n + kMergeSamples - 1) / kMergeSamples;
   hipLaunchKernelGGL((profile_merge_kernel<D, NC>), dim3(a.H, a.B, G), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -475,14 +545,17 @@ int32_t profile_sample_waves(int32_t n, int32_t n_cand) {
 }
 
 // Key chunks per (b, h): the count that minimises rounds of resident workgroups times
-// key tiles per chunk (fewest chunks on ties), with 256 compute units holding one
-// workgroup of more than 4 waves or two smaller ones (LDS and registers), and at most
-// 8192 workgroups.
-int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t n, int32_t n_cand) {
+// key tiles per chunk (fewest chunks on ties), with each of the 256 compute units holding
+// as many workgroups as its LDS (160 KB against the K and V rings) and its waves (two per
+// SIMD) allow, and at most 8192 workgroups.
+int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand) {
   const int nK = (S + pipe::BK - 1) / pipe::BK;
   const int nws = profile_sample_waves(n, n_cand);
   const long long per_chunk = (long long)B * H * ((n + nws * 32 - 1) / (nws * 32));
-  const long long slots = 256LL * (nws * n_cand > 4 ? 1 : 2);
+  const int lds = 2 * kStages * pipe::BK * D * 2;
+  const int by_lds = (160 * 1024) / lds;
+  const int by_waves = 8 / (nws * n_cand);
+  const long long slots = 256LL * imax(1, imin(by_lds, by_waves));
   const long long lim = 8192 / (per_chunk > 0 ? per_chunk : 1);
   const long long c_max = lim < 1 ? 1 : (lim < nK ? lim : nK);
   int best = 1;
@@ -497,10 +570,24 @@ int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t n, int32_t n_can
   return best;
 }
 
-size_t profile_ws_floats(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand,
-                         int32_t n_chunks) {
+int32_t profile_pad_samples(int32_t n, int32_t n_cand) {
+  const int sg = 32 * profile_sample_waves(n, n_cand);
+  return (n + sg - 1) / sg * sg;
+}
+
+// Workspace: the chunk partials, the merge sums, then (at a 256-byte boundary) the mask
+// word table, sized for every candidate having one.
+size_t profile_words_offset(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand, int32_t n_chunks) {
   const size_t groups = (size_t)(n + kMergeSamples - 1) / kMergeSamples;
-  return (size_t)B * H * n_chunks * n_cand * n * (D + 4) + (size_t)H * B * groups * n_cand;
+  const size_t f = (size_t)B * H * n_chunks * n_cand * n * (D + 4) + (size_t)H * B * groups * n_cand;
+  return (f + 63) / 64 * 64;
+}
+
+size_t profile_ws_floats(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand,
+                         int32_t n_chunks) {
+  const size_t nK = ((size_t)S + pipe::BK - 1) / pipe::BK;
+  return profile_words_offset(B, H, D, n, n_cand, n_chunks) +
+         (size_t)H * nK * n_cand * profile_pad_samples(n, n_cand) * 2;
 }
 
 hipError_t launch_profile(const ProfArgs& a, const MaskTable& cands, hipStream_t stream) {

@@ -162,6 +162,13 @@ struct ProfArgs {
   float scale;
   int32_t is_bf16;
   Geom g;
+  // element-mask words of the sampled rows under the candidates that keep a strict
+  // subset of the keys (in the workspace): u32 [H][nK][n_masked][n_pad][2]
+  uint32_t* words;
+  int32_t n_masked;    // candidates with a word table
+  int32_t n_pad;       // samples rounded up to whole sample groups
+  int32_t cm[4];       // candidate -> its index in the table, -1 for keep-all candidates
+  int32_t cand_of[4];  // table index -> candidate
 };
 struct MergeArgs {
   const void* o[16];
@@ -172,10 +179,12 @@ struct MergeArgs {
 };
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
-size_t profile_ws_floats(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand,
+size_t profile_ws_floats(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand,
                          int32_t n_chunks);
+size_t profile_words_offset(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand, int32_t n_chunks);
+int32_t profile_pad_samples(int32_t n, int32_t n_cand);
 int32_t profile_sample_waves(int32_t n, int32_t n_cand);
-int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t n, int32_t n_cand);
+int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand);
 hipError_t launch_profile(const ProfArgs& a, const MaskTable& cands, hipStream_t stream);
 
 }  // namespace vsa

@@ -97,3 +97,34 @@ def test_profiler_full_config(gpu_lib):
     torch.cuda.synchronize()
     err_o, route_o = oracle_pool.profile_heads(q, k, v, g, "frame", idx, cfg["candidates"], list(range(cfg["H"])))
     _check(err, route, err_o, route_o, "stripe_route, 40 heads")
+
+
+@pytest.mark.parametrize("layout,n,cands", [
+    ("tile", 40, "box_stripe_sta"),
+    ("position", 64, "box_stripe"),
+    ("frame", 96, "all_all"),
+    ("tile", 33, "all_sta_all"),
+])
+def test_profiler_layouts_and_tables(gpu_lib, layout, n, cands):
+    """Tile- and position-major calls (the mask words of the sampled rows follow the
+    call's order), a ragged sample count, and candidate sets with no masked candidate
+    or keep-all candidates between masked ones."""
+    tile = (2, 3, 4)
+    g = W.grid(6, 9, 16, tile) if layout == "tile" else W.grid(5, 9, 15)
+    S = W.seq_len(g)
+    sets = {
+        "box_stripe_sta": [W.mask_all(), W.mask_box(1, 2, 3), W.mask_stripe(1, 0, 2, 3, 1, 7), W.mask_sta(1, 2, 2)],
+        "box_stripe": [W.mask_all(), W.mask_box(2, -1, 4, sink_frames=1), W.mask_stripe(2, 1, 3, 2, 0, 5)],
+        "all_all": [W.mask_all(), W.mask_all()],
+        "all_sta_all": [W.mask_all(), W.mask_sta(1, 1, 2), W.mask_all()],
+    }
+    cs = sets[cands]
+    q, k, v = W.qkv(2, S, 3, 128, "bf16", seed=7 + n)
+    idx = W.sample_rows(S, n, 3, n + 11)
+    d = dev()
+    say(f"profiler layout={layout} n={n} candidates={cands}")
+    err, route = gpu_lib.vsa_profile_heads(q.to(d), k.to(d), v.to(d), g, layout,
+                                           torch.from_numpy(idx).to(d), cs)
+    torch.cuda.synchronize()
+    err_o, route_o = oracle.profile_heads(q, k, v, g, layout, idx, cs)
+    _check(err, route, err_o, route_o, f"{layout} n={n} {cands}")
