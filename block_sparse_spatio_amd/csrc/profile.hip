@@ -19,8 +19,8 @@
 // chunk's unnormalised output, running max and row sum go to the workspace.  At most 8
 // waves per workgroup (two per SIMD); the sample groups of one (chunk, b, h) are
 // adjacent on one XCD.
-// Pass 2 (profile_merge_kernel, profile_route_kernel): groups of 16 samples merge their
-// chunk partials with the softmax statistics (lanes over channels) into sums of
+// Pass 2 (profile_merge_kernel, profile_route_kernel): each sampled row merges its chunk
+// partials with the softmax statistics (lanes over channels) into sums of
 // (o_c - o_0)^2; per head these are added in a fixed order, err[h][c] = sqrt(.) and
 // route[h] = argmin over c >= 1 (lowest c on ties).
 #include "lds_pipe.h"
@@ -392,104 +392,102 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   }
 }
 
-// Samples per merge workgroup (4 waves, 4 samples each)
-constexpr int kMergeSamples = 16;
-
 __host__ __device__ inline size_t part_floats(const ProfArgs& a) {
   return (size_t)a.B * a.H * a.n_chunks * a.n_cand * a.n * (a.D + 4);
 }
 
-// Pass 2a: workgroup (h, b, g) merges the chunk partials of samples g*16 .. g*16+15 of
-// (b, h) (wave w: samples g*16 + 4w + k; lane l: channels l + 64 t) with a single-pass
-// online max, and writes sum over its samples and channels of (o_c - o_0)^2.
+// Pass 2a: one wave per (b, h, sample) merges that row's chunk partials of every
+// candidate with the softmax statistics (the largest chunk max first, then each chunk
+// weighted by exp of its max against it; lanes over channels, D/64 adjacent channels
+// per lane) and writes sum over channels of (o_c - o_0)^2 for c >= 1 to
+// sums[h][b][sample][c].
 template <int D, int NC>
 __global__ __launch_bounds__(256) void profile_merge_kernel(ProfArgs a) {
-  constexpr int DT = D / 64;
-  const int h = blockIdx.x, b = blockIdx.y, grp = blockIdx.z;
-  const int n = a.n, H = a.H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int DL = D / 64;
+  typedef float fvec __attribute__((ext_vector_type(DL)));
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n = a.n, H = a.H, nch = a.n_chunks;
+  if (row >= (long long)a.B * H * n) return;
+  const int si = (int)(row % n);
+  const int bh = (int)(row / n);
+  const int h = bh % H, b = bh / H;
   const float c_log2 = a.scale * 1.4426950408889634f;
-  const size_t row = kProfRow<D>;
-  const size_t ch_stride = (size_t)NC * n * row;
-  float part[NC];
+  constexpr size_t RW = kProfRow<D>;
+  const size_t ch_stride = (size_t)NC * n * RW;
+  const float* base = a.ws + (size_t)bh * nch * ch_stride + (size_t)si * RW;
+  fvec o[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) part[c] = 0.f;
-  for (int k = 0; k < kMergeSamples / 4; ++k) {
-    const int si = grp * kMergeSamples + wave * (kMergeSamples / 4) + k;
-    if (si >= n) break;
-    const float* base = a.ws + ((size_t)(b * H + h) * a.n_chunks) * ch_stride + (size_t)si * row;
-    float o[NC][DT];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float* pc = base + (size_t)c * n * row;
-      float mu = -INFINITY, l = 0.f, x[DT];
-#pragma unroll
-      for (int t = 0; t < DT; ++t) x[t] = 0.f;
-      for (int ch = 0; ch < a.n_chunks; ++ch) {
+  for (int c = 0; c < NC; ++c) {
+    const float* pc = base + (size_t)c * n * RW;
+    float mu = -INFINITY;
+    for (int ch = 0; ch < nch; ++ch) mu = fmaxf(mu, pc[ch * ch_stride + D]);
+    float l = 0.f;
+    fvec x = {};
+    if (mu != -INFINITY) {  // uniform: some chunk kept a key
+#pragma unroll 4
+      for (int ch = 0; ch < nch; ++ch) {
         const float* p = pc + ch * ch_stride;
         const float m = p[D];
-        if (m == -INFINITY) continue;  // chunk without a kept key (uniform)
-        const float nmu = fmaxf(mu, m);
-        const float so = mu == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mu - nmu) * c_log2);
-        const float w = __builtin_amdgcn_exp2f((m - nmu) * c_log2);
-        l = l * so + p[D + 1] * w;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) x[t] = x[t] * so + p[lane + 64 * t] * w;
-        mu = nmu;
+        const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mu) * c_log2);
+        l = fmaf(p[D + 1], w, l);
+        x += *(const fvec*)(p + lane * DL) * w;
       }
-      const float linv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) o[c][t] = x[t] * linv;
     }
-#pragma unroll
-    for (int c = 1; c < NC; ++c)
-#pragma unroll
-      for (int t = 0; t < DT; ++t) part[c] += (o[c][t] - o[0][t]) * (o[c][t] - o[0][t]);
+    o[c] = x * (l > 0.f ? 1.f / l : 0.f);
   }
-  __shared__ float red[NC][4];
+  float* dst = a.ws + part_floats(a) + (((size_t)h * a.B + b) * n + si) * NC;
 #pragma unroll
   for (int c = 1; c < NC; ++c) {
-    float v = part[c];
+    const fvec e = o[c] - o[0];
+    float v = 0.f;
+#pragma unroll
+    for (int t = 0; t < DL; ++t) v = fmaf(e[t], e[t], v);
 #pragma unroll
     for (int s = 32; s > 0; s >>= 1) v += __shfl_xor(v, s);
-    if (lane == 0) red[c][wave] = v;
+    if (lane == 0) dst[c] = v;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int G = gridDim.z;
-    float* dst = a.ws + part_floats(a) + (((size_t)h * a.B + b) * G + grp) * NC;
-    dst[0] = 0.f;
-#pragma unroll
-    for (int c = 1; c < NC; ++c) dst[c] = ((red[c][0] + red[c][1]) + red[c][2]) + red[c][3];
-  }
+  if (lane == 0) dst[0] = 0.f;
 }
 
-// Pass 2b: per head, the merge sums in a fixed order, err = sqrt(.), route = argmin
-// over c >= 1 (lowest c on ties).
+// Pass 2b: one workgroup per head adds its B * n row sums in a fixed order (thread t
+// takes rows t, t + 256, ..., then a fixed pairwise tree), err = sqrt(.), route =
+// argmin over c >= 1 (lowest c on ties).
 template <int NC>
-__global__ __launch_bounds__(64) void profile_route_kernel(ProfArgs a, int G) {
-  const int h = blockIdx.x * 64 + threadIdx.x;
-  if (h >= a.H) return;
-  const float* src = a.ws + part_floats(a) + (size_t)h * a.B * G * NC;
-  float tot[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) tot[c] = 0.f;
-  for (int e = 0; e < a.B * G; ++e)
-#pragma unroll
-    for (int c = 1; c < NC; ++c) tot[c] += src[(size_t)e * NC + c];
-  int best = 1;
-  float best_e = 0.f;
-  a.err[(size_t)h * NC + 0] = 0.f;
+__global__ __launch_bounds__(256) void profile_route_kernel(ProfArgs a) {
+  const int h = blockIdx.x;
+  const int t = threadIdx.x;
+  const long long rows = (long long)a.B * a.n;
+  const float* src = a.ws + part_floats(a) + (size_t)h * rows * NC;
+  __shared__ float red[NC][256];
 #pragma unroll
   for (int c = 1; c < NC; ++c) {
-    const float e = sqrtf(tot[c]);
-    a.err[(size_t)h * NC + c] = e;
-    if (c == 1 || e < best_e) {
-      best_e = e;
-      best = c;
-    }
+    float v = 0.f;
+    for (long long r = t; r < rows; r += 256) v += src[r * NC + c];
+    red[c][t] = v;
   }
-  a.route[h] = best;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w)
+#pragma unroll
+      for (int c = 1; c < NC; ++c) red[c][t] += red[c][t + w];
+    __syncthreads();
+  }
+  if (t == 0) {
+    int best = 1;
+    float best_e = 0.f;
+    a.err[(size_t)h * NC + 0] = 0.f;
+#pragma unroll
+    for (int c = 1; c < NC; ++c) {
+      const float e = sqrtf(red[c][0]);
+      a.err[(size_t)h * NC + c] = e;
+      if (c == 1 || e < best_e) {
+        best_e = e;
+        best = c;
+      }
+    }
+    a.route[h] = best;
+  }
 }
 
 template <int D, int NWS, int NC>
@@ -508,10 +506,11 @@ hipError_t launch_t(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
   hipLaunchKernelGGL((profile_part_kernel<D, NWS, NC>), dim3((unsigned)blocks), dim3(NWS * NC * 64), 0, st, a,
                      cands);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int G = (a.n + kMergeSamples - 1) / kMergeSamples;
-  hipLaunchKernelGGL((profile_merge_kernel<D, NC>), dim3(a.H, a.B, G), dim3(256), 0, st, a);
+  const long long mrows = (long long)a.B * a.H * a.n;
+  if ((mrows + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((profile_merge_kernel<D, NC>), dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((profile_route_kernel<NC>), dim3((a.H + 63) / 64), dim3(64), 0, st, a, G);
+  hipLaunchKernelGGL((profile_route_kernel<NC>), dim3(a.H), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -578,8 +577,7 @@ int32_t profile_pad_samples(int32_t n, int32_t n_cand) {
 // Workspace: the chunk partials, the merge sums, then (at a 256-byte boundary) the mask
 // word table, sized for every candidate having one.
 size_t profile_words_offset(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand, int32_t n_chunks) {
-  const size_t groups = (size_t)(n + kMergeSamples - 1) / kMergeSamples;
-  const size_t f = (size_t)B * H * n_chunks * n_cand * n * (D + 4) + (size_t)H * B * groups * n_cand;
+  const size_t f = (size_t)B * H * n_chunks * n_cand * n * (D + 4) + (size_t)H * B * n * n_cand;
   return (f + 63) / 64 * 64;
 }
 
