@@ -8,14 +8,14 @@
 // Pass 0 (profile_words_kernel): the element masks of the sampled rows under every
 // candidate that keeps a strict subset of the keys, one 32-bit word per (row, key tile,
 // half-wave) in the bit order of the score registers, shared by all batch items.
-// Pass 1 (profile_part_kernel): one workgroup per (sample group, key chunk, b, h), with
-// one group of waves per candidate.  Each wave holds 32 sampled query rows of (b, h) in
-// registers and runs the attention pipeline of the bf16 forward kernel over the chunk's
-// key tiles: K and V tiles (and the tile's mask words) reach LDS by DMA (issued by the
-// first 2, 4 or 8 waves) through a ring of kStages tiles, shared by every candidate;
-// S^T = K Q^T on the matrix cores overlaps the softmax of the previous tile, and the
-// wave's candidate mask applies to every tile (the all-keep reference only at the
-// sequence tail).  V stays row-major and is read with transposing LDS reads.  The
+// Pass 1 (profile_part_kernel): one workgroup per (sample group, key chunk, b, h).  Its
+// score waves hold 32 sampled query rows of (b, h) each and compute S^T = K Q^T for every
+// key tile of the chunk once, into LDS; one softmax wave per (candidate, 32 rows) takes
+// those scores under its candidate's mask (the all-keep reference only at the sequence
+// tail) through the online softmax and O^T += V^T P^T on the matrix cores, so the scores
+// are not recomputed per candidate and every SIMD carries the same matrix work per tile.
+// K and V tiles (and the tile's mask words) reach LDS by DMA through a ring of stages
+// shared by all waves; V stays row-major and is read with transposing LDS reads.  The
 // chunk's unnormalised output, running max and row sum go to the workspace.  At most 8
 // waves per workgroup (two per SIMD); the sample groups of one (chunk, b, h) are
 // adjacent on one XCD.
@@ -31,6 +31,14 @@ namespace {
 
 using namespace pipe;
 
+// LDS-typed pointers: arithmetic on them stays in 32-bit LDS addresses, so a read at a
+// run-time stage is one base register plus the instruction's immediate offset
+typedef __attribute__((address_space(3))) char lchar;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 l_f32x4;
+typedef __attribute__((address_space(3))) u32x4 l_u32x4;
+typedef __attribute__((address_space(3))) uint32_t l_u32;
+
 // one partial row of the workspace: D unnormalised outputs, the running max (raw score
 // units) and the row sum, padded to a multiple of 16 bytes
 template <int D>
@@ -39,9 +47,16 @@ constexpr int kProfRow = D + 4;
 // waves that issue a workgroup's K/V DMAs: the largest power of two up to its waves
 constexpr int dma_waves(int nw) { return nw >= 8 ? 8 : (nw >= 4 ? 4 : 2); }
 
-// K and V ring depth in key tiles: with one workgroup per compute unit, four stages
-// (128 KB of LDS at D = 128) keep three tiles loading while one is computed on.
-constexpr int kStages = 4;
+// LDS of a pass-1 workgroup with NS ring stages: the K and V rings, NS stages of mask
+// words (1 KB DMAs) and two 64 x 32 fp32 score blocks per sample wave.
+constexpr int prof_word_dmas(int nws, int nc) { return (nc * nws * 32 * 8 + 1023) / 1024; }
+constexpr int prof_lds(int d, int nws, int nc, int ns) {
+  return 2 * ns * pipe::BK * d * 2 + ns * prof_word_dmas(nws, nc) * 1024 + 2 * nws * 8192;
+}
+// Ring depth in key tiles: the deepest of 4, 3, 2 stages whose LDS fits in 160 KB.
+constexpr int prof_stages(int d, int nws, int nc) {
+  return prof_lds(d, nws, nc, 4) <= 160 * 1024 ? 4 : (prof_lds(d, nws, nc, 3) <= 160 * 1024 ? 3 : 2);
+}
 
 // Score register (kb, i) of S^T holds key kb*32 + (i>>3)*16 + 8*g2 + (i&7) of the tile
 // for the lanes of half-wave g2: the 32 bits of a 64-key row mask that half-wave g2
@@ -71,20 +86,26 @@ __global__ __launch_bounds__(256) void profile_words_kernel(ProfArgs a, MaskTabl
 }
 
 template <int D, int NWS, int NC>
-__global__ __launch_bounds__(NWS * NC * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(NWS * (NC + 1) * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void profile_part_kernel(ProfArgs a, MaskTable cands) {
-  constexpr int NWT = NWS * NC;  // NWS waves of 32 samples per candidate
-  constexpr int SG = NWS * 32;   // samples per workgroup
+  constexpr int NWT = NWS * (NC + 1);  // NWS score waves, then NWS waves per candidate
+  constexpr int SG = NWS * 32;         // samples per workgroup
   constexpr int NWD = dma_waves(NWT);
   using C = Cfg<D, NWD>;
   constexpr int KSTEPS = C::KSTEPS;
   constexpr int DB = C::DB;
   constexpr int NI = C::NI;
-  constexpr int NS = kStages;
-  constexpr int ND = (NC * SG * 8 + 1023) / 1024;  // 1 KB DMAs for one tile's mask words
+  constexpr int NS = prof_stages(D, NWS, NC);
+  constexpr int ND = prof_word_dmas(NWS, NC);  // 1 KB DMAs for one tile's mask words
+  constexpr int SB = 32 * 64 * 4;                  // one 64 x 32 score block, fp32
   __shared__ __attribute__((aligned(1024))) char kring[NS * C::TILE_B];
   __shared__ __attribute__((aligned(1024))) char vring[NS * C::TILE_B];
   __shared__ __attribute__((aligned(1024))) char wring[NS * ND * 1024];
+  __shared__ __attribute__((aligned(1024))) char sring[2 * NWS * SB];
+  lchar* const KL = (lchar*)kring;
+  lchar* const VL = (lchar*)vring;
+  lchar* const WL = (lchar*)wring;
+  lchar* const SL = (lchar*)sring;
 
   const Geom& g = a.g;
   const int S = a.S, H = a.H, n = a.n;
@@ -106,13 +127,15 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = wv / NWS;                    // this wave's candidate
-  const bool dma_wave = wv < dma_waves(NWT);
-  const int wave = dma_wave ? wv : 0;        // DMA slot (unused by the other waves)
+  const bool scorer = wv < NWS;
+  const int sw = scorer ? wv : (wv - NWS) % NWS;  // sample wave: 32 of the group's rows
+  const int c = scorer ? 0 : (wv - NWS) / NWS;    // candidate of a softmax wave
+  const bool dma_wave = wv < NWD;
+  const int wave = dma_wave ? wv : 0;  // DMA slot (unused by the other waves)
   const DevMask m = cands.m[c];
   const int g2 = lane >> 5;
   const int l32 = lane & 31;
-  const int si = sg * SG + (wv % NWS) * 32 + l32;  // sample slot of this lane's query row
+  const int si = sg * SG + sw * 32 + l32;  // sample slot of this lane's query row
   const int qrow = imin(imax(a.sample_idx[(size_t)h * n + imin(si, n - 1)], 0), S - 1);
 
   const uint16_t* qp = (const uint16_t*)a.q;
@@ -122,12 +145,12 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   const size_t base_bh = ((size_t)b * S) * tok_stride + (size_t)h * D;
 
   bf16x8 qf[KSTEPS];
-  {
+  if (scorer) {
     const uint16_t* src = qp + base_bh + (size_t)qrow * tok_stride + g2 * 8;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + s * 16));
   }
-  const int cm = a.cm[c];  // this candidate's rows in the word table, -1 for keep-all
+  const int cm = scorer ? -1 : a.cm[c];  // the candidate's rows in the word table, -1 for keep-all
   // wave 0 DMAs each tile's mask words: the workgroup's block is [table index][SG][2]
   // u32; 16 bytes per lane, lanes past the table read its first word (unused)
   const bool wdma = wv == 0 && a.n_masked > 0;
@@ -204,20 +227,32 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
       for (int i = 0; i < NI; ++i) dma16(src, 2 * dma_off(i, is_v, S - 1 - c0), lds0 + i * 1024);
     }
   };
-  auto qk = [&](const char* kb_, f32x16* s) __attribute__((always_inline)) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+  // score wave: S^T = K Q^T of the tile in K stage st for its 32 rows, stored to score
+  // buffer sb as 8 float4 per lane (float4 q of lane l at (q*64 + l)*16: conflict-free)
+  auto score = [&](int st, int sb) __attribute__((always_inline)) {
+    const lchar* kb_ = KL + st * C::TILE_B;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 kf = *(const u32x4*)(kb_ + kb * 32 * C::ROWB + kofs[ks]);
+        const u32x4 kf = *(const l_u32x4*)(kb_ + kb * 32 * C::ROWB + kofs[ks]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[ks], s[kb], 0, 0, 0);
       }
+    lchar* dst = SL + (sb * NWS + sw) * SB + lane * 16;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      *(l_f32x4*)(dst + q * 1024) = f32x4{s[q >> 2][(q & 3) * 4 + 0], s[q >> 2][(q & 3) * 4 + 1],
+                                          s[q >> 2][(q & 3) * 4 + 2], s[q >> 2][(q & 3) * 4 + 3]};
+  };
+  // register (kb, i) of S^T holds key kb*32 + (i>>3)*16 + 8*g2 + (i&7) of the tile
+  auto masked = [](float x, uint32_t w, int v) __attribute__((always_inline)) {
+    const uint32_t f = (uint32_t)((int32_t)(w << (31 - v)) >> 31);
+    return __uint_as_float((__float_as_uint(x) & f) | (0xff800000u & ~f));
   };
   // this lane's mask word of the chunk tile in word stage st (table candidates)
   auto lds_word = [&](int st) __attribute__((always_inline)) -> uint32_t {
-    return *(const uint32_t*)(wring + st * ND * 1024 + ((cm * SG + (wv % NWS) * 32 + l32) * 2 + g2) * 4);
+    return *(const l_u32*)(WL + st * ND * 1024 + ((cm * SG + sw * 32 + l32) * 2 + g2) * 4);
   };
   // keep-all candidates: only the keys past the sequence end are masked
   auto tail_word = [&](int kt) __attribute__((always_inline)) -> uint32_t {
@@ -228,30 +263,27 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   auto word = [&](int it) __attribute__((always_inline)) -> uint32_t {
     return cm >= 0 ? lds_word(it % NS) : tail_word(kt_begin + it);
   };
-  auto masked = [](float x, uint32_t w, int v) __attribute__((always_inline)) {
-    const uint32_t f = (uint32_t)((int32_t)(w << (31 - v)) >> 31);
-    return __uint_as_float((__float_as_uint(x) & f) | (0xff800000u & ~f));
-  };
 
   f32x16 acc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f, mt_cur = -INFINITY;
+  float m_run = -INFINITY, l_run = 0.f;
   const float c_log2 = a.scale * 1.4426950408889634f;
   const float lazy = kLazyLog2 / c_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  f32x16 s_cur[2];
 
   // the all-keep reference needs the element mask only on the tile that holds the
   // sequence tail
-  const bool need_mask = m.kind != VSA_MASK_ALL || (kt_begin + n_tiles) * BK > S;
+  const bool need_mask = !scorer && (m.kind != VSA_MASK_ALL || (kt_begin + n_tiles) * BK > S);
 
-  // DMA batch j (j = 0, 1, ...) loads K of chunk tile j into K stage j % NS and V of
-  // chunk tile j - 1 into V stage (j - 1) % NS; the prologue issues batches 0 .. NS-1 and
-  // step it issues batch it + NS.  Entering step it, S(it) is masked in registers with
-  // its row max, and step it needs batch it + 1 (K(it+1) for the next scores, V(it) for
-  // the product): the stages it overwrites held K(it) and V(it-1), read in step it-1,
-  // which every wave has left at the barrier.
+  // DMA batch j (j = 0, 1, ...) loads K of chunk tile j into K stage j % NS (with the
+  // tile's mask words into word stage j % NS) and V of chunk tile j - 1 into V stage
+  // (j - 1) % NS; the prologue issues batches 0 .. NS-1 and step it issues batch it + NS.
+  // Step it needs batch it + 1: the score waves turn K(it+1) into S(it+1) (score buffer
+  // (it+1) & 1) while the softmax waves take S(it) (written in the step before) with
+  // V(it) and read the mask words of tile it+1 for the next step.  The stages a batch
+  // overwrites were last read in the step before it is issued, and a score buffer is
+  // rewritten two steps after it was filled, both past a barrier.
   auto issue_batch = [&](int j) __attribute__((always_inline)) {
     if (j < n_tiles) {
       issue(kt_begin + j, kring + (j % NS) * C::TILE_B, false);
@@ -265,8 +297,8 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
     if (j >= 1 && j - 1 < n_tiles) issue(kt_begin + j - 1, vring + ((j - 1) % NS) * C::TILE_B, true);
   };
   // wait until batch j has landed: while every batch after it up to j + later is whole
-  // (2 NI DMAs per wave, and ND more for wave 0's mask words), the later batches may
-  // stay in flight, else wait for all
+  // (2 NI DMAs per DMA wave, and ND more for wave 0's mask words), the later batches
+  // may stay in flight, else wait for all
   auto wait_batch = [&](int j, auto later_tag) __attribute__((always_inline)) {
     constexpr int L = decltype(later_tag)::value;
     if (j + L >= n_tiles)
@@ -277,102 +309,113 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
       wait_vmcnt<L * 2 * NI>();
   };
 
-  auto run = [&](auto mask_tag) __attribute__((always_inline)) {
+  // softmax wave, step it: S(it) from score buffer it & 1 under mask word w, the
+  // online softmax, and O^T += V(it)^T P(it)^T
+  auto softmax_pv = [&](auto mask_tag, int it, uint32_t w) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(mask_tag)::value;
-    auto step = [&](int it) __attribute__((always_inline)) {
-      const char* k_use = kring + ((it + 1) % NS) * C::TILE_B;
-      const char* v_use = vring + (it % NS) * C::TILE_B;
+    f32x16 s[2];
+    const lchar* src = SL + ((it & 1) * NWS + sw) * SB + lane * 16;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 x = *(const l_f32x4*)(src + q * 1024);
+      s[q >> 2][(q & 3) * 4 + 0] = x.x;
+      s[q >> 2][(q & 3) * 4 + 1] = x.y;
+      s[q >> 2][(q & 3) * 4 + 2] = x.z;
+      s[q >> 2][(q & 3) * 4 + 3] = x.w;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 32; ++v) {
+      float x = s[v >> 4][v & 15];
+      if constexpr (MASKED) {
+        x = masked(x, w, v);
+        s[v >> 4][v & 15] = x;
+      }
+      mx = __builtin_elementwise_maximum(mx, x);
+    }
+    const float mt = pair_max(mx);
+    const bool grow = mt > m_run + lazy;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c_log2) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c_log2;
+    bf16x2 pk[16];
+#pragma unroll
+    for (int v = 0; v < 32; v += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[v >> 4][v & 15], c_log2, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[v >> 4][(v & 15) + 1], c_log2, -mc));
+      pk[v >> 1] = pack_bf16x2(p0, p1);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[v >> 1], ones, l_run, false);
+    }
+    // the stage's byte offset as one scalar, so that each read is its lane's base plus
+    // an immediate offset (the compiler otherwise spreads the ring index arithmetic
+    // over one register per read)
+    const lchar* v_use = VL + __builtin_amdgcn_readfirstlane((it % NS) * C::TILE_B);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 pf = __builtin_bit_cast(
+          bf16x8, u32x4{__builtin_bit_cast(uint32_t, pk[4 * j + 0]), __builtin_bit_cast(uint32_t, pk[4 * j + 1]),
+                        __builtin_bit_cast(uint32_t, pk[4 * j + 2]), __builtin_bit_cast(uint32_t, pk[4 * j + 3])});
+      i16x4 v0[DB], v1[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const lchar* base = v_use + vofs[db] + j * 16 * C::ROWB;
+        v0[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+        v1[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * C::ROWB));
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x8 vv = __builtin_shufflevector(v0[db], v1[db], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // Every wave passes the same barriers: one after the prologue's DMAs, one per step.
+  // The two roles run their own loops so that the score waves' query fragments and the
+  // softmax waves' accumulators are never live together.
+  auto steps = [&](auto&& body) __attribute__((always_inline)) {
+    for (int it = 0; it < n_tiles; ++it) {
       wait_batch(it + 1, std::integral_constant<int, NS - 2>{});
       barrier_lds();
       issue_batch(it + NS);
-      uint32_t w_next = ~0u;
-      if (MASKED && it + 1 < n_tiles) w_next = word(it + 1);
-
-      const bool grow = mt_cur > m_run + lazy;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mt_cur : m_run;
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c_log2) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-        m_run = m_new;
-      }
-      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c_log2;
-
-      // S(it+1) on the matrix cores with the probabilities of S(it) (the product on the
-      // last tile reads a stale stage and is discarded)
-      f32x16 s_next[2];
-      qk(k_use, s_next);
-      bf16x2 pk[16];
-#pragma unroll
-      for (int v = 0; v < 32; v += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][v & 15], c_log2, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][(v & 15) + 1], c_log2, -mc));
-        pk[v >> 1] = pack_bf16x2(p0, p1);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[v >> 1], ones, l_run, false);
-      }
-      // O^T += V(it)^T P(it)^T
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 pf = __builtin_bit_cast(
-            bf16x8, u32x4{__builtin_bit_cast(uint32_t, pk[4 * j + 0]), __builtin_bit_cast(uint32_t, pk[4 * j + 1]),
-                          __builtin_bit_cast(uint32_t, pk[4 * j + 2]), __builtin_bit_cast(uint32_t, pk[4 * j + 3])});
-        i16x4 v0[DB], v1[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const char* base = v_use + vofs[db] + j * 16 * C::ROWB;
-          v0[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-          v1[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * C::ROWB));
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const i16x8 vv = __builtin_shufflevector(v0[db], v1[db], 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
-        }
-      }
-      // mask and row max of S(it+1)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 32; ++v) {
-        float x = s_next[v >> 4][v & 15];
-        if constexpr (MASKED) {
-          x = masked(x, w_next, v);
-          s_next[v >> 4][v & 15] = x;
-        }
-        mx = __builtin_elementwise_maximum(mx, x);
-      }
-      mt_cur = pair_max(mx);
-      s_cur[0] = s_next[0];
-      s_cur[1] = s_next[1];
-    };
-
-    wait_vmcnt<0>();  // query fragments before the first DMA
-    if (n_tiles > 0) {
-#pragma unroll
-      for (int j = 0; j < NS; ++j) issue_batch(j);
-      wait_batch(0, std::integral_constant<int, NS - 1>{});
-      barrier_lds();
-      qk(kring, s_cur);
-      const uint32_t w = MASKED ? word(0) : ~0u;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 32; ++v) {
-        float x = s_cur[v >> 4][v & 15];
-        if constexpr (MASKED) {
-          x = masked(x, w, v);
-          s_cur[v >> 4][v & 15] = x;
-        }
-        mx = __builtin_elementwise_maximum(mx, x);
-      }
-      mt_cur = pair_max(mx);
+      body(it);
     }
-    for (int it = 0; it < n_tiles; ++it) step(it);
-    wait_vmcnt<0>();
   };
-  if (need_mask)
-    run(std::integral_constant<bool, true>{});
-  else
-    run(std::integral_constant<bool, false>{});
+  auto softmax_steps = [&](auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(mask_tag)::value;
+    uint32_t w = MASKED ? word(0) : ~0u;
+    steps([&](int it) __attribute__((always_inline)) {
+      const uint32_t w_next = MASKED && it + 1 < n_tiles ? word(it + 1) : ~0u;
+      softmax_pv(mask_tag, it, w);
+      w = w_next;
+    });
+  };
+
+  wait_vmcnt<0>();  // query fragments before the first DMA
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) issue_batch(j);
+    wait_batch(0, std::integral_constant<int, NS - 1>{});
+    barrier_lds();
+    if (scorer) {
+      score(0, 0);
+      steps([&](int it) __attribute__((always_inline)) {
+        if (it + 1 < n_tiles) score((it + 1) % NS, (it + 1) & 1);
+      });
+    } else if (need_mask) {
+      softmax_steps(std::integral_constant<bool, true>{});
+    } else {
+      softmax_steps(std::integral_constant<bool, false>{});
+    }
+  }
+  wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it ends
+  if (scorer) return;
 
   const float l_tot = pair_sum(l_run);
   if (si < n) {
@@ -503,7 +546,7 @@ hipError_t launch_t(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
     hipLaunchKernelGGL(profile_words_kernel, dim3((unsigned)wblocks, a.H * a.n_masked), dim3(256), 0, st, a, cands);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((profile_part_kernel<D, NWS, NC>), dim3((unsigned)blocks), dim3(NWS * NC * 64), 0, st, a,
+  hipLaunchKernelGGL((profile_part_kernel<D, NWS, NC>), dim3((unsigned)blocks), dim3(NWS * (NC + 1) * 64), 0, st, a,
                      cands);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long mrows = (long long)a.B * a.H * a.n;
@@ -518,10 +561,10 @@ template <int D, int NC>
 hipError_t launch_nw(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
   switch (profile_sample_waves(a.n, NC)) {
     case 1: return launch_t<D, 1, NC>(a, cands, st);
-    case 2: return launch_t<D, 2, NC>(a, cands, st);
-    default:
-      if constexpr (NC == 2) return launch_t<D, 4, NC>(a, cands, st);
+    case 2:
+      if constexpr (NC <= 3) return launch_t<D, 2, NC>(a, cands, st);
       return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -538,9 +581,8 @@ hipError_t launch_nc(const ProfArgs& a, const MaskTable& cands, hipStream_t st) 
 }  // namespace
 
 int32_t profile_sample_waves(int32_t n, int32_t n_cand) {
-  const int cap = n_cand <= 2 ? 4 : 2;  // at most 8 waves per workgroup
-  const int need = (n + 31) / 32;
-  return need <= 1 ? 1 : (need <= 2 || cap == 2 ? 2 : 4);
+  const int cap = n_cand <= 3 ? 2 : 1;  // (n_cand + 1) * waves <= 8 per workgroup
+  return n <= 32 ? 1 : cap;
 }
 
 // Key chunks per (b, h): the count that minimises rounds of resident workgroups times
@@ -551,9 +593,9 @@ int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, in
   const int nK = (S + pipe::BK - 1) / pipe::BK;
   const int nws = profile_sample_waves(n, n_cand);
   const long long per_chunk = (long long)B * H * ((n + nws * 32 - 1) / (nws * 32));
-  const int lds = 2 * kStages * pipe::BK * D * 2;
+  const int lds = prof_lds(D, nws, n_cand, prof_stages(D, nws, n_cand));
   const int by_lds = (160 * 1024) / lds;
-  const int by_waves = 8 / (nws * n_cand);
+  const int by_waves = 8 / (nws * (n_cand + 1));
   const long long slots = 256LL * imax(1, imin(by_lds, by_waves));
   const long long lim = 8192 / (per_chunk > 0 ? per_chunk : 1);
   const long long c_max = lim < 1 ? 1 : (lim < nK ? lim : nK);
