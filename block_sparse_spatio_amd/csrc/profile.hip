@@ -67,22 +67,28 @@ __device__ __forceinline__ uint32_t reg_order_word(uint64_t bits, int g2) {
          (((hi >> (16 + 8 * g2)) & 0xffu) << 24);
 }
 
-// Pass 0: thread (x = kt * n_pad + sample slot, y = h * n_masked + table index) writes the
-// two half-wave words of that sampled row's mask over key tile kt.  Slots past the
-// samples repeat the last sample.
-__global__ __launch_bounds__(256) void profile_words_kernel(ProfArgs a, MaskTable cands) {
+// Pass 0: one wave per (kWordTiles key tiles, h, table index); lane l takes sample slots
+// l, l + 64, ... and writes the two half-wave words of each slot's mask over every tile of
+// the group (the key tile is the same for the whole wave, so the walk over its runs is
+// scalar work).  Slots past the samples repeat the last sample.
+constexpr int kWordTiles = 8;
+
+__global__ __launch_bounds__(64) void profile_words_kernel(ProfArgs a, MaskTable cands) {
   const int nK = (a.S + BK - 1) / BK;
   const int cmi = blockIdx.y % a.n_masked;
   const int h = blockIdx.y / a.n_masked;
-  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (x >= (long long)nK * a.n_pad) return;
-  const int kt = (int)(x / a.n_pad);
-  const int si = (int)(x % a.n_pad);
+  const int kt0 = blockIdx.x * kWordTiles;
+  const int kt1 = imin(kt0 + kWordTiles, nK);
   const DevMask m = cands.m[a.cand_of[cmi]];
-  const int qrow = imin(imax(a.sample_idx[(size_t)h * a.n + imin(si, a.n - 1)], 0), a.S - 1);
-  const uint64_t bits = tile_row_mask(a.g, m, make_query(a.g, m, qrow), kt * BK, BK);
-  const size_t t = (((size_t)h * nK + kt) * a.n_masked + cmi) * a.n_pad + si;
-  *(u32x2*)(a.words + 2 * t) = u32x2{reg_order_word(bits, 0), reg_order_word(bits, 1)};
+  for (int si = threadIdx.x; si < a.n_pad; si += 64) {
+    const int qrow = imin(imax(a.sample_idx[(size_t)h * a.n + imin(si, a.n - 1)], 0), a.S - 1);
+    const QueryPos qp = make_query(a.g, m, qrow);
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const uint64_t bits = tile_row_mask(a.g, m, qp, kt * BK, BK);
+      const size_t t = (((size_t)h * nK + kt) * a.n_masked + cmi) * a.n_pad + si;
+      *(u32x2*)(a.words + 2 * t) = u32x2{reg_order_word(bits, 0), reg_order_word(bits, 1)};
+    }
+  }
 }
 
 template <int D, int NWS, int NC>
@@ -440,9 +446,10 @@ __host__ __device__ inline size_t part_floats(const ProfArgs& a) {
 }
 
 // Pass 2a: one wave per (b, h, sample) merges that row's chunk partials of every
-// candidate with the softmax statistics (the largest chunk max first, then each chunk
-// weighted by exp of its max against it; lanes over channels, D/64 adjacent channels
-// per lane) and writes sum over channels of (o_c - o_0)^2 for c >= 1 to
+// candidate with the softmax statistics: lane ch reads chunk ch's max and row sum (64
+// chunks per round), the wave takes the largest max, and each chunk's output row
+// (lanes over channels, D/64 adjacent channels per lane) is added with weight exp of
+// its max against that one.  Writes sum over channels of (o_c - o_0)^2 for c >= 1 to
 // sums[h][b][sample][c].
 template <int D, int NC>
 __global__ __launch_bounds__(256) void profile_merge_kernel(ProfArgs a) {
@@ -464,18 +471,27 @@ __global__ __launch_bounds__(256) void profile_merge_kernel(ProfArgs a) {
   for (int c = 0; c < NC; ++c) {
     const float* pc = base + (size_t)c * n * RW;
     float mu = -INFINITY;
-    for (int ch = 0; ch < nch; ++ch) mu = fmaxf(mu, pc[ch * ch_stride + D]);
+    for (int c0 = 0; c0 < nch; c0 += 64)
+      if (c0 + lane < nch) mu = fmaxf(mu, pc[(c0 + lane) * ch_stride + D]);
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) mu = fmaxf(mu, __shfl_xor(mu, s));
     float l = 0.f;
     fvec x = {};
     if (mu != -INFINITY) {  // uniform: some chunk kept a key
-#pragma unroll 4
-      for (int ch = 0; ch < nch; ++ch) {
-        const float* p = pc + ch * ch_stride;
-        const float m = p[D];
+      for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int ch = c0 + lane;
+        const float m = ch < nch ? pc[ch * ch_stride + D] : -INFINITY;
         const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mu) * c_log2);
-        l = fmaf(p[D + 1], w, l);
-        x += *(const fvec*)(p + lane * DL) * w;
+        if (ch < nch) l = fmaf(pc[ch * ch_stride + D + 1], w, l);
+        const int cnt = imin(64, nch - c0);
+#pragma unroll 8
+        for (int j = 0; j < cnt; ++j) {
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+          x += *(const fvec*)(pc + (c0 + j) * ch_stride + lane * DL) * wj;
+        }
       }
+#pragma unroll
+      for (int s = 32; s > 0; s >>= 1) l += __shfl_xor(l, s);
     }
     o[c] = x * (l > 0.f ? 1.f / l : 0.f);
   }
@@ -541,9 +557,9 @@ hipError_t launch_t(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipError_t e;
   if (a.n_masked > 0) {
-    const long long wblocks = ((long long)((a.S + BK - 1) / BK) * a.n_pad + 255) / 256;
-    if (wblocks > 0x7fffffffLL || (long long)a.H * a.n_masked > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(profile_words_kernel, dim3((unsigned)wblocks, a.H * a.n_masked), dim3(256), 0, st, a, cands);
+    const int wblocks = ((a.S + BK - 1) / BK + kWordTiles - 1) / kWordTiles;
+    if ((long long)a.H * a.n_masked > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(profile_words_kernel, dim3(wblocks, a.H * a.n_masked), dim3(64), 0, st, a, cands);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL((profile_part_kernel<D, NWS, NC>), dim3((unsigned)blocks), dim3(NWS * (NC + 1) * 64), 0, st, a,

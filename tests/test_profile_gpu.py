@@ -128,3 +128,20 @@ def test_profiler_layouts_and_tables(gpu_lib, layout, n, cands):
     torch.cuda.synchronize()
     err_o, route_o = oracle.profile_heads(q, k, v, g, layout, idx, cs)
     _check(err, route, err_o, route_o, f"{layout} n={n} {cands}")
+
+
+def test_profiler_many_chunks(gpu_lib):
+    """One (b, h) over 120 key tiles: the keys split into one chunk per tile, more chunk
+    partials per row than a wave has lanes, so the merge takes them in two rounds."""
+    g = W.grid(10, 24, 32)
+    S = W.seq_len(g)
+    q, k, v = W.qkv(1, S, 1, 128, "bf16", seed=21)
+    idx = W.sample_rows(S, 24, 1, 22)
+    cands = [W.mask_all(), W.mask_spatial(1), W.mask_temporal(3)]
+    d = dev()
+    say("profiler many chunks")
+    err, route = gpu_lib.vsa_profile_heads(q.to(d), k.to(d), v.to(d), g, "frame",
+                                           torch.from_numpy(idx).to(d), cands)
+    torch.cuda.synchronize()
+    err_o, route_o = oracle.profile_heads(q, k, v, g, "frame", idx, cands)
+    _check(err, route, err_o, route_o, "many chunks")
