@@ -163,15 +163,16 @@ def cpu_baseline(cfg, q, k, v, tiles, head_map, budget_s=12.0):
 
 
 # ---------------------------------------------------------------------------
-def traffic_from_profiles(khash, n_launch_units):
+def traffic_from_profiles(khash, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, when it was
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and on this workload in its default run; else
+    None."""
     path = os.path.join(ROOT, "profiles", "attn_bf16_wan_mixed_traffic.json")
-    if not os.path.exists(path):
+    if workload is None or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_hash") != khash:
+    if rec.get("kernel_hash") != khash or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -427,7 +428,11 @@ def main():
     del pa, pb, la, lb, mo, ml
 
     khash = kernel_hash()
-    traffic = traffic_from_profiles(khash, 1)
+    # the counters were taken on the workload's default run (its Bq, flags, orders and
+    # the precomputed mask words)
+    default_run = (args.Bq is None and args.flags == 0 and not args.round_tiles and args.temporal_layout == "frame"
+                   and args.head_layouts == "workload" and not args.no_mask_words)
+    traffic = traffic_from_profiles(khash, args.config if default_run else None)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
