@@ -145,3 +145,20 @@ def test_profiler_many_chunks(gpu_lib):
     torch.cuda.synchronize()
     err_o, route_o = oracle.profile_heads(q, k, v, g, "frame", idx, cands)
     _check(err, route, err_o, route_o, "many chunks")
+
+
+@pytest.mark.parametrize("n,nc", [(24, 2), (64, 3), (90, 4)])
+def test_profiler_d64(gpu_lib, n, nc):
+    """Head dim 64: the other instances of the score / softmax kernel (four ring stages)."""
+    g = W.grid(5, 10, 14)
+    S = W.seq_len(g)
+    q, k, v = W.qkv(2, S, 3, 64, "bf16", seed=40 + n)
+    idx = W.sample_rows(S, n, 3, 41 + n)
+    cands = [W.mask_all(), W.mask_spatial(1), W.mask_temporal(2), W.mask_box(1, 3, 3)][:nc]
+    d = dev()
+    say(f"profiler D=64 n={n} n_cand={nc}")
+    err, route = gpu_lib.vsa_profile_heads(q.to(d), k.to(d), v.to(d), g, "frame",
+                                           torch.from_numpy(idx).to(d), cands)
+    torch.cuda.synchronize()
+    err_o, route_o = oracle.profile_heads(q, k, v, g, "frame", idx, cands)
+    _check(err, route, err_o, route_o, f"D=64 n={n} n_cand={nc}")
