@@ -304,7 +304,8 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   };
   // wait until batch j has landed: while every batch after it up to j + later is whole
   // (2 NI DMAs per DMA wave, and ND more for wave 0's mask words), the later batches
-  // may stay in flight, else wait for all
+  // may stay in flight (vector-memory loads count down vmcnt in the order they were
+  // issued), else wait for all
   auto wait_batch = [&](int j, auto later_tag) __attribute__((always_inline)) {
     constexpr int L = decltype(later_tag)::value;
     if (j + L >= n_tiles)
