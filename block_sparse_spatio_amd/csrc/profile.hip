@@ -8,19 +8,23 @@
 // Pass 0 (profile_words_kernel): the element masks of the sampled rows under every
 // candidate that keeps a strict subset of the keys, one 32-bit word per (row, key tile,
 // half-wave) in the bit order of the score registers, shared by all batch items.
-// Pass 1 (profile_part_kernel): one workgroup per (sample group, key chunk, b, h).  Its
-// score waves hold 32 sampled query rows of (b, h) each and compute S^T = K Q^T for every
-// key tile of the chunk once, into LDS; one softmax wave per (candidate, 32 rows) takes
-// those scores under its candidate's mask (the all-keep reference only at the sequence
-// tail) through the online softmax and O^T += V^T P^T on the matrix cores, so the scores
-// are not recomputed per candidate and every SIMD carries the same matrix work per tile.
-// K and V tiles (and the tile's mask words) reach LDS by DMA through a ring of stages
-// shared by all waves; V stays row-major and is read with transposing LDS reads.  The
-// chunk's unnormalised output, running max and row sum go to the workspace.  At most 8
-// waves per workgroup (two per SIMD); the sample groups of one (chunk, b, h) are
-// adjacent on one XCD.
-// Pass 2 (profile_merge_kernel, profile_route_kernel): each sampled row merges its chunk
-// partials with the softmax statistics (lanes over channels) into sums of
+// Pass 1 (profile_part_kernel): a unit is (b, h, sample group); the key tiles of all
+// units, unit after unit, form one sequence that is cut into as many equal contiguous
+// ranges as workgroups can be resident at once, one range per workgroup.  A workgroup
+// runs the segments of its range (the part of each unit it covers, at most two or three)
+// one after the other.  Its score waves hold 32 sampled query rows each and compute
+// S^T = K Q^T for every key tile once, into LDS; one softmax wave per (candidate, 32
+// rows) takes those scores under its candidate's mask (the all-keep reference only at
+// the sequence tail) through the online softmax and O^T += V^T P^T on the matrix cores,
+// so the scores are not recomputed per candidate and every SIMD carries the same matrix
+// work per tile.  K and V tiles (and the tile's mask words) reach LDS by DMA through a
+// ring of stages shared by all waves; V stays row-major and is read with transposing LDS
+// reads.  Each segment's unnormalised output, running max and row sum go to the
+// workspace as the unit's partial slot (its index among the workgroups that cover the
+// unit).  The ranges keep every workgroup equally busy with few partial rows: writes
+// mixed into the K/V read stream slow it far more than their bytes.
+// Pass 2 (profile_merge_kernel, profile_route_kernel): each sampled row merges its
+// unit's partial slots with the softmax statistics (lanes over channels) into sums of
 // (o_c - o_0)^2; per head these are added in a fixed order, err[h][c] = sqrt(.) and
 // route[h] = argmin over c >= 1 (lowest c on ties).
 #include "lds_pipe.h"
@@ -56,6 +60,13 @@ constexpr int prof_lds(int d, int nws, int nc, int ns) {
 // Ring depth in key tiles: the deepest of 4, 3, 2 stages whose LDS fits in 160 KB.
 constexpr int prof_stages(int d, int nws, int nc) {
   return prof_lds(d, nws, nc, 4) <= 160 * 1024 ? 4 : (prof_lds(d, nws, nc, 3) <= 160 * 1024 ? 3 : 2);
+}
+
+// The tile sequence of all units cut into a.n_wg ranges: workgroup w takes tiles
+// [range_start(w), range_start(w + 1)); tile x lies in the range of workgroup range_of(x).
+__host__ __device__ inline int64_t range_start(const ProfArgs& a, int64_t w) { return w * a.total / a.n_wg; }
+__host__ __device__ inline int64_t range_of(const ProfArgs& a, int64_t x) {
+  return ((x + 1) * a.n_wg + a.total - 1) / a.total - 1;
 }
 
 // Score register (kb, i) of S^T holds key kb*32 + (i>>3)*16 + 8*g2 + (i&7) of the tile
@@ -115,20 +126,9 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
 
   const Geom& g = a.g;
   const int S = a.S, H = a.H, n = a.n;
-  const int n_sg = (n + SG - 1) / SG;
-  // workgroup -> (sample group, chunk, b, h): XCD x = blockIdx & 7 takes units u = j*8 + x
-  // of (chunk, b*H + h), each as n_sg consecutive workgroups
-  const int xcd = blockIdx.x & 7;
-  const int local = blockIdx.x >> 3;
-  const int sg = local % n_sg;
-  const int u = (local / n_sg) * 8 + xcd;
-  if (u >= a.n_chunks * a.B * H) return;
-  const int chunk = u % a.n_chunks;
-  const int bh = u / a.n_chunks;
-  const int h = bh % H, b = bh / H;
   const int nK = (S + BK - 1) / BK;
-  const int kt_begin = chunk * a.chunk_tiles;
-  const int n_tiles = imax(imin(nK, kt_begin + a.chunk_tiles) - kt_begin, 0);
+  const int64_t lo = range_start(a, blockIdx.x), hi = range_start(a, blockIdx.x + 1);
+  if (lo >= hi) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,34 +141,24 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   const DevMask m = cands.m[c];
   const int g2 = lane >> 5;
   const int l32 = lane & 31;
-  const int si = sg * SG + sw * 32 + l32;  // sample slot of this lane's query row
-  const int qrow = imin(imax(a.sample_idx[(size_t)h * n + imin(si, n - 1)], 0), S - 1);
 
   const uint16_t* qp = (const uint16_t*)a.q;
   const uint16_t* kp = (const uint16_t*)a.k;
   const uint16_t* vp = (const uint16_t*)a.v;
   const int tok_stride = H * D;
-  const size_t base_bh = ((size_t)b * S) * tok_stride + (size_t)h * D;
-
-  bf16x8 qf[KSTEPS];
-  if (scorer) {
-    const uint16_t* src = qp + base_bh + (size_t)qrow * tok_stride + g2 * 8;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + s * 16));
-  }
   const int cm = scorer ? -1 : a.cm[c];  // the candidate's rows in the word table, -1 for keep-all
   // wave 0 DMAs each tile's mask words: the workgroup's block is [table index][SG][2]
   // u32; 16 bytes per lane, lanes past the table read its first word (unused)
   const bool wdma = wv == 0 && a.n_masked > 0;
   const size_t wtile = (size_t)a.n_masked * a.n_pad * 8;  // bytes of one tile's words
-  const char* wsrc = (const char*)a.words + (size_t)h * nK * wtile;
+
+  // the current segment: unit (b, h, sample group sg), its key tiles
+  // [kt_begin, kt_begin + n_tiles) and this lane's sampled row
+  int b = 0, h = 0, sg = 0, kt_begin = 0, n_tiles = 0, si = 0;
+  size_t base_bh = 0;
+  const char* wsrc = nullptr;
   uint32_t woff[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    const int byte = d * 1024 + lane * 16;
-    const int t = byte / (SG * 8);
-    woff[d] = t < a.n_masked ? (uint32_t)(t * a.n_pad * 8 + sg * SG * 8 + byte % (SG * 8)) : 0u;
-  }
+  bf16x8 qf[KSTEPS];
 
   // DMA: K row R of LDS holds key swap_bits23(R) (chunks swizzled by ksw), V row R holds
   // key R (chunks swizzled by vsw for the transposing reads)
@@ -271,16 +261,10 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   };
 
   f32x16 acc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c_log2 = a.scale * 1.4426950408889634f;
   const float lazy = kLazyLog2 / c_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  // the all-keep reference needs the element mask only on the tile that holds the
-  // sequence tail
-  const bool need_mask = !scorer && (m.kind != VSA_MASK_ALL || (kt_begin + n_tiles) * BK > S);
 
   // DMA batch j (j = 0, 1, ...) loads K of chunk tile j into K stage j % NS (with the
   // tile's mask words into word stage j % NS) and V of chunk tile j - 1 into V stage
@@ -404,53 +388,90 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
     });
   };
 
-  wait_vmcnt<0>();  // query fragments before the first DMA
-  if (n_tiles > 0) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) issue_batch(j);
-    wait_batch(0, std::integral_constant<int, NS - 1>{});
-    barrier_lds();
+  for (int64_t pos = lo; pos < hi;) {
+    // ---- segment: the part of unit U in this workgroup's range ----
+    const int U = (int)(pos / nK);
+    const int64_t seg_end = hi < (int64_t)(U + 1) * nK ? hi : (int64_t)(U + 1) * nK;
+    const int slot = (int)(blockIdx.x - range_of(a, (int64_t)U * nK));  // index among the unit's ranges
+    kt_begin = (int)(pos - (int64_t)U * nK);
+    n_tiles = (int)(seg_end - pos);
+    sg = U % a.n_sg;
+    const int bh = U / a.n_sg;
+    h = bh % H;
+    b = bh / H;
+    si = sg * SG + sw * 32 + l32;
+    base_bh = ((size_t)b * S) * tok_stride + (size_t)h * D;
     if (scorer) {
-      score(0, 0);
-      steps([&](int it) __attribute__((always_inline)) {
-        if (it + 1 < n_tiles) score((it + 1) % NS, (it + 1) & 1);
-      });
-    } else if (need_mask) {
-      softmax_steps(std::integral_constant<bool, true>{});
-    } else {
-      softmax_steps(std::integral_constant<bool, false>{});
+      const int qrow = imin(imax(a.sample_idx[(size_t)h * n + imin(si, n - 1)], 0), S - 1);
+      const uint16_t* src = qp + base_bh + (size_t)qrow * tok_stride + g2 * 8;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + s * 16));
     }
-  }
-  wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it ends
-  if (scorer) return;
+    wsrc = (const char*)a.words + (size_t)h * nK * wtile;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const int byte = d * 1024 + lane * 16;
+      const int t = byte / (SG * 8);
+      woff[d] = t < a.n_masked ? (uint32_t)(t * a.n_pad * 8 + sg * SG * 8 + byte % (SG * 8)) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    // the all-keep reference needs the element mask only on the tile that holds the
+    // sequence tail
+    const bool need_mask = !scorer && (m.kind != VSA_MASK_ALL || (kt_begin + n_tiles) * BK > S);
 
-  const float l_tot = pair_sum(l_run);
-  if (si < n) {
-    float* dst = a.ws + ((((size_t)bh * a.n_chunks + chunk) * NC + c) * n + si) * kProfRow<D>;
+    wait_vmcnt<0>();  // query fragments before the first DMA
+    if (n_tiles > 0) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = db * 32 + r4 * 8 + g2 * 4;
-        *(float4*)(dst + d) = float4{acc[db][r4 * 4 + 0], acc[db][r4 * 4 + 1], acc[db][r4 * 4 + 2],
-                                     acc[db][r4 * 4 + 3]};
+      for (int j = 0; j < NS; ++j) issue_batch(j);
+      wait_batch(0, std::integral_constant<int, NS - 1>{});
+      barrier_lds();
+      if (scorer) {
+        score(0, 0);
+        steps([&](int it) __attribute__((always_inline)) {
+          if (it + 1 < n_tiles) score((it + 1) % NS, (it + 1) & 1);
+        });
+      } else if (need_mask) {
+        softmax_steps(std::integral_constant<bool, true>{});
+      } else {
+        softmax_steps(std::integral_constant<bool, false>{});
       }
-    if (g2 == 0) {
-      dst[D] = m_run;
-      dst[D + 1] = l_tot;
     }
+    wait_vmcnt<0>();  // no DMA may still be writing the rings
+    if (!scorer) {
+      const float l_tot = pair_sum(l_run);
+      if (si < n) {
+        float* dst = a.ws + ((((size_t)U * a.n_slots + slot) * NC + c) * SG + sw * 32 + l32) * kProfRow<D>;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = db * 32 + r4 * 8 + g2 * 4;
+            *(float4*)(dst + d) = float4{acc[db][r4 * 4 + 0], acc[db][r4 * 4 + 1], acc[db][r4 * 4 + 2],
+                                         acc[db][r4 * 4 + 3]};
+          }
+        if (g2 == 0) {
+          dst[D] = m_run;
+          dst[D + 1] = l_tot;
+        }
+      }
+    }
+    barrier_lds();  // every wave is done with the rings before the next segment's DMAs
+    pos = seg_end;
   }
 }
 
 __host__ __device__ inline size_t part_floats(const ProfArgs& a) {
-  return (size_t)a.B * a.H * a.n_chunks * a.n_cand * a.n * (a.D + 4);
+  return (size_t)a.B * a.H * a.n_slots * a.n_cand * a.n_pad * (a.D + 4);
 }
 
-// Pass 2a: one wave per (b, h, sample) merges that row's chunk partials of every
-// candidate with the softmax statistics: lane ch reads chunk ch's max and row sum (64
-// chunks per round), the wave takes the largest max, and each chunk's output row
-// (lanes over channels, D/64 adjacent channels per lane) is added with weight exp of
-// its max against that one.  Writes sum over channels of (o_c - o_0)^2 for c >= 1 to
+// Pass 2a: one wave per (b, h, sample) merges that row's partial slots of every
+// candidate with the softmax statistics: lane ch reads slot ch's max and row sum (64
+// slots per round), the wave takes the largest max, and each slot's output row (lanes
+// over channels, D/64 adjacent channels per lane) is added with weight exp of its max
+// against that one.  Writes sum over channels of (o_c - o_0)^2 for c >= 1 to
 // sums[h][b][sample][c].
 template <int D, int NC>
 __global__ __launch_bounds__(256) void profile_merge_kernel(ProfArgs a) {
@@ -458,19 +479,25 @@ __global__ __launch_bounds__(256) void profile_merge_kernel(ProfArgs a) {
   typedef float fvec __attribute__((ext_vector_type(DL)));
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n = a.n, H = a.H, nch = a.n_chunks;
+  const int n = a.n, H = a.H;
   if (row >= (long long)a.B * H * n) return;
   const int si = (int)(row % n);
   const int bh = (int)(row / n);
   const int h = bh % H, b = bh / H;
   const float c_log2 = a.scale * 1.4426950408889634f;
   constexpr size_t RW = kProfRow<D>;
-  const size_t ch_stride = (size_t)NC * n * RW;
-  const float* base = a.ws + (size_t)bh * nch * ch_stride + (size_t)si * RW;
+  // the row's unit and the workgroup ranges that cover the unit's key tiles
+  const int sgr = a.n_pad / a.n_sg;  // rows per sample group
+  const int U = bh * a.n_sg + si / sgr;
+  const int64_t nK = (a.S + BK - 1) / BK;
+  const int64_t w0 = range_of(a, U * nK);
+  const int nch = (int)(range_of(a, (U + 1) * nK - 1) - w0 + 1);
+  const size_t ch_stride = (size_t)NC * sgr * RW;  // between partial slots
+  const float* base = a.ws + ((size_t)U * a.n_slots * NC * sgr + si % sgr) * RW;
   fvec o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const float* pc = base + (size_t)c * n * RW;
+    const float* pc = base + (size_t)c * sgr * RW;
     float mu = -INFINITY;
     for (int c0 = 0; c0 < nch; c0 += 64)
       if (c0 + lane < nch) mu = fmaxf(mu, pc[(c0 + lane) * ch_stride + D]);
@@ -552,10 +579,7 @@ __global__ __launch_bounds__(256) void profile_route_kernel(ProfArgs a) {
 
 template <int D, int NWS, int NC>
 hipError_t launch_t(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
-  const long long units = (long long)a.n_chunks * a.B * a.H;
-  const int n_sg = (a.n + NWS * 32 - 1) / (NWS * 32);
-  const long long blocks = ((units + 7) / 8) * 8 * n_sg;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.n_pad != a.n_sg * NWS * 32 || a.n_wg <= 0) return hipErrorInvalidValue;
   hipError_t e;
   if (a.n_masked > 0) {
     const int wblocks = ((a.S + BK - 1) / BK + kWordTiles - 1) / kWordTiles;
@@ -563,7 +587,7 @@ hipError_t launch_t(const ProfArgs& a, const MaskTable& cands, hipStream_t st) {
     hipLaunchKernelGGL(profile_words_kernel, dim3(wblocks, a.H * a.n_masked), dim3(64), 0, st, a, cands);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((profile_part_kernel<D, NWS, NC>), dim3((unsigned)blocks), dim3(NWS * (NC + 1) * 64), 0, st, a,
+  hipLaunchKernelGGL((profile_part_kernel<D, NWS, NC>), dim3((unsigned)a.n_wg), dim3(NWS * (NC + 1) * 64), 0, st, a,
                      cands);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long mrows = (long long)a.B * a.H * a.n;
@@ -602,49 +626,31 @@ int32_t profile_sample_waves(int32_t n, int32_t n_cand) {
   return n <= 32 ? 1 : cap;
 }
 
-// Key chunks per (b, h): the count that minimises rounds of resident workgroups times
-// key tiles per chunk (fewest chunks on ties), with each of the 256 compute units holding
-// as many workgroups as its LDS (160 KB against the K and V rings) and its waves (two per
-// SIMD) allow, and at most 8192 workgroups.
-int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand) {
-  const int nK = (S + pipe::BK - 1) / pipe::BK;
+// The launch plan: units (b, h, sample group), the workgroups that can be resident at
+// once (each of the 256 compute units holding as many as its LDS, 160 KB, and its waves,
+// two per SIMD, allow), one contiguous range of the units' key tiles per workgroup, and
+// the partial slots a unit needs (a range has at least total / n_wg tiles, so at most
+// (nK - 1) / that + 2 ranges meet one unit).  Workspace: the partial rows, the per-row
+// squared-deviation sums, then (at a 256-byte boundary) the mask-word table, sized for
+// every candidate having one.
+ProfPlan profile_plan(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand) {
+  ProfPlan p;
   const int nws = profile_sample_waves(n, n_cand);
-  const long long per_chunk = (long long)B * H * ((n + nws * 32 - 1) / (nws * 32));
+  const int sg = 32 * nws;
+  p.n_sg = (n + sg - 1) / sg;
+  p.n_pad = p.n_sg * sg;
+  const int64_t nK = ((int64_t)S + pipe::BK - 1) / pipe::BK;
+  p.total = (int64_t)B * H * p.n_sg * nK;
   const int lds = prof_lds(D, nws, n_cand, prof_stages(D, nws, n_cand));
-  const int by_lds = (160 * 1024) / lds;
-  const int by_waves = 8 / (nws * (n_cand + 1));
-  const long long slots = 256LL * imax(1, imin(by_lds, by_waves));
-  const long long lim = 8192 / (per_chunk > 0 ? per_chunk : 1);
-  const long long c_max = lim < 1 ? 1 : (lim < nK ? lim : nK);
-  int best = 1;
-  long long best_cost = -1;
-  for (long long c = 1; c <= c_max; ++c) {
-    const long long cost = ((c * per_chunk + slots - 1) / slots) * ((nK + c - 1) / c);
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best = (int)c;
-    }
-  }
-  return best;
-}
-
-int32_t profile_pad_samples(int32_t n, int32_t n_cand) {
-  const int sg = 32 * profile_sample_waves(n, n_cand);
-  return (n + sg - 1) / sg * sg;
-}
-
-// Workspace: the chunk partials, the merge sums, then (at a 256-byte boundary) the mask
-// word table, sized for every candidate having one.
-size_t profile_words_offset(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand, int32_t n_chunks) {
-  const size_t f = (size_t)B * H * n_chunks * n_cand * n * (D + 4) + (size_t)H * B * n * n_cand;
-  return (f + 63) / 64 * 64;
-}
-
-size_t profile_ws_floats(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand,
-                         int32_t n_chunks) {
-  const size_t nK = ((size_t)S + pipe::BK - 1) / pipe::BK;
-  return profile_words_offset(B, H, D, n, n_cand, n_chunks) +
-         (size_t)H * nK * n_cand * profile_pad_samples(n, n_cand) * 2;
+  const int per_cu = imax(1, imin((160 * 1024) / lds, 8 / (nws * (n_cand + 1))));
+  p.n_wg = (int32_t)(p.total < 256LL * per_cu ? p.total : 256LL * per_cu);
+  const int64_t per_min = p.total / (p.n_wg > 0 ? p.n_wg : 1);
+  p.n_slots = (int32_t)((nK - 1) / (per_min > 0 ? per_min : 1) + 2);
+  const size_t part = (size_t)B * H * p.n_slots * n_cand * p.n_pad * (D + 4);
+  const size_t sums = (size_t)H * B * n * n_cand;
+  p.words_off = (part + sums + 63) / 64 * 64;
+  p.ws_floats = p.words_off + (size_t)H * nK * n_cand * p.n_pad * 2;
+  return p;
 }
 
 hipError_t launch_profile(const ProfArgs& a, const MaskTable& cands, hipStream_t stream) {

@@ -683,8 +683,7 @@ vsa_status vsa_profile_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t 
   if (!bytes) return fail(VSA_ERR_INVALID_ARG, "bytes is NULL");
   if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || n_samples <= 0 || n_cand <= 0)
     return fail(VSA_ERR_INVALID_ARG, "sizes must be positive");
-  *bytes = vsa::profile_ws_floats(B, S, H, D, n_samples, n_cand, vsa::profile_chunks(B, S, H, D, n_samples, n_cand)) *
-           sizeof(float);
+  *bytes = vsa::profile_plan(B, S, H, D, n_samples, n_cand).ws_floats * sizeof(float);
   return ok();
 }
 
@@ -718,12 +717,14 @@ vsa_status vsa_profile_heads(const void* q, const void* k, const void* v, vsa_dt
   }
   vsa::ProfArgs a;
   memset(&a, 0, sizeof a);
-  a.n_chunks = vsa::profile_chunks(B, S, H, D, n_samples, n_cand);
-  const size_t need = vsa::profile_ws_floats(B, S, H, D, n_samples, n_cand, a.n_chunks) * sizeof(float);
+  const vsa::ProfPlan plan = vsa::profile_plan(B, S, H, D, n_samples, n_cand);
+  const size_t need = plan.ws_floats * sizeof(float);
   if (!workspace || ws_bytes < need)
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
-  const int nK = (S + 63) / 64;
-  a.chunk_tiles = (nK + a.n_chunks - 1) / a.n_chunks;
+  a.n_sg = plan.n_sg;
+  a.n_wg = plan.n_wg;
+  a.n_slots = plan.n_slots;
+  a.total = plan.total;
   a.q = q; a.k = k; a.v = v;
   a.sample_idx = sample_idx;
   a.err = err; a.route = route;
@@ -732,8 +733,8 @@ vsa_status vsa_profile_heads(const void* q, const void* k, const void* v, vsa_dt
   a.scale = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
   a.is_bf16 = 1;
   a.g = make_geom(grid, layout);
-  a.n_pad = vsa::profile_pad_samples(n_samples, n_cand);
-  a.words = (uint32_t*)(a.ws + vsa::profile_words_offset(B, H, D, n_samples, n_cand, a.n_chunks));
+  a.n_pad = plan.n_pad;
+  a.words = (uint32_t*)(a.ws + plan.words_off);
   for (int c = 0; c < 4; ++c) a.cm[c] = a.cand_of[c] = -1;
   for (int c = 0; c < n_cand; ++c)
     if (table.m[c].kind != VSA_MASK_ALL) {

@@ -158,7 +158,11 @@ struct ProfArgs {
   float* err;
   int32_t* route;
   float* ws;
-  int32_t B, S, H, D, n, n_cand, n_chunks, chunk_tiles;
+  int32_t B, S, H, D, n, n_cand;
+  int32_t n_sg;     // sample groups per (b, h); a unit is (b, h, sample group)
+  int32_t n_wg;     // workgroups of pass 1, each one contiguous range of the units' key tiles
+  int32_t n_slots;  // partial slots per unit
+  int64_t total;    // key tiles of all units
   float scale;
   int32_t is_bf16;
   Geom g;
@@ -179,12 +183,14 @@ struct MergeArgs {
 };
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
-size_t profile_ws_floats(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand,
-                         int32_t n_chunks);
-size_t profile_words_offset(int32_t B, int32_t H, int32_t D, int32_t n, int32_t n_cand, int32_t n_chunks);
-int32_t profile_pad_samples(int32_t n, int32_t n_cand);
+struct ProfPlan {
+  int32_t n_sg, n_pad, n_wg, n_slots;
+  int64_t total;
+  size_t words_off;  // floats before the mask-word table
+  size_t ws_floats;  // workspace size in floats
+};
+ProfPlan profile_plan(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand);
 int32_t profile_sample_waves(int32_t n, int32_t n_cand);
-int32_t profile_chunks(int32_t B, int32_t S, int32_t H, int32_t D, int32_t n, int32_t n_cand);
 hipError_t launch_profile(const ProfArgs& a, const MaskTable& cands, hipStream_t stream);
 
 }  // namespace vsa
