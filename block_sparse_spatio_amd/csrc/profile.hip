@@ -52,10 +52,10 @@ constexpr int kProfRow = D + 4;
 constexpr int dma_waves(int nw) { return nw >= 8 ? 8 : (nw >= 4 ? 4 : 2); }
 
 // LDS of a pass-1 workgroup with NS ring stages: the K and V rings, NS stages of mask
-// words (1 KB DMAs) and two 64 x 32 fp32 score blocks per sample wave.
+// words (1 KB DMAs) and three 64 x 32 fp32 score blocks per sample wave.
 constexpr int prof_word_dmas(int nws, int nc) { return (nc * nws * 32 * 8 + 1023) / 1024; }
 constexpr int prof_lds(int d, int nws, int nc, int ns) {
-  return 2 * ns * pipe::BK * d * 2 + ns * prof_word_dmas(nws, nc) * 1024 + 2 * nws * 8192;
+  return 2 * ns * pipe::BK * d * 2 + ns * prof_word_dmas(nws, nc) * 1024 + 3 * nws * 8192;
 }
 // Ring depth in key tiles: the deepest of 4, 3, 2 stages whose LDS fits in 160 KB.
 constexpr int prof_stages(int d, int nws, int nc) {
@@ -118,7 +118,7 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   __shared__ __attribute__((aligned(1024))) char kring[NS * C::TILE_B];
   __shared__ __attribute__((aligned(1024))) char vring[NS * C::TILE_B];
   __shared__ __attribute__((aligned(1024))) char wring[NS * ND * 1024];
-  __shared__ __attribute__((aligned(1024))) char sring[2 * NWS * SB];
+  __shared__ __attribute__((aligned(1024))) char sring[3 * NWS * SB];
   lchar* const KL = (lchar*)kring;
   lchar* const VL = (lchar*)vring;
   lchar* const WL = (lchar*)wring;
@@ -266,25 +266,24 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
   const float lazy = kLazyLog2 / c_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // DMA batch j (j = 0, 1, ...) loads K of chunk tile j into K stage j % NS (with the
-  // tile's mask words into word stage j % NS) and V of chunk tile j - 1 into V stage
-  // (j - 1) % NS; the prologue issues batches 0 .. NS-1 and step it issues batch it + NS.
-  // Step it needs batch it + 1: the score waves turn K(it+1) into S(it+1) (score buffer
-  // (it+1) & 1) while the softmax waves take S(it) (written in the step before) with
-  // V(it) and read the mask words of tile it+1 for the next step.  The stages a batch
-  // overwrites were last read in the step before it is issued, and a score buffer is
-  // rewritten two steps after it was filled, both past a barrier.
+  // DMA batch j (j = 0, 1, ...) loads K of segment tile j into K stage j % NS, the mask
+  // words of tile j-1 into word stage (j-1) % NS and V of tile j-2 into V stage
+  // (j-2) % NS: all three are first needed in step j-2.  The prologue issues batches
+  // 0 .. NS (batch NS after S(0)) and step it issues batch it + NS + 1.  In step it the score waves turn K(it+2)
+  // into S(it+2) (score buffer (it+2) % 3) while the softmax waves exponentiate S(it)
+  // (masked, in registers since the step before), multiply it with V(it), and mask and
+  // max-reduce S(it+1) (written in the step before) with the words of tile it+1.  The
+  // stages a batch overwrites were last read in the step before it is issued, and a score
+  // buffer is rewritten three steps after it was filled, both past a barrier.
   auto issue_batch = [&](int j) __attribute__((always_inline)) {
-    if (j < n_tiles) {
-      issue(kt_begin + j, kring + (j % NS) * C::TILE_B, false);
-      if (wdma) {
-        const char* src = wsrc + (size_t)(kt_begin + j) * wtile;
-        const uint32_t dst = lds_addr(wring + (j % NS) * ND * 1024);
+    if (j < n_tiles) issue(kt_begin + j, kring + (j % NS) * C::TILE_B, false);
+    if (wdma && j >= 1 && j - 1 < n_tiles) {
+      const char* src = wsrc + (size_t)(kt_begin + j - 1) * wtile;
+      const uint32_t dst = lds_addr(wring + ((j - 1) % NS) * ND * 1024);
 #pragma unroll
-        for (int d = 0; d < ND; ++d) dma16(src, woff[d], dst + d * 1024);
-      }
+      for (int d = 0; d < ND; ++d) dma16(src, woff[d], dst + d * 1024);
     }
-    if (j >= 1 && j - 1 < n_tiles) issue(kt_begin + j - 1, vring + ((j - 1) % NS) * C::TILE_B, true);
+    if (j >= 2 && j - 2 < n_tiles) issue(kt_begin + j - 2, vring + ((j - 2) % NS) * C::TILE_B, true);
   };
   // wait until batch j has landed: while every batch after it up to j + later is whole
   // (2 NI DMAs per DMA wave, and ND more for wave 0's mask words), the later batches
@@ -300,12 +299,9 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
       wait_vmcnt<L * 2 * NI>();
   };
 
-  // softmax wave, step it: S(it) from score buffer it & 1 under mask word w, the
-  // online softmax, and O^T += V(it)^T P(it)^T
-  auto softmax_pv = [&](auto mask_tag, int it, uint32_t w) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(mask_tag)::value;
-    f32x16 s[2];
-    const lchar* src = SL + ((it & 1) * NWS + sw) * SB + lane * 16;
+  // softmax wave: S(t) from score buffer t % 3, under this lane's mask word of tile t
+  auto read_scores = [&](int t, f32x16* s) __attribute__((always_inline)) {
+    const lchar* src = SL + ((t % 3) * NWS + sw) * SB + lane * 16;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const f32x4 x = *(const l_f32x4*)(src + q * 1024);
@@ -314,20 +310,22 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
       s[q >> 2][(q & 3) * 4 + 2] = x.z;
       s[q >> 2][(q & 3) * 4 + 3] = x.w;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 32; ++v) {
-      float x = s[v >> 4][v & 15];
-      if constexpr (MASKED) {
-        x = masked(x, w, v);
-        s[v >> 4][v & 15] = x;
-      }
-      mx = __builtin_elementwise_maximum(mx, x);
-    }
-    const float mt = pair_max(mx);
-    const bool grow = mt > m_run + lazy;
+  };
+  f32x16 s_cur[2];
+  float mt_cur = -INFINITY;
+
+  // softmax wave, step it: the online softmax of S(it) and O^T += V(it)^T P(it)^T, with
+  // the mask and row max of S(it+1) between the products
+  auto softmax_pv = [&](auto mask_tag, int it) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(mask_tag)::value;
+    // S(it+1) and its words; after the last tile a stale buffer and stage (nothing
+    // writes them any more), read only to keep the step straight-line code
+    f32x16 s_next[2];
+    read_scores(it + 1, s_next);
+    const uint32_t w_next = MASKED ? word(it + 1) : ~0u;
+    const bool grow = mt_cur > m_run + lazy;
     if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mt : m_run;
+      const float m_new = grow ? mt_cur : m_run;
       const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c_log2) : 1.f;
       l_run *= alpha;
 #pragma unroll
@@ -338,8 +336,8 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
     bf16x2 pk[16];
 #pragma unroll
     for (int v = 0; v < 32; v += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[v >> 4][v & 15], c_log2, -mc));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[v >> 4][(v & 15) + 1], c_log2, -mc));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][v & 15], c_log2, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][(v & 15) + 1], c_log2, -mc));
       pk[v >> 1] = pack_bf16x2(p0, p1);
       l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[v >> 1], ones, l_run, false);
     }
@@ -347,6 +345,7 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
     // an immediate offset (the compiler otherwise spreads the ring index arithmetic
     // over one register per read)
     const lchar* v_use = VL + __builtin_amdgcn_readfirstlane((it % NS) * C::TILE_B);
+    float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16x8 pf = __builtin_bit_cast(
@@ -364,28 +363,50 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
         const i16x8 vv = __builtin_shufflevector(v0[db], v1[db], 0, 1, 2, 3, 4, 5, 6, 7);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
       }
+      // a quarter of S(it+1): mask and row max (discarded after the last tile)
+#pragma unroll
+      for (int v = 8 * j; v < 8 * j + 8; ++v) {
+        float x = s_next[v >> 4][v & 15];
+        if constexpr (MASKED) {
+          x = masked(x, w_next, v);
+          s_next[v >> 4][v & 15] = x;
+        }
+        mx = __builtin_elementwise_maximum(mx, x);
+      }
     }
+    mt_cur = pair_max(mx);
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
   };
 
-  // Every wave passes the same barriers: one after the prologue's DMAs, one per step.
-  // The two roles run their own loops so that the score waves' query fragments and the
-  // softmax waves' accumulators are never live together.
+  // Every wave passes the same barriers: two in the prologue, one per step.  The two
+  // roles run their own loops so that the score waves' query fragments and the softmax
+  // waves' accumulators are never live together.
   auto steps = [&](auto&& body) __attribute__((always_inline)) {
     for (int it = 0; it < n_tiles; ++it) {
-      wait_batch(it + 1, std::integral_constant<int, NS - 2>{});
+      wait_batch(it + 2, std::integral_constant<int, NS - 2>{});
       barrier_lds();
-      issue_batch(it + NS);
+      issue_batch(it + NS + 1);
       body(it);
     }
   };
   auto softmax_steps = [&](auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(mask_tag)::value;
-    uint32_t w = MASKED ? word(0) : ~0u;
-    steps([&](int it) __attribute__((always_inline)) {
-      const uint32_t w_next = MASKED && it + 1 < n_tiles ? word(it + 1) : ~0u;
-      softmax_pv(mask_tag, it, w);
-      w = w_next;
-    });
+    // S(0), written in the prologue
+    read_scores(0, s_cur);
+    const uint32_t w = MASKED ? word(0) : ~0u;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 32; ++v) {
+      float x = s_cur[v >> 4][v & 15];
+      if constexpr (MASKED) {
+        x = masked(x, w, v);
+        s_cur[v >> 4][v & 15] = x;
+      }
+      mx = __builtin_elementwise_maximum(mx, x);
+    }
+    mt_cur = pair_max(mx);
+    steps([&](int it) __attribute__((always_inline)) { softmax_pv(mask_tag, it); });
   };
 
   for (int64_t pos = lo; pos < hi;) {
@@ -424,14 +445,21 @@ void profile_part_kernel(ProfArgs a, MaskTable cands) {
 
     wait_vmcnt<0>();  // query fragments before the first DMA
     if (n_tiles > 0) {
+      // prologue: K(0), K(1) and the words of tile 0 (batches 0 and 1), S(0) and S(1);
+      // batch NS puts K(NS) into K(0)'s stage, so it goes out once S(0) is done
 #pragma unroll
       for (int j = 0; j < NS; ++j) issue_batch(j);
-      wait_batch(0, std::integral_constant<int, NS - 1>{});
+      wait_batch(1, std::integral_constant<int, NS - 2>{});
       barrier_lds();
       if (scorer) {
         score(0, 0);
+        if (n_tiles > 1) score(1, 1);
+      }
+      barrier_lds();
+      issue_batch(NS);
+      if (scorer) {
         steps([&](int it) __attribute__((always_inline)) {
-          if (it + 1 < n_tiles) score((it + 1) % NS, (it + 1) & 1);
+          if (it + 2 < n_tiles) score((it + 2) % NS, (it + 2) % 3);
         });
       } else if (need_mask) {
         softmax_steps(std::integral_constant<bool, true>{});
