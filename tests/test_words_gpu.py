@@ -143,6 +143,28 @@ def test_words_match_oracle(gpu_lib, seed):
     _check_words(g, layout, masks, tiles, compact)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_words_frame_major_stripes(gpu_lib, seed):
+    """Stripe heads in frame-major order on frames of at least 64 tokens (the kernel's
+    shortcut through the position difference, frame crossings inside query and key
+    tiles, sink frames, ragged tails): every word against the oracle."""
+    rng = np.random.default_rng(9200 + seed)
+    while True:
+        dims = [int(rng.integers(1, 7)), int(rng.integers(2, 20)), int(rng.integers(2, 30))]
+        if dims[1] * dims[2] >= 64:
+            break
+    g = W.grid(*dims)
+    masks = [W.mask_stripe(int(rng.integers(1, 4)), int(rng.integers(-2, 3)), int(rng.integers(1, 6)),
+                           int(rng.integers(1, 6)), int(rng.integers(-3, 4)), int(rng.integers(1, 120)),
+                           sink_frames=int(rng.integers(0, 3))) for _ in range(int(rng.integers(1, 5)))]
+    Bq = int(rng.choice([64, 128, 256]))
+    say(f"frame-major stripe words seed={seed} grid={g} Bq={Bq} masks={masks}")
+    tiles = vsa.vsa_classify_tiles(g, "frame", masks, Bq, 64, device=dev(), with_cls=False)
+    words = _words(g, "frame", masks, tiles, "compact")
+    torch.cuda.synchronize()
+    assert _check_words(g, "frame", masks, tiles, words) == int(tiles["bnd_offs"][-1])
+
+
 @pytest.mark.parametrize("seed", range(16))
 def test_forward_with_words_is_identical(gpu_lib, seed):
     g, layout, masks, Bq, D = _case(seed)
