@@ -89,10 +89,11 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   const int b = rank % a.B;
   const int slot = hm.slot[h];
   const int q_lo = a.sched[slot * 9 + xcd], q_hi = imin(a.sched[slot * 9 + xcd + 1], a.nQ);
-  const int qt = q_lo + (kk - rank * cq);
-  if (qt >= q_hi || qt < 0) return;
+  const int qv = q_lo + (kk - rank * cq);  // position in the mask's visiting order
+  if (qv >= q_hi || qv < 0) return;
 
   const DevMask m_head = masks.m[slot];
+  const int qt = qtile_visit(qv, qtile_bands(a.g, m_head, Bq), a.nQ);
   // The body is instantiated for the common (order, mask kind) pairs with both fixed at
   // compile time, so that the per-tile mask arithmetic of a boundary tile carries no
   // other case and stays in straight-line code, plus one generic instance.
@@ -592,14 +593,16 @@ hipError_t launch_t(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
 // Per-call schedule, one workgroup.  Cost of a query tile = 5 per full and 6 per
 // boundary key tile (a boundary tile is about 1.2 full tiles) plus 10 for the per-tile
 // prologue and epilogue.  For every distinct mask u: the prefix sum P of the costs over
-// its query tiles, raw splits s_x = min{k : P(k) >= x*P(nQ)/8}, then the ranges clamped
-// to at most cq tiles each (sched_cq), so that the grid covers every tile.  Then the
-// heads in descending order of their mask's total cost (ties by head index).
+// its query tiles in the mask's visiting order (qtile_visit), raw splits
+// s_x = min{k : P(k) >= x*P(nQ)/8}, then the ranges clamped to at most cq tiles each
+// (sched_cq), so that the grid covers every tile.  Then the heads in descending order of
+// their mask's total cost (ties by head index).
 constexpr int kSchedThreads = 1024;
 
 __global__ __launch_bounds__(kSchedThreads) void fwd_schedule_kernel(const int32_t* __restrict__ n_full,
                                                                      const int32_t* __restrict__ n_bnd, int U,
                                                                      int nQ, int nK, int H, int cq, HeadMap hm,
+                                                                     Geom g, MaskTable masks, int Bq,
                                                                      int32_t* __restrict__ sched) {
   __shared__ long long seg[kSchedThreads];
   __shared__ long long tot[VSA_MAX_UNIQUE_MASKS];
@@ -612,8 +615,9 @@ __global__ __launch_bounds__(kSchedThreads) void fwd_schedule_kernel(const int32
   };
   for (int u = 0; u < U; ++u) {
     const size_t row0 = (size_t)u * nQ;
+    const int W = qtile_bands(g, masks.m[u], Bq);
     long long sum = 0;
-    for (int i = i0; i < i1; ++i) sum += cost(row0 + i);
+    for (int i = i0; i < i1; ++i) sum += cost(row0 + qtile_visit(i, W, nQ));
     seg[t] = sum;
     __syncthreads();
     for (int d = 1; d < kSchedThreads; d <<= 1) {
@@ -626,7 +630,7 @@ __global__ __launch_bounds__(kSchedThreads) void fwd_schedule_kernel(const int32
     // P(i0) = seg[t] - sum; raw split x (1..7): the first k with P(k) >= x*total/8
     long long p = seg[t] - sum;
     for (int i = i0; i < i1; ++i) {
-      const long long pn = p + cost(row0 + i);
+      const long long pn = p + cost(row0 + qtile_visit(i, W, nQ));
       for (int x = 1; x < 8; ++x) {
         const long long tgt = (total * x + 7) / 8;  // P(k) >= x*total/8 <=> 8*P(k) >= x*total
         if (p < tgt && pn >= tgt) raw[x] = i + 1;
@@ -671,10 +675,11 @@ int32_t sched_cq(int32_t nQ) { return (int32_t)((3LL * nQ + 15) / 16); }
 
 size_t sched_ints(int32_t U, int32_t H) { return (size_t)VSA_MAX_UNIQUE_MASKS * 9 + VSA_MAX_HEADS; }
 
-hipError_t launch_fwd_schedule(const FwdArgs& a, int32_t U, const HeadMap& hm, int32_t* sched, hipStream_t stream) {
+hipError_t launch_fwd_schedule(const FwdArgs& a, int32_t U, const HeadMap& hm, const MaskTable& masks, int32_t* sched,
+                               hipStream_t stream) {
   if (U < 1 || U > VSA_MAX_UNIQUE_MASKS || a.H > VSA_MAX_HEADS) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fwd_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a.n_full, a.n_bnd, U, a.nQ, a.nK,
-                     a.H, a.cq, hm, sched);
+                     a.H, a.cq, hm, a.g, masks, a.Bq, sched);
   return hipGetLastError();
 }
 

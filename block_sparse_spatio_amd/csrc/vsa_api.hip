@@ -548,7 +548,7 @@ vsa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float*
     int32_t* sched = (int32_t*)((char*)vt + (size_t)B * H * D * a.s_pad * eb);
     a.cq = vsa::sched_cq(a.nQ);
     a.sched = sched;
-    if ((e = vsa::launch_fwd_schedule(a, U, hm, sched, hs)) != hipSuccess) return hip_fail(e, "schedule");
+    if ((e = vsa::launch_fwd_schedule(a, U, hm, table, sched, hs)) != hipSuccess) return hip_fail(e, "schedule");
     if ((e = vsa::launch_transpose_v(v, vt, B, a.S, H, D, a.s_pad, G, hl, reorder ? 1 : 0, S, hs)) != hipSuccess)
       return hip_fail(e, "transpose v");
     a.vt = vt;

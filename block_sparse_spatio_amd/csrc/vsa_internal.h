@@ -115,9 +115,10 @@ struct FwdArgs {
   int32_t words_cap;
   const int64_t* bnd_offs;
   // bf16 path: the per-call schedule (launch_fwd_schedule): for every distinct mask the
-  // query tiles that XCD x runs, [sched[u*9 + x], sched[u*9 + x + 1]), and after the
-  // U*9 entries the heads in descending order of cost; cq = query tiles per XCD and
-  // head that the grid provides (sched_cq, at least every chunk's length)
+  // query tiles that XCD x runs, positions [sched[u*9 + x], sched[u*9 + x + 1]) of the
+  // mask's visiting order (qtile_visit), and after the U*9 entries the heads in
+  // descending order of cost; cq = query tiles per XCD and head that the grid provides
+  // (sched_cq, at least every chunk's length)
   const int32_t* sched;
   int32_t cq;
   Geom g;
@@ -131,7 +132,40 @@ hipError_t launch_attn_bf16(const FwdArgs& a, const MaskTable& masks, const Head
 // orders the heads heaviest first; it is written by one small kernel per call.
 int32_t sched_cq(int32_t nQ);
 size_t sched_ints(int32_t U, int32_t H);
-hipError_t launch_fwd_schedule(const FwdArgs& a, int32_t U, const HeadMap& hm, int32_t* sched,
+// The order in which a head's query tiles are dealt to the XCDs.  A box mask that is
+// unbounded in time and bounded in space (a temporal head) keeps the keys of the query's
+// in-frame neighbourhood in every frame, so in frame-major order the query tiles at the
+// same place in different frames need the same key tiles.  Such heads visit the tiles
+// band by band: the tiles form a grid of W = round(HW / Bq) columns (qt = r*W + c, so a
+// column holds the tiles about one frame apart), read column after column; the
+// workgroups an XCD runs at once then walk nearly the same key tiles in the same order,
+// and those reach L2 once.  Every other head keeps the identity order (W = 1).
+__host__ __device__ inline int32_t qtile_bands(const Geom& g, const DevMask& m, int32_t Bq) {
+  if (m.layout != VSA_LAYOUT_FRAME_MAJOR || g.padded || m.kind != VSA_MASK_BOX || m.rt >= 0 ||
+      (m.rh < 0 && m.rw < 0))
+    return 1;
+  const int32_t w = (g.HW + Bq / 2) / Bq;
+  return w >= 2 ? w : 1;
+}
+// position j of the visiting order -> query tile (a bijection on [0, nQ)): column c of
+// the W-column grid holds R = ceil(nQ / W) tiles for c < full = nQ - (R - 1) W, else R - 1
+__host__ __device__ inline int32_t qtile_visit(int32_t j, int32_t W, int32_t nQ) {
+  if (W <= 1) return j;
+  const int32_t R = (nQ + W - 1) / W;
+  const int32_t full = nQ - (R - 1) * W;
+  int32_t c, r;
+  if (j < full * R) {
+    c = j / R;
+    r = j - c * R;
+  } else {
+    const int32_t jj = j - full * R;
+    c = full + jj / (R - 1);
+    r = jj - (c - full) * (R - 1);
+  }
+  return r * W + c;
+}
+
+hipError_t launch_fwd_schedule(const FwdArgs& a, int32_t U, const HeadMap& hm, const MaskTable& masks, int32_t* sched,
                                hipStream_t stream);
 hipError_t launch_attn_f32(const FwdArgs& a, const MaskTable& masks, const HeadMap& hm,
                            hipStream_t stream);

@@ -48,6 +48,16 @@ int main(int argc, char** argv){
     if(d<(1u<<20)) for(int a=-3*(int)d-2;a<=3*(int)d+2;a+=1+(int)d/7){ int ref=a>=0?a/(int)d:-((-a+(int)d-1)/(int)d);
       if(floor_div_by(a,v)!=ref){ if(nbad<5) printf("BAD floor_div_by %d / %u\n",a,d); nbad++; } }
   }
+  // the query-tile visiting order of the forward's schedule: a bijection on [0, nQ) that
+  // reads the W-column grid of tiles (qt = r*W + c) column after column
+  for(int nQ=1;nQ<=700;nQ+=(nQ<100?1:7)) for(int W=1;W<=90;++W){
+    std::vector<char> seen(nQ,0); int pc=0, pr=-1;  // the previous tile's column and row
+    for(int j=0;j<nQ;++j){ int q=qtile_visit(j,W,nQ);
+      bool ok = q>=0 && q<nQ && !seen[q];
+      if(ok){ seen[q]=1; const int c=q%W, r=q/W;
+        ok = (c==pc && r==pr+1) || (c==pc+1 && r==0);  // down the column, or the next one from its top
+        pc=c; pr=r; }
+      if(!ok){ if(nbad<5) printf("BAD visit nQ %d W %d j %d -> %d\n",nQ,W,j,q); nbad++; break; } } }
   for(int trial=0; trial<trials; ++trial){
     Geom g; int layout = rand()%4;  // 3: tile-major over the padded grid
     g.padded = 0;
