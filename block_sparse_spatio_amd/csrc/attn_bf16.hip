@@ -270,10 +270,10 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 
   // ---- software pipeline over the listed key tiles.  Entering step i, S(i) is in
   // registers (masked) with its row max, K(i+1) and V(i) are in LDS.  The step
-  // prefetches K(i+2) and V(i+1), then runs two stages, each an even interleave of
-  // matrix-core work and vector work:
-  //   A: S(i+1) = K(i+1) Q^T   with   P(i) = exp2(S(i) - max), row sums
-  //   B: O^T += V(i)^T P(i)^T  with   the element mask and row max of S(i+1)
+  // prefetches K(i+2) and V(i+1), then runs two stages and a tail:
+  //   A: S(i+1) = K(i+1) Q^T   interleaved with   P(i) = exp2(S(i) - max)
+  //   B: O^T += V(i)^T P(i)^T  (the compiler places the vector work of B in the tail)
+  //   tail: the element mask and row max of S(i+1), the row sums of P(i)
   // One barrier per step: after it, every wave has finished the previous step (so its
   // buffers may be refilled) and every DMA of this step's inputs has landed.
   f32x16 s_cur[2];
@@ -401,8 +401,6 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
           const float p0 = __builtin_amdgcn_exp2f(s_cur[v >> 4][v & 15]);
           const float p1 = __builtin_amdgcn_exp2f(s_cur[v >> 4][(v & 15) + 1]);
           pk[v >> 1] = pack_bf16x2(p0, p1);
-          // the row sum adds exactly the rounded probabilities the PV product uses
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[v >> 1], ones, l_run, false);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -446,6 +444,13 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
         __builtin_amdgcn_sched_barrier(0);
       }
       mt_cur = pair_max(mx);
+      // The row sum adds exactly the rounded probabilities the PV product used.  It runs
+      // here, in the stage's tail where this wave has no matrix work left, rather than
+      // between the QK^T products of stage A: stage A's vector work is what the two waves
+      // of a SIMD contend for (same box, bit-identical output: mixed layer 0.3 %, single
+      // mask 1.7 %, sliding tiles 1.3 % faster).
+#pragma unroll
+      for (int v = 0; v < 16; ++v) l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[v], ones, l_run, false);
     }
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
