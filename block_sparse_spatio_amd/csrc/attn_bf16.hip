@@ -271,7 +271,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   // ---- software pipeline over the listed key tiles.  Entering step i, S(i) is in
   // registers (masked) with its row max, K(i+1) and V(i) are in LDS.  The step
   // prefetches K(i+2) and V(i+1), then runs two stages and a tail:
-  //   A: S(i+1) = K(i+1) Q^T   interleaved with   P(i) = exp2(S(i) - max)
+  //   A: S(i+1) = K(i+1) Q^T   with, in its second half,   P(i) = exp2(S(i) - max)
   //   B: O^T += V(i)^T P(i)^T  (the compiler places the vector work of B in the tail)
   //   tail: the element mask and row max of S(i+1), the row sums of P(i)
   // One barrier per step: after it, every wave has finished the previous step (so its
@@ -283,7 +283,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
   constexpr int NQK = 2 * KSTEPS;  // MFMAs of stage A
   constexpr int NPV = 4 * DB;      // MFMAs of stage B
   static_assert(NQK % C::NI == 0 && NPV % C::NI == 0, "DMA spread");
-  constexpr int EA = 32 / NQK;     // scores per lane exponentiated per stage-A MFMA
+  constexpr int EA = 32 / NQK;     // scores per lane per stage-A MFMA on average (2*EA in its second half)
   constexpr int EB = 32 / NPV;     // scores per lane max-reduced per stage-B MFMA
   static_assert(EA % 2 == 0 && EB % 2 == 0, "score pairs");
   // LDS operand of stage-A MFMA i (key half i&1, k-step i>>1) and of stage-B MFMA i
@@ -364,7 +364,7 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
 
     // stage A.  On the last tile the product runs on the stale buffer and is discarded:
     // keeping it unconditional keeps the stage straight-line code.  Chunk i issues the
-    // operand read of MFMA i + kOperandLead, MFMA i, and the exponentials of EA scores;
+    // operand read of MFMA i + kOperandLead, MFMA i, and (second half) the exponentials of 2*EA scores;
     // scheduling fences between chunks keep that order, so every LDS read has
     // kOperandLead MFMAs to land.
     f32x16 s_next[2] = {f32x16{}, f32x16{}};
@@ -395,12 +395,18 @@ void attn_fwd_bf16_kernel(FwdArgs a, const int32_t* __restrict__ n_full_p, const
           dma16(ksrc, koff[d], kl0 + d * 1024);
           if (d == 0 && has_words(it + 2)) issue_words(it + 2, P == 0 ? mbuf0 : mbuf1);
         }
+        // The exponentials ride on the second half of the stage only (2*EA per chunk), so
+        // that the stage opens with back-to-back MFMAs: measured on one box, bit-identical
+        // output, mixed layer 1.0-1.8 %, single mask 0.6 %, sliding tiles 0.6-1.1 % faster
+        // than EA per chunk throughout; front-loading them was slower.
+        if (i >= NQK / 2) {
 #pragma unroll
-        for (int e = 0; e < EA; e += 2) {
-          const int v = i * EA + e;
-          const float p0 = __builtin_amdgcn_exp2f(s_cur[v >> 4][v & 15]);
-          const float p1 = __builtin_amdgcn_exp2f(s_cur[v >> 4][(v & 15) + 1]);
-          pk[v >> 1] = pack_bf16x2(p0, p1);
+          for (int e = 0; e < 2 * EA; e += 2) {
+            const int v = (i - NQK / 2) * 2 * EA + e;
+            const float p0 = __builtin_amdgcn_exp2f(s_cur[v >> 4][v & 15]);
+            const float p1 = __builtin_amdgcn_exp2f(s_cur[v >> 4][(v & 15) + 1]);
+            pk[v >> 1] = pack_bf16x2(p0, p1);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
